@@ -1,0 +1,265 @@
+"""Benchmark of the simulated two-stage quantized allreduce on one MI355X.
+
+One step = one simulated allreduce per codec of the 64 MB workload (W=2
+ranks, fp16, 32Mi elements per rank, N(0,1) with 0.1% x50 outliers; codecs
+FP, fp8, Q8, Q6, Q4 symmetric), each as its three launches: quantize all
+ranks, fused stage 1, stage 2 -- exactly the launches qr_allreduce_sim makes.
+Inputs are resident in HBM before the timed region starts.
+
+Prints one JSON line: effective GB/s = per-rank payload bytes (2n per
+allreduce) / time, per step over all codecs; per-codec microseconds and
+GB/s; per-kernel durations from HIP events recorded on the launch stream;
+the roofline of the kernel that takes the most time; a cold-cache
+measurement of stage 1; and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import threading
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "effective GB/s and μs per simulated allreduce, 4KB–64MB, W=2/4/8, per codec"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_two_stage_amd", "csrc", f)
+                  for f in ("qr_kernels.hip", "qr_device.h")]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=1 << 21,
+                   help="elements per rank of the oracle's sample")
+    p.add_argument("--no-cold", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(stage, W, n, wb):
+    """bytes the method must move per launch (W ranks, n elements each, wire
+    image wb bytes): quantize reads 2n and writes wb per rank; stage 1 reads
+    W wire images and writes one; stage 2 reads the reduced image and writes
+    2n per rank."""
+    if stage == "quantize":
+        return W * (2 * n + wb)
+    if stage == "stage1":
+        return (W + 1) * wb
+    return W * (wb + 2 * n)
+
+
+def cpu_baseline(codecs, dtype, xs_np, sample, threads):
+    """The oracle as it stands, on blocks [0, sample/32) of every rank (the
+    same computation as the full buffers restricted to those blocks), split
+    over `threads` host threads by block range."""
+    import oracle
+    n = xs_np[0].size
+    nb = min(sample, n) // 32
+    bounds = np.linspace(0, nb, threads + 1).astype(int)
+    ys = [np.zeros(n, np.uint16) for _ in xs_np]
+
+    def work(lo, hi, codec):
+        oracle.allreduce(codec, dtype, xs_np, int(lo), int(hi), ys=ys)
+
+    t0 = time.perf_counter()
+    for codec in codecs:
+        ts = [threading.Thread(target=work, args=(bounds[i], bounds[i + 1], codec))
+              for i in range(threads)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+    dt = time.perf_counter() - t0
+    payload = len(codecs) * nb * 32 * 2
+    return {"value": payload / dt / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "blocks 0..%d (%d elements = %.1f MB per rank) of each of the %d "
+                      "ranks, all %d codecs, full pipeline; %.2f s wall" % (
+                          nb, nb * 32, nb * 64 / 2 ** 20, len(xs_np), len(codecs), dt),
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: the W ranks of the allreduce are simulated "
+              "as W buffers on that GPU; --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_two_stage_amd import inputs as I
+    from quantized_two_stage_amd import qr
+
+    torch.cuda.set_device(0)
+    cfg = I.CONFIGS[args.config]
+    W, n, dtype, codecs = cfg["W"], cfg["n"], cfg["dtype"], cfg["codecs"]
+    print("bench: config %d (%s), generating inputs" % (args.config, cfg["desc"]),
+          file=sys.stderr, flush=True)
+    xs_np = I.make(args.config)
+    xs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in xs_np]
+    ys = [torch.empty_like(xs[0]) for _ in range(W)]
+    bufs = {}
+    for c in codecs:
+        wb = qr.qr_wire_bytes(c, n)
+        bufs[c] = ([qr.alloc_wire(c, n) for _ in range(W)], qr.alloc_wire(c, n), wb)
+    stream = torch.cuda.current_stream()
+
+    def one_allreduce(c, ev=None):
+        wires, red, _ = bufs[c]
+        if ev is not None:
+            ev[0].record(stream)
+        qr.qr_quantize_ranks(c, xs, wires, dtype=dtype)
+        if ev is not None:
+            ev[1].record(stream)
+        qr.qr_reduce_stage1(c, wires, n, red, dtype)
+        if ev is not None:
+            ev[2].record(stream)
+        qr.qr_gather_stage2(c, red, ys, dtype=dtype)
+        if ev is not None:
+            ev[3].record(stream)
+
+    # check once against qr_allreduce_sim (the one-call entry point)
+    ws = qr.alloc_workspace(W, codecs[0], n)
+    ys_ref = [torch.empty_like(xs[0]) for _ in range(W)]
+    qr.qr_allreduce_sim(codecs[0], xs, ys_ref, ws, dtype=dtype)
+    one_allreduce(codecs[0])
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(ys, ys_ref)), "staged != one-call"
+    del ws, ys_ref
+
+    for _ in range(args.warmup):
+        for c in codecs:
+            one_allreduce(c)
+    torch.cuda.synchronize()
+
+    evs = {c: [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+               for _ in range(args.steps)] for c in codecs}
+    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for c in codecs:
+            one_allreduce(c, evs[c][s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    stages = ("quantize", "stage1", "stage2")
+    kernels, per_codec = [], {}
+    for c in codecs:
+        d = np.array([[evs[c][s][k].elapsed_time(evs[c][s][k + 1]) for k in range(3)]
+                      for s in range(args.steps)])            # ms
+        avg = d.mean(axis=0)
+        wb = bufs[c][2]
+        us = float(avg.sum() * 1e3)
+        per_codec[I.CODEC_NAMES[c]] = {
+            "us": us, "us_median": float(np.median(d.sum(axis=1)) * 1e3),
+            "effective_gbps": 2 * n / (us * 1e-6) / 1e9}
+        for k, st in enumerate(stages):
+            ab = algorithmic_bytes(st, W, n, wb)
+            kernels.append({"kernel": "%s/%s" % (st, I.CODEC_NAMES[c]),
+                            "us": float(avg[k] * 1e3),
+                            "algorithmic_bytes": ab,
+                            "gbps": ab / (avg[k] * 1e-3) / 1e9})
+    total_payload = len(codecs) * 2 * n
+    value = total_payload / (ms_per_step * 1e-3) / 1e9
+    dom = max(kernels, key=lambda k: k["us"])
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        tr = json.load(open(PROFILE_TRAFFIC))
+        ent = tr.get("kernels", {}).get(dom["kernel"])
+        if ent and tr.get("source_sha") == kernel_source_sha():
+            traffic = ent["bytes"]
+    roofline = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["gbps"],
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dom["gbps"] / HBM_PEAK_GBPS,
+                "traffic": traffic, "algorithmic_bytes_per_launch": dom["algorithmic_bytes"],
+                "avg_launch_us": dom["us"]}
+
+    # plain device copy of the same byte count as stage 1 of Q4: what a
+    # streaming kernel can reach on this GPU
+    src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(20):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    cold = None
+    if not args.no_cold:
+        # stage 1 with L2 and the 256 MB Infinity Cache flushed by streaming
+        # writes of 1 GiB before each timed launch
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cold = {}
+        for c in codecs:
+            wires, red, wb = bufs[c]
+            qr.qr_quantize_ranks(c, xs, wires, dtype=dtype)
+            ts = []
+            for _ in range(5):
+                flush.fill_(1)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                qr.qr_reduce_stage1(c, wires, n, red, dtype)
+                b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            us = float(np.median(ts) * 1e3)
+            ab = algorithmic_bytes("stage1", W, n, wb)
+            cold["stage1/" + I.CODEC_NAMES[c]] = {"us": us, "gbps": ab / (us * 1e-6) / 1e9,
+                                                  "frac": ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        del flush
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = min(16, os.cpu_count() or 1)
+        print("bench: CPU oracle on a sample, %d threads" % threads, file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(codecs, dtype, xs_np, args.cpu_sample, threads)
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "W=%d simulated ranks, %s, %d elements (%d MB) per rank, "
+                               "codecs %s, 32-element blocks; %s" % (
+                                   W, "fp16" if dtype == 0 else "bf16", n, 2 * n >> 20,
+                                   "/".join(I.CODEC_NAMES[c] for c in codecs), cfg["desc"]),
+                   "W": W, "elements_per_rank": n, "buffer_dtype": "fp16" if dtype == 0
+                   else "bf16", "codecs": [I.CODEC_NAMES[c] for c in codecs],
+                   "allreduces_per_step": len(codecs)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_codec": per_codec,
+        "kernels": kernels,
+        "stage1_cold": cold,
+        "device_copy_gbps": copy_gbps,
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,42 @@
+// qr_internal.h -- wire layout and kernel launchers shared by the C ABI
+// (qr_api.cpp) and the kernels (qr_kernels.hip).  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qr {
+
+constexpr int kMaxRanks = 8;
+
+// Byte layout of one rank's wire image for n elements (see qr.h): codes at
+// 0, binary16 scales at the next 256-byte boundary, binary16 zeros
+// (asymmetric codecs) at the next 256-byte boundary after the scales.
+struct Layout {
+  size_t n = 0;         // elements
+  size_t nb = 0;        // 32-element blocks
+  size_t nslices = 0;   // 16-element lane slices = 2 * nb
+  size_t code_bytes = 0;
+  size_t off_s = 0, off_z = 0;
+  size_t total = 0;     // qr_wire_bytes
+};
+
+bool codec_valid(int codec);
+Layout make_layout(int codec, size_t n);
+
+struct InPtrs { const uint8_t* p[kMaxRanks]; };
+struct OutPtrs { uint8_t* p[kMaxRanks]; };
+
+// stage 0 for W ranks: wires.p[r] <- quantize(xs.p[r])
+hipError_t launch_quantize(int codec, int dtype, int W, const InPtrs& xs,
+                           const OutPtrs& wires, const Layout& L, hipStream_t st);
+// stage 1 over blocks [blk_lo, blk_hi): reduced <- requant(sum_r dequant(wires.p[r]))
+hipError_t launch_stage1(int codec, int dtype, int W, const InPtrs& wires,
+                         uint8_t* reduced, size_t blk_lo, size_t blk_hi,
+                         const Layout& L, hipStream_t st);
+// stage 2 / dequantize for W outputs: ys.p[r] <- dequant(wire)
+hipError_t launch_dequantize(int codec, int dtype, int W, const uint8_t* wire,
+                             const OutPtrs& ys, const Layout& L, hipStream_t st);
+
+}  // namespace qr

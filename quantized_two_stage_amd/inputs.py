@@ -55,36 +55,33 @@ def shared_rng(config):
     return np.random.Generator(np.random.PCG64(1000 * config + 999))
 
 
-def to_bits(v64, dtype):
-    """Round float64 values to the buffer type; return raw uint16 patterns."""
-    if dtype == FP16:
-        return v64.astype(np.float16).view(np.uint16)
-    import torch
-    f32 = torch.from_numpy(np.ascontiguousarray(v64, dtype=np.float32))
-    return f32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
-
-
 def draw(config, rank, n, W=None):
     """float64 values of one rank's buffer for a workload."""
     g = rng(config, rank)
     if config in (1, 0):
         return g.standard_normal(n)
     if config == 2:
+        # each element independently x50 with probability 0.001: the number of
+        # outliers is binomial, their positions a uniform sample without repeats
         v = g.standard_normal(n)
-        spikes = g.random(n) < 0.001
-        v[spikes] *= 50.0
+        k = int(g.binomial(n, 0.001))
+        v[g.choice(n, k, replace=False)] *= 50.0
         return v
     if config == 3:
         v = g.normal(0.0, 0.5, n)
         rows = (n + ROW - 1) // ROW
         bias = g.uniform(-2.0, 2.0, rows)
-        v += np.repeat(bias, ROW)[:n]
+        full = n // ROW
+        v[:full * ROW].reshape(full, ROW)[:] += bias[:full, None]
+        if full < rows:
+            v[full * ROW:] += bias[full]
         return v
     if config == 4:
         sigma = 10.0 ** shared_rng(config).uniform(-3.0, 1.0, HIDDEN)
         v = g.laplace(0.0, 1.0, n)
-        reps = (n + HIDDEN - 1) // HIDDEN
-        v *= np.tile(sigma, reps)[:n]
+        full = n // HIDDEN
+        v[:full * HIDDEN].reshape(full, HIDDEN)[:] *= sigma[None, :]
+        v[full * HIDDEN:] *= sigma[:n - full * HIDDEN]
         return v
     if config == 5:
         return _adversarial(g, shared_rng(config), n)
@@ -98,25 +95,32 @@ def _adversarial(g, gs, n):
     value +-2^U(-14,15), 3 each element +-65504 with probability 1/2, else
     N(0,1)."""
     nb = (n + BLOCK - 1) // BLOCK
-    pad = nb * BLOCK
-    v = g.standard_normal(pad).reshape(nb, BLOCK)
+    v = g.standard_normal(nb * BLOCK).reshape(nb, BLOCK)
     k = np.arange(nb)
     kind = np.where(k % 2 == 1, -1, (k // 2) % 4)
     v[kind == 0] = 0.0
-    const = g.standard_normal(nb)
-    v[kind == 1] = const[kind == 1, None]
-    spike_pos = gs.integers(0, BLOCK, nb)            # shared across ranks
-    spike_val = np.exp2(g.uniform(-14.0, 15.0, nb)) * np.where(
-        g.random(nb) < 0.5, -1.0, 1.0)
-    sp = kind == 2
-    v[sp] = 0.0
-    v[sp, spike_pos[sp]] = spike_val[sp]
-    mx = kind == 3
-    pick = g.random((nb, BLOCK)) < 0.5
-    sign = np.where(g.random((nb, BLOCK)) < 0.5, -1.0, 1.0)
-    big = np.where(pick, 65504.0 * sign, v)
-    v[mx] = big[mx]
+    c1 = np.nonzero(kind == 1)[0]
+    v[c1] = g.standard_normal(c1.size)[:, None]
+    c2 = np.nonzero(kind == 2)[0]
+    pos = gs.integers(0, BLOCK, nb)[c2]               # shared across ranks
+    val = np.exp2(g.uniform(-14.0, 15.0, c2.size)) * np.where(
+        g.random(c2.size) < 0.5, -1.0, 1.0)
+    v[c2] = 0.0
+    v[c2, pos] = val
+    c3 = np.nonzero(kind == 3)[0]
+    pick = g.random((c3.size, BLOCK)) < 0.5
+    sign = np.where(g.random((c3.size, BLOCK)) < 0.5, -1.0, 1.0)
+    v[c3] = np.where(pick, 65504.0 * sign, v[c3])
     return v.reshape(-1)[:n]
+
+
+def to_bits(v64, dtype):
+    """Round float64 values to the buffer type; return raw uint16 patterns."""
+    if dtype == FP16:
+        return v64.astype(np.float16).view(np.uint16)
+    import torch
+    f32 = torch.from_numpy(np.ascontiguousarray(v64, dtype=np.float32))
+    return f32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 def make(config, W=None, n=None, dtype=None):

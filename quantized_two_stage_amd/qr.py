@@ -1,0 +1,153 @@
+"""Python binding of the C ABI in include/qr.h (argument marshalling only).
+
+Every function has the name of the C entry point it calls and takes torch
+tensors on the GPU; all work happens in libqr.so's HIP kernels, on the current
+torch stream unless `stream` is given.  There is no other implementation: if
+libqr.so is missing this module raises on import.
+"""
+import ctypes
+import os
+
+import torch
+
+QR_FP, QR_Q8, QR_Q6, QR_Q4, QR_FP8 = 0, 1, 2, 3, 5
+QR_Q8_ASYM, QR_Q6_ASYM, QR_Q4_ASYM = 9, 10, 11
+QR_FP16, QR_BF16 = 0, 1
+CODECS = (QR_FP, QR_FP8, QR_Q8, QR_Q6, QR_Q4, QR_Q8_ASYM, QR_Q6_ASYM, QR_Q4_ASYM)
+CODEC_NAMES = {QR_FP: "fp", QR_Q8: "q8", QR_Q6: "q6", QR_Q4: "q4", QR_FP8: "fp8",
+               QR_Q8_ASYM: "q8a", QR_Q6_ASYM: "q6a", QR_Q4_ASYM: "q4a"}
+ERRORS = {-1: "QR_ERR_ARG", -2: "QR_ERR_UNSUPPORTED", -3: "QR_ERR_SIZE",
+          -4: "QR_ERR_ALIGN", -5: "QR_ERR_WORKSPACE", -6: "QR_ERR_HIP"}
+QR_MAX_BYTES = 1 << 31
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqr.so")
+
+
+class QRError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (%d): %s" % (ERRORS.get(code, "?"), code, msg))
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libqr.so is not built (%s); run "
+                          "quantized_two_stage_amd/build.py" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    sz, i32, P = ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "qr_wire_bytes": (sz, [i32, sz]),
+        "qr_sim_workspace_bytes": (sz, [i32, i32, sz]),
+        "qr_quantize": (i32, [i32, i32, P, sz, P, P]),
+        "qr_dequantize": (i32, [i32, i32, P, sz, P, P]),
+        "qr_quantize_ranks": (i32, [i32, i32, i32, PP, sz, PP, P]),
+        "qr_reduce_stage1": (i32, [i32, i32, i32, PP, sz, i32, P, P]),
+        "qr_gather_stage2": (i32, [i32, i32, i32, P, sz, PP, P]),
+        "qr_allreduce_sim": (i32, [i32, i32, i32, PP, PP, sz, P, sz, P]),
+        "qr_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    return L
+
+
+LIB = _load()
+EXPORTS = ("qr_wire_bytes", "qr_sim_workspace_bytes", "qr_quantize", "qr_dequantize",
+           "qr_quantize_ranks", "qr_reduce_stage1", "qr_gather_stage2",
+           "qr_allreduce_sim", "qr_last_error")
+
+
+def _check(rc):
+    if rc != 0:
+        raise QRError(rc, LIB.qr_last_error().decode())
+
+
+def _dtype_of(t, dtype):
+    if dtype is not None:
+        return dtype
+    if t.dtype == torch.float16:
+        return QR_FP16
+    if t.dtype == torch.bfloat16:
+        return QR_BF16
+    raise TypeError("pass dtype= for a %s buffer" % t.dtype)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _ptrs(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def _n16(t):
+    return t.numel() * t.element_size() // 2
+
+
+def qr_last_error():
+    return LIB.qr_last_error().decode()
+
+
+def qr_wire_bytes(codec, n):
+    return LIB.qr_wire_bytes(codec, n)
+
+
+def qr_sim_workspace_bytes(W, codec, n):
+    return LIB.qr_sim_workspace_bytes(W, codec, n)
+
+
+def qr_quantize(codec, x, wire, dtype=None, stream=None):
+    _check(LIB.qr_quantize(codec, _dtype_of(x, dtype), _ptr(x), _n16(x), _ptr(wire),
+                           _stream(stream)))
+    return wire
+
+
+def qr_dequantize(codec, wire, y, dtype=None, stream=None):
+    _check(LIB.qr_dequantize(codec, _dtype_of(y, dtype), _ptr(wire), _n16(y), _ptr(y),
+                             _stream(stream)))
+    return y
+
+
+def qr_quantize_ranks(codec, xs, wires, dtype=None, stream=None):
+    _check(LIB.qr_quantize_ranks(codec, _dtype_of(xs[0], dtype), len(xs), _ptrs(xs),
+                                 _n16(xs[0]), _ptrs(wires), _stream(stream)))
+    return wires
+
+
+def qr_reduce_stage1(codec, wires, n, reduced, dtype, owner=-1, stream=None):
+    _check(LIB.qr_reduce_stage1(codec, dtype, len(wires), _ptrs(wires), n, owner,
+                                _ptr(reduced), _stream(stream)))
+    return reduced
+
+
+def qr_gather_stage2(codec, reduced, ys, dtype=None, stream=None):
+    _check(LIB.qr_gather_stage2(codec, _dtype_of(ys[0], dtype), len(ys), _ptr(reduced),
+                                _n16(ys[0]), _ptrs(ys), _stream(stream)))
+    return ys
+
+
+def qr_allreduce_sim(codec, xs, ys, workspace, dtype=None, stream=None):
+    """ys[r] = the simulated two-stage allreduce of xs (out-of-place)."""
+    n = _n16(xs[0])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(LIB.qr_allreduce_sim(len(xs), _dtype_of(xs[0], dtype), codec, _ptrs(xs),
+                                _ptrs(ys), n, _ptr(workspace), ws_bytes, _stream(stream)))
+    return ys
+
+
+def alloc_wire(codec, n, device="cuda"):
+    """A device buffer for one wire image (padding bytes start at zero)."""
+    return torch.zeros(qr_wire_bytes(codec, n), dtype=torch.uint8, device=device)
+
+
+def alloc_workspace(W, codec, n, device="cuda"):
+    return torch.empty(qr_sim_workspace_bytes(W, codec, n), dtype=torch.uint8,
+                       device=device)

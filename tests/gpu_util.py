@@ -1,0 +1,135 @@
+"""Helpers for the GPU parity tests: device/host transfer of raw 16-bit
+buffers, the HIP pipeline run stage by stage through the C ABI, the same
+pipeline on the oracle, and the comparisons the parity bar asks for."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+
+
+def say(*a):
+    """name the case before a GPU step (flushed, so it survives a crash)."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).cuda()
+
+
+def host16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def hostu8(t):
+    return t.cpu().numpy()
+
+
+def gpu_staged(qr, codec, dtype, xs, fill=0x5A5A):
+    """quantize_ranks -> reduce_stage1(all owners) -> gather_stage2."""
+    W, n = len(xs), xs[0].numel()
+    wires = [qr.alloc_wire(codec, n) for _ in range(W)]
+    qr.qr_quantize_ranks(codec, xs, wires, dtype=dtype)
+    red = qr.alloc_wire(codec, n)
+    qr.qr_reduce_stage1(codec, wires, n, red, dtype)
+    ys = [torch.full((n,), fill - 65536 if fill > 32767 else fill, dtype=torch.int16,
+                     device="cuda") for _ in range(W)]
+    qr.qr_gather_stage2(codec, red, ys, dtype=dtype)
+    torch.cuda.synchronize()
+    return wires, red, ys
+
+
+def oracle_staged(codec, dtype, xs_np, lo=0, hi=O.ALL):
+    W, n = len(xs_np), xs_np[0].size
+    wires = [O.quantize(codec, dtype, x, lo, hi) for x in xs_np]
+    red = O.stage1(codec, dtype, wires, n, lo, hi)
+    ys = O.stage2(codec, dtype, W, red, n, lo, hi)
+    return wires, red, ys
+
+
+def ordered(bits):
+    b = bits.astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def ulp_distance(a, b):
+    return np.abs(ordered(a) - ordered(b))
+
+
+def assert_bytes_equal(got, want, what):
+    got, want = np.asarray(got), np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, "%s: %d bytes differ, first at %d (got %02x want %02x)" % (
+        what, bad.size, bad[0], got[bad[0]], want[bad[0]])
+
+
+def _is_nan(bits, dtype):
+    exp = 0x7C00 if dtype == O.FP16 else 0x7F80
+    man = 0x03FF if dtype == O.FP16 else 0x007F
+    return ((bits & exp) == exp) & ((bits & man) != 0)
+
+
+def _is_inf(bits, dtype):
+    return (bits & 0x7FFF) == (0x7C00 if dtype == O.FP16 else 0x7F80)
+
+
+def assert_within_ulp(got, want, dtype, what, ulps=1):
+    """outputs within `ulps` units in the last place of the buffer type
+    (ordered-integer distance; +0 and -0 equal; inf only equals inf of the
+    same sign); returns how many elements are not bit-identical."""
+    got, want = np.asarray(got, np.uint16), np.asarray(want, np.uint16)
+    assert got.shape == want.shape
+    assert np.array_equal(_is_nan(got, dtype), _is_nan(want, dtype)), what
+    inf_g, inf_w = _is_inf(got, dtype), _is_inf(want, dtype)
+    assert np.array_equal(inf_g, inf_w), (what, np.nonzero(inf_g != inf_w)[0][:5])
+    assert np.array_equal(got[inf_g], want[inf_w]), what
+    fin = ~(inf_g | _is_nan(got, dtype))
+    d = ulp_distance(got[fin], want[fin])
+    worst = int(d.max()) if d.size else 0
+    assert worst <= ulps, "%s: %d ulp (index %d)" % (what, worst, np.nonzero(fin)[0][np.argmax(d)])
+    return int(np.count_nonzero((got != want) & ~(((got | want) & 0x7FFF) == 0)))
+
+
+def plane_slices(codec, n):
+    """byte ranges of the codes, scales and zeros planes of a wire image."""
+    if codec == O.FP:
+        return {"raw": (0, 2 * n)}
+    nb = (n + 31) // 32
+    cb = O.block_code_bytes(codec)
+    so = O.scale_offset(codec, n)
+    out = {"codes": (0, nb * cb), "scales": (so, so + 2 * nb)}
+    if codec & 8:
+        zo = O.zero_offset(codec, n)
+        out["zeros"] = (zo, zo + 2 * nb)
+    return out
+
+
+def block_ranges(codec, n, lo, hi):
+    """byte ranges of blocks [lo, hi) in each plane of a wire image."""
+    if codec == O.FP:
+        return {"raw": (64 * lo, min(64 * hi, 2 * n))}
+    cb = O.block_code_bytes(codec)
+    so = O.scale_offset(codec, n)
+    out = {"codes": (cb * lo, cb * hi), "scales": (so + 2 * lo, so + 2 * hi)}
+    if codec & 8:
+        zo = O.zero_offset(codec, n)
+        out["zeros"] = (zo + 2 * lo, zo + 2 * hi)
+    return out
+
+
+def assert_wire_blocks(got, want, codec, n, lo, hi, what):
+    for name, (a, b) in block_ranges(codec, n, lo, hi).items():
+        assert_bytes_equal(got[a:b], want[a:b], "%s %s blocks %d..%d" % (what, name, lo, hi))
+
+
+def sample_windows(nb, count=12, width=64, seed=0):
+    """block windows spread over [0, nb): the first, the last, and random."""
+    g = np.random.default_rng(seed)
+    w = min(width, nb)
+    starts = {0, nb - w}
+    if nb > w:
+        starts.update(int(s) for s in g.integers(0, nb - w, count))
+    return sorted((s, s + w) for s in starts)

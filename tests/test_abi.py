@@ -1,0 +1,134 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function include/qr.h declares, sizes wire images and workspaces as the wire
+definition says, and rejects every invalid argument with the documented code
+before anything is launched (the pointers below are fake, never touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qr.h")
+
+
+def _lib():
+    from quantized_two_stage_amd import qr
+    return qr
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qr_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("qr_quantize", "qr_dequantize", "qr_reduce_stage1", "qr_gather_stage2",
+                 "qr_allreduce_sim", "qr_wire_bytes", "qr_sim_workspace_bytes",
+                 "qr_last_error", "qr_quantize_ranks"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    qr = _lib()
+    for name in declared_functions():
+        assert hasattr(qr.LIB, name), name
+        assert name in qr.EXPORTS, name
+    # the binding exposes each under the same name
+    for name in declared_functions():
+        assert callable(getattr(qr, name)), name
+
+
+def test_wire_bytes_matches_definition():
+    qr = _lib()
+    n = 32 * 1024 * 1024
+    want = {qr.QR_FP: 67108864, qr.QR_FP8: 35651584, qr.QR_Q8: 35651584,
+            qr.QR_Q8_ASYM: 37748736, qr.QR_Q6: 27262976, qr.QR_Q6_ASYM: 29360128,
+            qr.QR_Q4: 18874368, qr.QR_Q4_ASYM: 20971520}
+    for c, w in want.items():
+        assert qr.qr_wire_bytes(c, n) == w
+    assert qr.qr_wire_bytes(qr.QR_Q8, 2048) == 2176
+    assert qr.qr_wire_bytes(qr.QR_Q4_ASYM, 2048) == 1408
+    assert qr.qr_wire_bytes(qr.QR_Q4, 40) == 260
+    assert qr.qr_wire_bytes(4, 2048) == 0                     # NONE is not a codec
+    assert qr.qr_sim_workspace_bytes(2, qr.QR_Q8, 2048) == 3 * 2304
+    assert qr.qr_sim_workspace_bytes(3, qr.QR_Q8, 2048) == 0
+
+
+def test_wire_bytes_agree_with_oracle():
+    import oracle
+    qr = _lib()
+    for c in qr.CODECS:
+        for n in (8, 16, 24, 32, 40, 2048, 2056, 8192 * 3 + 8, 1 << 20):
+            assert qr.qr_wire_bytes(c, n) == oracle.wire_bytes(c, n), (c, n)
+
+
+FAKE = 0x7f0000000000          # 16-byte aligned, never dereferenced
+
+
+def _pp(vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+def _call_sim(W=2, dtype=0, codec=1, xs=None, ys=None, n=2048, ws=None, ws_bytes=None):
+    qr = _lib()
+    xs = xs if xs is not None else [FAKE + i * 0x100000 for i in range(W)]
+    ys = ys if ys is not None else [FAKE + 0x10000000 + i * 0x100000 for i in range(W)]
+    ws = FAKE + 0x40000000 if ws is None else ws
+    need = qr.qr_sim_workspace_bytes(max(W, 2) if W in (2, 4, 8) else 2, codec
+                                     if codec in qr.CODECS else 1, n)
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return qr.LIB.qr_allreduce_sim(W, dtype, codec, _pp(xs), _pp(ys), n,
+                                   ctypes.c_void_p(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=3), -2), (dict(W=1), -2), (dict(W=16), -2),
+    (dict(dtype=2), -2), (dict(codec=4), -2), (dict(codec=7), -2), (dict(codec=12), -2),
+    (dict(n=0), -3), (dict(n=2044), -3), (dict(n=(1 << 30) + 8), -3),
+    (dict(ws_bytes=100), -5),
+    (dict(xs=[FAKE + 4, FAKE + 0x100000]), -4),
+    (dict(ys=[FAKE + 0x10000000, FAKE + 0x10000008]), -4),
+    (dict(ws=FAKE + 0x40000008), -4),
+    (dict(xs=[0, FAKE + 0x100000]), -1),
+    (dict(ws=0), -1),
+    (dict(ys=[FAKE, FAKE + 0x10000000]), -1),               # y aliases x
+    (dict(ys=[FAKE + 0x10000000, FAKE + 0x10000000]), -1),  # two ys alias
+    (dict(ws=FAKE), -1),                                   # workspace over x
+])
+def test_allreduce_sim_rejects(kw, code):
+    qr = _lib()
+    assert _call_sim(**kw) == code
+    assert qr.LIB.qr_last_error().decode() != ""
+
+
+def test_stage_entry_points_reject():
+    qr = _lib()
+    L = qr.LIB
+    P = ctypes.c_void_p
+    a, b = P(FAKE), P(FAKE + 0x1000000)
+    # quantize / dequantize
+    assert L.qr_quantize(4, 0, a, 2048, b, None) == -2
+    assert L.qr_quantize(1, 0, a, 2047, b, None) == -3
+    assert L.qr_quantize(1, 0, P(FAKE + 8), 2048, b, None) == -4
+    assert L.qr_quantize(1, 0, a, 2048, P(0), None) == -1
+    assert L.qr_quantize(1, 0, a, 2048, P(FAKE + 1024), None) == -1   # overlap
+    assert L.qr_dequantize(1, 1, a, 2048, P(FAKE + 0x10), None) == -1  # overlap
+    assert L.qr_dequantize(1, 3, a, 2048, b, None) == -2
+    # stage 1
+    w2 = _pp([FAKE, FAKE + 0x1000000])
+    assert L.qr_reduce_stage1(1, 0, 2, w2, 2048, 2, P(FAKE + 0x2000000), None) == -1
+    assert L.qr_reduce_stage1(1, 0, 2, w2, 2048, -2, P(FAKE + 0x2000000), None) == -1
+    assert L.qr_reduce_stage1(1, 0, 3, _pp([FAKE] * 3), 2048, -1, P(FAKE + 0x2000000),
+                              None) == -2
+    assert L.qr_reduce_stage1(1, 0, 2, w2, 2048, -1, P(FAKE + 0x1000010), None) == -1
+    assert L.qr_reduce_stage1(1, 0, 2, None, 2048, -1, P(FAKE + 0x2000000), None) == -1
+    # stage 2 and batched quantize
+    assert L.qr_gather_stage2(1, 0, 0, a, 2048, _pp([FAKE + 0x1000000]), None) == -2
+    assert L.qr_gather_stage2(1, 0, 9, a, 2048, _pp([FAKE] * 9), None) == -2
+    assert L.qr_gather_stage2(1, 0, 2, a, 2048, _pp([FAKE + 0x1000000] * 2), None) == -1
+    assert L.qr_quantize_ranks(1, 0, 2, _pp([FAKE, FAKE + 0x1000]), 2048,
+                               _pp([FAKE + 0x2000000, FAKE + 0x2000010]), None) == -1
+    assert "overlap" in L.qr_last_error().decode()

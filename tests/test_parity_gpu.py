@@ -1,0 +1,244 @@
+"""Parity of the HIP path with the oracle, element by element, through the C
+ABI: every wire plane (codes, scales, zeros) bit-exact, every output within
+1 ulp of the buffer type (in practice identical), for every codec x buffer
+type x W in {2,4,8}, at sizes that span several 256-lane workgroups and end in
+a ragged partial block; plus the hand-worked fixtures, owner-restricted
+stage 1, edge cases, guard bands and the no-write-on-error rule."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import pins
+from gpu_util import (assert_bytes_equal, assert_within_ulp, dev16, gpu_staged, host16,
+                      hostu8, oracle_staged, plane_slices, say)
+from quantized_two_stage_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qr():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from quantized_two_stage_amd import qr as q
+    return q
+
+
+CODECS = (O.FP, O.FP8, O.Q8, O.Q6, O.Q4, O.Q8A, O.Q6A, O.Q4A)
+GENS = {O.FP16: (1, 2, 5), O.BF16: (3, 4, 5)}
+
+
+def _inputs(cfg, W, n, dtype, salt=0):
+    return [I.to_bits(I.draw(cfg, r + 16 * salt, n), dtype) for r in range(W)]
+
+
+def _check_case(qr, codec, dtype, xs_np, label):
+    W, n = len(xs_np), xs_np[0].size
+    say("case", label)
+    xs = [dev16(x) for x in xs_np]
+    g_wires, g_red, g_ys = gpu_staged(qr, codec, dtype, xs)
+    r_wires, r_red, r_ys = oracle_staged(codec, dtype, xs_np)
+    for r in range(W):
+        assert_bytes_equal(hostu8(g_wires[r]), r_wires[r], "%s wire[%d]" % (label, r))
+    assert_bytes_equal(hostu8(g_red), r_red, "%s reduced" % label)
+    for r in range(W):
+        assert_within_ulp(host16(g_ys[r]), r_ys[r], dtype, "%s y[%d]" % (label, r))
+    # the one-call pipeline gives the same outputs
+    ys2 = [torch.empty_like(xs[0]) for _ in range(W)]
+    ws = qr.alloc_workspace(W, codec, n)
+    qr.qr_allreduce_sim(codec, xs, ys2, ws, dtype=dtype)
+    torch.cuda.synchronize()
+    for r in range(W):
+        assert_within_ulp(host16(ys2[r]), r_ys[r], dtype, "%s sim y[%d]" % (label, r))
+    # inputs are never modified
+    for r in range(W):
+        assert np.array_equal(host16(xs[r]), xs_np[r]), label
+
+
+SIZES = (8, 24, 40, 3 * 8192 + 24)    # one partial block ... several workgroups + tail
+
+
+@pytest.mark.parametrize("W", (2, 4, 8))
+@pytest.mark.parametrize("dtype", (O.FP16, O.BF16), ids=("fp16", "bf16"))
+@pytest.mark.parametrize("codec", CODECS, ids=[I.CODEC_NAMES[c] for c in CODECS])
+def test_parity_small(qr, codec, dtype, W):
+    for cfg in GENS[dtype]:
+        for n in SIZES:
+            xs_np = _inputs(cfg, W, n, dtype)
+            _check_case(qr, codec, dtype, xs_np, "c%d %s W%d n%d gen%d" % (
+                codec, "bf16" if dtype else "fp16", W, n, cfg))
+
+
+def test_golden_fixtures_gpu(qr):
+    """The hand-worked examples through the HIP path."""
+    for case in pins.golden_cases():
+        codec, dt = case["codec"], case["dtype"]
+        dtype = O.FP16 if dt == "fp16" else O.BF16
+        xs_np = [pins.to_buf(x, dt) for x in case["x"]]
+        n = xs_np[0].size
+        want_y = np.array(case["x"][0] if case["y"] == "x" else case["y"], np.float64)
+        say("golden", case["name"])
+        xs = [dev16(x) for x in xs_np]
+        if case["W"] == 1:
+            wire = qr.alloc_wire(codec, n)
+            qr.qr_quantize(codec, xs[0], wire, dtype=dtype)
+            y = torch.empty_like(xs[0])
+            qr.qr_dequantize(codec, wire, y, dtype=dtype)
+            torch.cuda.synchronize()
+            pins.check_wire_planes(codec, n, hostu8(wire), case["wire"])
+            ys = [y]
+        else:
+            _, red, ys = gpu_staged(qr, codec, dtype, xs)
+            pins.check_wire_planes(codec, n, hostu8(red), case["reduced"])
+        for y in ys:
+            got = pins.from_buf(host16(y), dt)
+            assert np.array_equal(got, want_y), (case["name"], got)
+
+
+@pytest.mark.parametrize("W", (2, 4, 8))
+def test_owner_chunks(qr, W):
+    """stage 1 for each owner writes exactly its chunk; together they give
+    the full reduced image."""
+    for codec in (O.FP, O.Q4, O.Q6A, O.FP8):
+        n = 32 * 37 + 16
+        xs_np = _inputs(5, W, n, O.FP16, salt=1)
+        say("owners", codec, W, n)
+        xs = [dev16(x) for x in xs_np]
+        wires = [qr.alloc_wire(codec, n) for _ in range(W)]
+        qr.qr_quantize_ranks(codec, xs, wires, dtype=O.FP16)
+        full = qr.alloc_wire(codec, n)
+        qr.qr_reduce_stage1(codec, wires, n, full, O.FP16)
+        acc = qr.alloc_wire(codec, n)
+        for j in range(W):
+            part = qr.alloc_wire(codec, n)
+            qr.qr_reduce_stage1(codec, wires, n, part, O.FP16, owner=j)
+            torch.cuda.synchronize()
+            p = hostu8(part)
+            want = O.stage1(codec, O.FP16, [hostu8(w) for w in wires], n,
+                            *O.chunk(W, n, j))
+            assert_bytes_equal(p, want, "owner %d" % j)
+            acc |= part
+        torch.cuda.synchronize()
+        assert_bytes_equal(hostu8(acc), hostu8(full), "union of owners")
+
+
+@pytest.mark.parametrize("dtype", (O.FP16, O.BF16), ids=("fp16", "bf16"))
+def test_edge_values(qr, dtype):
+    """all-zero, constant, +-0 mixes, sums that overflow to inf, huge and
+    tiny magnitudes, identical ranks, and cancellation across ranks."""
+    W, n = 4, 32 * 10 + 8
+    one = pins.to_buf([1.0], "fp16" if dtype == O.FP16 else "bf16")[0]
+    big = 0x7BFF if dtype == O.FP16 else 0x7F7F       # largest finite
+    tiny = 0x0001                                       # smallest subnormal
+    cases = {
+        "zeros": [np.zeros(n, np.uint16)] * W,
+        "neg_zeros": [np.full(n, 0x8000, np.uint16)] * W,
+        "constant": [np.full(n, one, np.uint16)] * W,
+        "overflow": [np.full(n, big, np.uint16)] * W,
+        "tiny": [np.full(n, tiny, np.uint16) | (np.arange(n, dtype=np.uint16) & 1) * 0x8000] * W,
+        "identical": [I.to_bits(I.draw(1, 0, n), dtype)] * W,
+        "cancel": [I.to_bits(I.draw(1, 0, n), dtype),
+                   I.to_bits(I.draw(1, 0, n), dtype) ^ 0x8000,
+                   I.to_bits(I.draw(1, 1, n), dtype),
+                   I.to_bits(I.draw(1, 1, n), dtype) ^ 0x8000],
+    }
+    for name, xs_np in cases.items():
+        for codec in CODECS:
+            _check_case(qr, codec, dtype, [x.copy() for x in xs_np],
+                        "edge %s c%d" % (name, codec))
+
+
+def test_single_rank_entry_points(qr):
+    """qr_quantize / qr_dequantize on their own (W = 1 of the pipeline)."""
+    for dtype in (O.FP16, O.BF16):
+        for codec in CODECS:
+            n = 8192 + 16
+            x_np = I.to_bits(I.draw(5 if dtype == O.FP16 else 4, 7, n), dtype)
+            say("single", codec, dtype)
+            x = dev16(x_np)
+            wire = qr.alloc_wire(codec, n)
+            qr.qr_quantize(codec, x, wire, dtype=dtype)
+            y = torch.empty_like(x)
+            qr.qr_dequantize(codec, wire, y, dtype=dtype)
+            torch.cuda.synchronize()
+            rw = O.quantize(codec, dtype, x_np)
+            assert_bytes_equal(hostu8(wire), rw, "single wire")
+            assert_within_ulp(host16(y), O.dequantize(codec, dtype, rw, n), dtype, "single y")
+
+
+def test_guard_bands(qr):
+    """nothing is written outside the buffers: every output sits inside a
+    larger allocation filled with a canary pattern."""
+    G = 4096
+    for codec in CODECS:
+        for n in (8, 40, 8192 + 24):
+            W = 4
+            say("guard", codec, n)
+            xs = [dev16(x) for x in _inputs(5, W, n, O.FP16)]
+            wb = qr.qr_wire_bytes(codec, n)
+            big_w = [torch.full((wb + 2 * G,), 0xA5, dtype=torch.uint8, device="cuda")
+                     for _ in range(W + 1)]
+            big_y = [torch.full((n + G,), 0x3C3C, dtype=torch.int16, device="cuda")
+                     for _ in range(W)]
+            wires = [b[G:G + wb] for b in big_w[:W]]
+            red = big_w[W][G:G + wb]
+            ys = [b[G // 2:G // 2 + n] for b in big_y]
+            qr.qr_quantize_ranks(codec, xs, wires, dtype=O.FP16)
+            qr.qr_reduce_stage1(codec, wires, n, red, O.FP16)
+            qr.qr_gather_stage2(codec, red, ys, dtype=O.FP16)
+            torch.cuda.synchronize()
+            for b in big_w:
+                h = hostu8(b)
+                assert np.all(h[:G] == 0xA5) and np.all(h[G + wb:] == 0xA5), codec
+                # plane padding is left untouched too
+                planes = sorted(plane_slices(codec, n).values())
+                inner = h[G:G + wb].copy()
+                for a, e in planes:
+                    inner[a:e] = 0xA5
+                assert np.all(inner == 0xA5), ("padding written", codec, n)
+            for b in big_y:
+                h = host16(b)
+                assert np.all(h[:G // 2] == 0x3C3C) and np.all(h[G // 2 + n:] == 0x3C3C)
+
+
+def test_rejected_call_writes_nothing(qr):
+    n, W, codec = 4096, 2, O.Q4
+    xs = [dev16(x) for x in _inputs(1, W, n, O.FP16)]
+    ybuf = [torch.full((n + 8,), 77, dtype=torch.int16, device="cuda") for _ in range(W)]
+    ys = [b[:n] for b in ybuf]
+    ws = torch.full((qr.qr_sim_workspace_bytes(W, codec, n),), 9, dtype=torch.uint8,
+                    device="cuda")
+    say("rejects")
+    with pytest.raises(qr.QRError) as e:                        # workspace too small
+        qr.qr_allreduce_sim(codec, xs, ys, ws[:-1], dtype=O.FP16)
+    assert e.value.code == -5
+    with pytest.raises(qr.QRError) as e:                        # misaligned output
+        qr.qr_allreduce_sim(codec, xs, [ys[0], ybuf[1][1:n + 1]], ws, dtype=O.FP16)
+    assert e.value.code == -4
+    with pytest.raises(qr.QRError) as e:                        # y overlaps x
+        qr.qr_allreduce_sim(codec, xs, [xs[1], ys[1]], ws, dtype=O.FP16)
+    assert e.value.code == -1
+    with pytest.raises(qr.QRError) as e:                        # W not in {2,4,8}
+        qr.qr_allreduce_sim(codec, xs + [xs[0]], ys + [ybuf[0][8:8 + n]], ws, dtype=O.FP16)
+    assert e.value.code == -2
+    torch.cuda.synchronize()
+    for b in ybuf:
+        assert torch.all(b == 77)
+    assert torch.all(ws == 9)
+
+
+def test_nondefault_stream(qr):
+    n, W, codec = 8192 * 2, 8, O.Q6
+    xs_np = _inputs(5, W, n, O.FP16)
+    xs = [dev16(x) for x in xs_np]
+    ys = [torch.empty_like(xs[0]) for _ in range(W)]
+    ws = qr.alloc_workspace(W, codec, n)
+    s = torch.cuda.Stream()
+    say("stream")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        qr.qr_allreduce_sim(codec, xs, ys, ws, dtype=O.FP16)
+    s.synchronize()
+    want = O.allreduce(codec, O.FP16, xs_np)
+    for r in range(W):
+        assert_within_ulp(host16(ys[r]), want[r], O.FP16, "stream y")
