@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=1 << 21,
+    p.add_argument("--cpu-sample", type=int, default=1 << 25,
                    help="elements per rank of the oracle's sample")
     p.add_argument("--no-cold", action="store_true")
     return p.parse_args()
@@ -192,33 +192,37 @@ def main():
                 "traffic": traffic, "algorithmic_bytes_per_launch": dom["algorithmic_bytes"],
                 "avg_launch_us": dom["us"]}
 
-    # plain device copy of the same byte count as stage 1 of Q4: what a
-    # streaming kernel can reach on this GPU
-    src = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(20):
-        dst.copy_(src)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * src.numel() * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+    # plain device copies: 64 MB (fits the 256 MB Infinity Cache, like the
+    # workload's own buffers) and 1 GiB (streams from HBM)
+    copy_gbps = {}
+    for size in (64 << 20, 1 << 30):
+        src = torch.empty(size, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20 if size < (1 << 30) else 5
+        e0.record(stream)
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps["%dMiB" % (size >> 20)] = 2 * size * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
 
     cold = None
     if not args.no_cold:
-        # stage 1 with L2 and the 256 MB Infinity Cache flushed by streaming
-        # writes of 1 GiB before each timed launch
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # stage 1 with L2 and the 256 MB Infinity Cache flushed before each
+        # timed launch by reading 1 GiB of other data (a read leaves no dirty
+        # lines to write back during the timed kernel)
+        flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
         cold = {}
         for c in codecs:
             wires, red, wb = bufs[c]
             qr.qr_quantize_ranks(c, xs, wires, dtype=dtype)
             ts = []
             for _ in range(5):
-                flush.fill_(1)
+                flush.sum()
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
                 qr.qr_reduce_stage1(c, wires, n, red, dtype)

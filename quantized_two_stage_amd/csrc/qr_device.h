@@ -1,14 +1,14 @@
 // qr_device.h -- device helpers of the two-stage quantized allreduce for
-// gfx950: number formats, the per-lane block quantizer and the wire-slice
-// code I/O.
+// gfx950: number formats, code packing/unpacking and the block quantizer.
 //
-// Work decomposition used by every kernel: a 32-element block is handled by
-// a pair of adjacent lanes, each owning a 16-element "slice" (lane 2j takes
-// elements 0..15 of block j, lane 2j+1 elements 16..31).  A slice is 32
-// bytes of fp16/bf16 input (two 128-bit accesses) and 16*b/8 bytes of codes
-// (8 for 4-bit, 12 for 6-bit, 16 for 8-bit codes), so consecutive lanes
-// touch consecutive bytes in every plane.  The block statistics (max/min)
-// need one exchange between the two lanes of a pair (a DPP quad permute).
+// Two work decompositions are used (see qr_kernels.hip):
+//   - one lane per 32-element block (stage 1): the block's codes are 16, 24
+//     or 32 contiguous bytes, its statistics and scale are computed once, in
+//     registers, with no cross-lane traffic;
+//   - four lanes per block, 8 elements each (stage 0 and stage 2): every lane
+//     reads or writes 16 contiguous bytes of 16-bit data, so those planes
+//     stream at full coalescing; stage 0 combines the block's max/min across
+//     the four lanes with two DPP quad permutes.
 //
 // The numerics follow the readings taken for the formats named in "Integrate
 // quick allreduce and select the best allreduce implementation" (vLLM PR
@@ -33,8 +33,8 @@ enum Codec { kFP = 0, kQ8 = 1, kQ6 = 2, kQ4 = 3, kFP8 = 5,
              kQ8A = 9, kQ6A = 10, kQ4A = 11 };
 enum DType { kF16 = 0, kBF16 = 1 };
 
-constexpr int kSlice = 16;   // elements per lane
-constexpr int kBlock = 32;   // elements per block (a lane pair)
+constexpr int kBlock = 32;   // elements per block
+constexpr int kQuarter = 8;  // elements per lane in the four-lane layout
 
 template <int C>
 struct CodecT {
@@ -45,7 +45,10 @@ struct CodecT {
   static constexpr float qmax =
       fp8 ? 448.0f
           : asym ? float((1 << bits) - 1) : float((1 << (bits - 1)) - 1);
-  static constexpr int slice_bytes = kSlice * bits / 8;
+  static constexpr int block_bytes = kBlock * bits / 8;   // 16, 24, 32
+  static constexpr int words = block_bytes / 4;           // 4, 6, 8
+  // symmetric 4-bit codes are unpacked as 16*q (see code_values)
+  static constexpr float unpack_scale = (!asym && bits == 4) ? 0.0625f : 1.0f;
 };
 
 // ---------------------------------------------------------------------------
@@ -59,13 +62,13 @@ __device__ __forceinline__ uint32_t f2h(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 __device__ __forceinline__ float bf2f(uint32_t b) {
-  return __builtin_bit_cast(float, b << 16);
+  return (float)__builtin_bit_cast(__bf16, (uint16_t)b);      // exact
 }
-// binary32 -> bfloat16, nearest-even on the bit pattern, overflow to inf
+// binary32 -> bfloat16, nearest-even, overflow to inf (v_cvt_pk_bf16_f32;
+// for every non-NaN binary32 input this is round-to-nearest-even on the bit
+// pattern)
 __device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 template <int D>
@@ -75,6 +78,11 @@ __device__ __forceinline__ float ld16(uint32_t bits) {
 template <int D>
 __device__ __forceinline__ uint32_t st16(float v) {
   return D == kBF16 ? f2bf(v) : f2h(v);
+}
+// two 16-bit values of a packed word
+template <int D>
+__device__ __forceinline__ uint32_t st16x2(float lo, float hi) {
+  return st16<D>(lo) | (st16<D>(hi) << 16);
 }
 
 // least binary16 >= v (v >= 0), saturated at 65504: round to nearest, then
@@ -92,193 +100,232 @@ __device__ __forceinline__ uint32_t rd16(float v) {
   return (h & 0x7fffu) >= 0x7c00u ? (h & 0x8000u) | 0x7bffu : h;
 }
 
-// OCP E4M3FN encode: nearest, ties to even, saturating at 448; the sign of
-// t is kept when the magnitude rounds to zero
-__device__ __forceinline__ uint32_t e4m3_enc(float t) {
-  uint32_t u = __builtin_bit_cast(uint32_t, t);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t au = u & 0x7fffffffu;
-  float a = __builtin_bit_cast(float, au);
-  uint32_t code;
-  if (a >= 448.0f) {
-    code = 0x7eu;
-  } else if (a < 0.015625f) {                 // below 2^-6: steps of 2^-9
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {                                    // round the fraction to 3 bits
-    code = ((au + 0x7ffffu + ((au >> 20) & 1u)) >> 20) - (120u << 3);
-  }
-  return code | sign;
+// OCP E4M3FN (bias 7, 3 fraction bits, largest finite 448, 0x7f/0xff NaN).
+// gfx950's conversions use this format: v_cvt_pk_fp8_f32 rounds to nearest,
+// ties to even, keeps the sign of a zero result, and gives 448 for
+// 448 <= |t| <= 464 (NaN above: callers clamp first where that can occur);
+// v_cvt_f32_fp8 decodes exactly.
+__device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t old, bool hi) {
+  return hi ? (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, true)
+            : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false);
+}
+template <int Byte>
+__device__ __forceinline__ float e4m3_dec(uint32_t word) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)word, Byte);
 }
 
-// OCP E4M3FN decode (exact); code 0x7f/0xff (NaN) is never produced here
-__device__ __forceinline__ float e4m3_dec(uint32_t c) {
-  uint32_t em = c & 0x7fu;
-  float mag = em < 8u ? (float)em * 0.001953125f
-                      : __builtin_bit_cast(float, (em + (120u << 3)) << 20);
-  return __builtin_bit_cast(float,
-                            __builtin_bit_cast(uint32_t, mag) | ((c & 0x80u) << 24));
+// Round-half-even to an integer by one binary32 addition: for |c| <= 2^22,
+// c + 1.5*2^23 lies in [2^23, 2^24), where the spacing is 1, so the sum is
+// 1.5*2^23 + rint(c) exactly and its low fraction bits hold rint(c) in two's
+// complement.
+constexpr float kRoundMagic = 12582912.0f;
+__device__ __forceinline__ uint32_t rint_bits(float c) {
+  return __builtin_bit_cast(uint32_t, c + kRoundMagic);
 }
 
-// value held by the other lane of this lane's pair (DPP quad_perm [1,0,3,2])
-__device__ __forceinline__ float pair_other(float v) {
+// value held by another lane of this lane's quad (DPP quad permute)
+template <int Ctrl>
+__device__ __forceinline__ float quad_perm(float v) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xb1, 0xf, 0xf,
-                                      false));
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), Ctrl, 0xf, 0xf, false));
 }
+template <int Ctrl>
+__device__ __forceinline__ uint32_t quad_perm_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, Ctrl, 0xf, 0xf, false);
+}
+constexpr int kSwap1 = 0xb1;    // quad_perm [1,0,3,2]
+constexpr int kSwap2 = 0x4e;    // quad_perm [2,3,0,1]
+constexpr int kFromOdd = 0xf5;  // quad_perm [1,1,3,3]
 
 // ---------------------------------------------------------------------------
-// block quantizer: the lane's 16 values (first `valid` of them real, valid in
-// {0, 8, 16}) together with the partner lane's form one block.  Writes the
-// lane's 16 codes (b-bit patterns, zero for invalid slots) and the block's
-// binary16 scale and zero (identical in both lanes).
+// code packing: code i at bits [b*i, b*i+b) of a little-endian bitstring
 
-template <int C>
-__device__ __forceinline__ void quantize_slice(const float (&v)[kSlice], int valid,
-                                               uint32_t (&code)[kSlice],
-                                               uint32_t& s_out, uint32_t& z_out) {
+// Packs N b-bit codes, code i taken from the low bits of c[i] (higher bits
+// are ignored), into ceil(N*b/32) words: each code is shifted in at the top
+// of the current word with one funnel shift (v_alignbit_b32); a code that
+// straddles two words is shifted in as two pieces.  The bits of a last,
+// partly filled word beyond N*b are zero.
+template <int B, int N>
+__device__ __forceinline__ void pack_bits(const uint32_t (&c)[N],
+                                          uint32_t (&w)[(N * B + 31) / 32]) {
+  constexpr int nw = (N * B + 31) / 32;
+#pragma unroll
+  for (int k = 0; k < nw; k++) {
+    uint32_t acc = 0;
+    int filled = 0;
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+      const int lo = B * i, hi = lo + B;             // code i's bit range
+      const int a = lo > 32 * k ? lo : 32 * k;       // its part in word k
+      const int e = hi < 32 * (k + 1) ? hi : 32 * (k + 1);
+      if (a < e) {
+        const uint32_t piece = a > lo ? c[i] >> (a - lo) : c[i];
+        acc = __builtin_amdgcn_alignbit(piece, acc, e - a);
+        filled += e - a;
+      }
+    }
+    w[k] = filled == 32 ? acc : acc >> (32 - filled);
+  }
+}
+
+// Scaled values t[i] (v*inv, or (v-z)*inv) -> packed codes.  `sat` marks a
+// block whose scale or zero saturated at the binary16 range, the only case in
+// which t can leave the code range (see block_params): then t is clamped
+// first, as the definition does; otherwise the clamp is the identity and
+// skipped.
+template <int C, int N>
+__device__ __forceinline__ void encode(float (&t)[N], bool sat,
+                                       uint32_t (&w)[(N * CodecT<C>::bits + 31) / 32]) {
   using T = CodecT<C>;
-  float mx = v[0], mn = v[0];
+  if (sat) {
+    const float lo = T::asym ? 0.0f : -T::qmax;
 #pragma unroll
-  for (int i = 1; i < 8; i++) {
-    mx = fmaxf(mx, v[i]);
-    mn = fminf(mn, v[i]);
+    for (int i = 0; i < N; i++) t[i] = fminf(fmaxf(t[i], lo), T::qmax);
   }
-  if (valid == kSlice) {
+  if constexpr (T::fp8) {
 #pragma unroll
-    for (int i = 8; i < kSlice; i++) {
-      mx = fmaxf(mx, v[i]);
-      mn = fminf(mn, v[i]);
-    }
-  }
-  if (valid == 0) {
-    mx = -__builtin_inff();
-    mn = __builtin_inff();
-  }
-  mx = fmaxf(mx, pair_other(mx));
-  mn = fminf(mn, pair_other(mn));
-
-  uint32_t s = 0, z = 0;
-#pragma unroll
-  for (int i = 0; i < kSlice; i++) code[i] = 0;
-
-  if constexpr (!T::asym) {
-    float a = fmaxf(fabsf(mx), fabsf(mn));
-    if (a != 0.0f) {
-      // a constant block takes its own magnitude as the scale
-      float arg = (mx == mn) ? a : a / T::qmax;
-      s = ru16(arg);
-      float inv = 1.0f / h2f(s);
-#pragma unroll
-      for (int i = 0; i < kSlice; i++) {
-        float t = v[i] * inv;
-        uint32_t c;
-        if constexpr (T::fp8) {
-          c = e4m3_enc(t);
-        } else {
-          float q = fminf(fmaxf(__builtin_rintf(t), -T::qmax), T::qmax);
-          c = (uint32_t)(int)q & ((1u << T::bits) - 1u);
-        }
-        code[i] = (i < valid) ? c : 0u;
-      }
-    }
+    for (int k = 0; k < N / 4; k++)
+      w[k] = e4m3_pack2(t[4 * k + 2], t[4 * k + 3],
+                        e4m3_pack2(t[4 * k], t[4 * k + 1], 0u, false), true);
   } else {
-    if (mn == 0.0f) mn = 0.0f;                  // a zero minimum is +0
-    z = rd16(mn);
-    float fz = h2f(z);
-    float d = mx - fz;
-    if (d > 0.0f) {
-      s = ru16(d / T::qmax);
-      float inv = 1.0f / h2f(s);
+    uint32_t c[N];
 #pragma unroll
-      for (int i = 0; i < kSlice; i++) {
-        float t = (v[i] - fz) * inv;
-        float u = fminf(fmaxf(__builtin_rintf(t), 0.0f), T::qmax);
-        code[i] = (i < valid) ? (uint32_t)(int)u : 0u;
+    for (int i = 0; i < N; i++) c[i] = rint_bits(t[i]);
+    pack_bits<T::bits, N>(c, w);
+  }
+}
+
+// a & m computed once per word.  Opaque to the optimizer on purpose: seen
+// through, the mask is folded into every byte extraction below, which then
+// takes two instructions per code instead of one sign- or zero-extending byte
+// select inside the conversion (SDWA).
+__device__ __forceinline__ uint32_t and_word(uint32_t a, uint32_t m) {
+  uint32_t r;
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(m));
+  return r;
+}
+
+// Code values of N codes packed from bit 0 of w, as binary32: q (or 16*q for
+// symmetric 4-bit codes, so that a sign-extended byte select does the
+// unpacking), u for asymmetric codes, the decoded value for fp8.  The value
+// of a code is then cv[i] * (s * unpack_scale) (+ z): the product is exact.
+template <int C, int N>
+__device__ __forceinline__ void code_values(const uint32_t* w, float (&cv)[N]) {
+  using T = CodecT<C>;
+  constexpr int b = T::bits;
+  if constexpr (T::fp8) {
+#pragma unroll
+    for (int k = 0; k < N / 4; k++) {
+      cv[4 * k] = e4m3_dec<0>(w[k]);
+      cv[4 * k + 1] = e4m3_dec<1>(w[k]);
+      cv[4 * k + 2] = e4m3_dec<2>(w[k]);
+      cv[4 * k + 3] = e4m3_dec<3>(w[k]);
+    }
+  } else if constexpr (b == 8) {
+#pragma unroll
+    for (int k = 0; k < N / 4; k++)
+#pragma unroll
+      for (int m = 0; m < 4; m++)
+        cv[4 * k + m] = T::asym ? (float)((w[k] >> (8 * m)) & 0xffu)
+                                : (float)(int)(int8_t)(w[k] >> (8 * m));
+  } else if constexpr (b == 4) {
+#pragma unroll
+    for (int k = 0; k < N / 8; k++) {
+      // even codes of the word in the bytes of `ev`, odd codes in `od`
+      const uint32_t ev = T::asym ? and_word(w[k], 0x0f0f0f0fu)
+                                  : and_word(w[k] << 4, 0xf0f0f0f0u);
+      const uint32_t od = T::asym ? and_word(w[k] >> 4, 0x0f0f0f0fu)
+                                  : and_word(w[k], 0xf0f0f0f0u);
+#pragma unroll
+      for (int m = 0; m < 4; m++) {
+        cv[8 * k + 2 * m] = T::asym ? (float)((ev >> (8 * m)) & 0xffu)
+                                    : (float)(int)(int8_t)(ev >> (8 * m));
+        cv[8 * k + 2 * m + 1] = T::asym ? (float)((od >> (8 * m)) & 0xffu)
+                                        : (float)(int)(int8_t)(od >> (8 * m));
       }
     }
+  } else {                                           // 6-bit
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+      const int off = b * i, k = off >> 5, sh = off & 31;
+      const uint32_t x = (sh + b <= 32) ? w[k] : __builtin_amdgcn_alignbit(w[k + 1], w[k], sh);
+      const int s = (sh + b <= 32) ? sh : 0;
+      // (the bit-field builtins return unsigned: the signed field must be
+      // converted as int)
+      cv[i] = T::asym ? (float)__builtin_amdgcn_ubfe(x, s, b)
+                      : (float)(int)__builtin_amdgcn_sbfe((int)x, s, b);
+    }
   }
-  s_out = s;
-  z_out = z;
 }
 
 // ---------------------------------------------------------------------------
-// slice code words: 16 codes of b bits, little-endian bitstream
+// block quantizer
 
+// max and min of p[0..8), or (-inf, +inf) when the group holds no value
+__device__ __forceinline__ void group_max_min(const float* p, bool any, float& mx,
+                                              float& mn) {
+  mx = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])),
+             fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7])));
+  mn = fminf(fminf(fminf(p[0], p[1]), fminf(p[2], p[3])),
+             fminf(fminf(p[4], p[5]), fminf(p[6], p[7])));
+  mx = any ? mx : -__builtin_inff();
+  mn = any ? mn : __builtin_inff();
+}
+
+// Scale and zero of a block from its max and min, and the parameters that
+// turn a value into t = (v - tz) * inv.
 template <int C>
-struct SliceWords {
-  static constexpr int nw = CodecT<C>::slice_bytes / 4;   // 2, 3 or 4
-  uint32_t w[nw];
+struct BlockParams {
+  uint32_t s = 0, z = 0;   // binary16 scale and zero (z = 0: symmetric)
+  float tz = 0.0f;         // subtracted before scaling (the zero)
+  float inv = 0.0f;        // 1/s, or 0 for a block whose codes are all 0
+  bool sat = false;        // scale or zero saturated at the binary16 range
 };
 
 template <int C>
-__device__ __forceinline__ SliceWords<C> load_slice(const uint8_t* p) {
-  SliceWords<C> r;
-  if constexpr (SliceWords<C>::nw == 4) {
-    u32x4 q = *reinterpret_cast<const u32x4*>(p);
-    r.w[0] = q.x; r.w[1] = q.y; r.w[2] = q.z; r.w[3] = q.w;
-  } else if constexpr (SliceWords<C>::nw == 2) {
-    u32x2 q = *reinterpret_cast<const u32x2*>(p);
-    r.w[0] = q.x; r.w[1] = q.y;
-  } else {
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-    r.w[0] = q[0]; r.w[1] = q[1]; r.w[2] = q[2];
-  }
-  return r;
-}
-
-template <int C>
-__device__ __forceinline__ void store_slice(uint8_t* p, const SliceWords<C>& r) {
-  if constexpr (SliceWords<C>::nw == 4) {
-    *reinterpret_cast<u32x4*>(p) = u32x4{r.w[0], r.w[1], r.w[2], r.w[3]};
-  } else if constexpr (SliceWords<C>::nw == 2) {
-    *reinterpret_cast<u32x2*>(p) = u32x2{r.w[0], r.w[1]};
-  } else {
-    uint32_t* q = reinterpret_cast<uint32_t*>(p);
-    q[0] = r.w[0]; q[1] = r.w[1]; q[2] = r.w[2];
-  }
-}
-
-// raw b-bit field i of the slice (zero-extended)
-template <int C>
-__device__ __forceinline__ uint32_t get_field(const SliceWords<C>& r, int i) {
-  constexpr int b = CodecT<C>::bits;
-  const int off = b * i, k = off >> 5, sh = off & 31;
-  uint32_t x;
-  if (sh + b <= 32 || k + 1 >= SliceWords<C>::nw)
-    x = r.w[k] >> sh;
-  else
-    x = __builtin_amdgcn_alignbit(r.w[k + 1], r.w[k], sh);
-  return x & ((1u << b) - 1u);
-}
-
-template <int C>
-__device__ __forceinline__ SliceWords<C> pack_slice(const uint32_t (&code)[kSlice]) {
-  constexpr int b = CodecT<C>::bits;
-  SliceWords<C> r;
-#pragma unroll
-  for (int k = 0; k < SliceWords<C>::nw; k++) r.w[k] = 0;
-#pragma unroll
-  for (int i = 0; i < kSlice; i++) {
-    const int off = b * i, k = off >> 5, sh = off & 31;
-    r.w[k] |= code[i] << sh;
-    if (sh + b > 32) r.w[k + 1] |= code[i] >> (32 - sh);
-  }
-  return r;
-}
-
-// dequantized value of field i: code*s exact, plus z for asymmetric codecs
-template <int C>
-__device__ __forceinline__ float dequant_field(const SliceWords<C>& r, int i,
-                                               float s, float z) {
+__device__ __forceinline__ BlockParams<C> block_params(float mx, float mn) {
   using T = CodecT<C>;
-  uint32_t f = get_field<C>(r, i);
-  if constexpr (T::fp8) {
-    return e4m3_dec(f) * s;
-  } else if constexpr (T::asym) {
-    return __builtin_fmaf((float)f, s, z);    // f*s is exact: one rounding
+  BlockParams<C> p;
+  // t lies within qmax*(1 + 3*2^-24) < qmax + 1/2 of the code range whenever
+  // the scale (and zero) are not saturated: s >= f32(range/qmax) and 1/s is
+  // rounded once.  Rounding t then already gives a code in range; the clamp
+  // of the definition is only executed for saturated blocks (|x| beyond the
+  // binary16 range), where it matters.
+  if constexpr (!T::asym) {
+    const float a = fmaxf(fabsf(mx), fabsf(mn));
+    // a constant block takes its own magnitude as the scale
+    const float arg = (mx == mn) ? a : a / T::qmax;
+    p.s = a != 0.0f ? ru16(arg) : 0u;
+    // all-zero block: scale +0 and codes 0 (inv = 0 gives t = +-0)
+    p.inv = a != 0.0f ? 1.0f / h2f(p.s) : 0.0f;
+    p.sat = p.s == 0x7bffu;
   } else {
-    int q = (int)(f << (32 - T::bits)) >> (32 - T::bits);
-    return (float)q * s;
+    if (mn == 0.0f) mn = 0.0f;                // a zero minimum is +0
+    p.z = rd16(mn);
+    p.tz = h2f(p.z);
+    const float d = mx - p.tz;
+    p.s = d > 0.0f ? ru16(d / T::qmax) : 0u;
+    // d <= 0 (constant block): scale +0, codes 0 (inv = 0 gives t = +-0)
+    p.inv = d > 0.0f ? 1.0f / h2f(p.s) : 0.0f;
+    p.sat = p.s == 0x7bffu || p.z == 0xfbffu;
+  }
+  return p;
+}
+
+// Quantizes N values of a block with its parameters.  For fp8 an all-zero
+// block (s = 0) must give code 0x00 even for -0 inputs: the codes are masked.
+template <int C, int N>
+__device__ __forceinline__ void quantize_values(const float (&v)[N], const BlockParams<C>& p,
+                                                uint32_t (&w)[(N * CodecT<C>::bits + 31) / 32]) {
+  using T = CodecT<C>;
+  float t[N];
+#pragma unroll
+  for (int i = 0; i < N; i++) t[i] = T::asym ? (v[i] - p.tz) * p.inv : v[i] * p.inv;
+  encode<C, N>(t, p.sat, w);
+  if constexpr (T::fp8) {
+    const uint32_t keep = p.s != 0u ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int k = 0; k < N / 4; k++) w[k] &= keep;
   }
 }
 

@@ -12,11 +12,19 @@
 // item 2), with the symmetric/asymmetric integer codecs of "Add quickreduce
 // as alternative to custom allreduce" (vLLM PR #16804, PR description).
 //
-// Every kernel is HBM-streaming: one 64-lane wave handles 32 blocks = 1024
-// elements, each lane a 16-element slice; every plane is read and written
-// with consecutive lanes on consecutive addresses (128-bit accesses for the
-// 16-bit data and the 8-bit codes, 96/64-bit for 6/4-bit codes).  No LDS and
-// no MFMA: nothing here is a contraction.
+// Every kernel streams HBM; nothing is a contraction, so no MFMA and no LDS.
+//   - k_quantize and k_dequant give each lane one quarter block (8 elements
+//     = 16 contiguous bytes of 16-bit data, consecutive lanes on consecutive
+//     quarters), four quarters per lane issued before any is used.  The four
+//     lanes of a block share its statistics through DPP quad permutes and
+//     each computes the block's scale itself (a few instructions, instead of
+//     a round trip through LDS).
+//   - k_stage1 gives each lane a whole block: W code blocks of 16/24/32
+//     contiguous bytes and W scales in, one code block and scale out; the
+//     per-block work (max/min, two divisions, rounding of the scale) is done
+//     once, which matters because this kernel is the one closest to the
+//     VALU limit (W=2, 4-bit codes: 1.7 bytes of HBM per element).
+//   - the FP kernels give each lane 16-byte chunks, four per lane.
 #include "qr_device.h"
 #include "qr_internal.h"
 
@@ -24,41 +32,15 @@ namespace qr {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPerLane = 4;        // quarters / chunks per lane (k_quantize,
+                                   // k_dequant and the FP kernels)
 
 struct Geo {
   uint32_t n;        // elements per rank
+  uint32_t nb;       // blocks per rank
   uint32_t off_s;    // scale plane offset
   uint32_t off_z;    // zero plane offset
 };
-
-__device__ __forceinline__ int slice_valid(uint32_t slice, uint32_t n) {
-  uint32_t e0 = slice * kSlice;
-  return e0 >= n ? 0 : (n - e0 >= (uint32_t)kSlice ? kSlice : (int)(n - e0));
-}
-
-template <int D>
-__device__ __forceinline__ void load_vals(const uint8_t* x, int valid,
-                                          float (&v)[kSlice]) {
-  u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-  if (valid >= 8) a = *reinterpret_cast<const u32x4*>(x);
-  if (valid >= 16) b = *reinterpret_cast<const u32x4*>(x + 16);
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int k = 0; k < 8; k++) {
-    v[2 * k] = ld16<D>(w[k] & 0xffffu);
-    v[2 * k + 1] = ld16<D>(w[k] >> 16);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_vals(uint8_t* y, int valid,
-                                           const float (&v)[kSlice]) {
-  uint32_t w[8];
-#pragma unroll
-  for (int k = 0; k < 8; k++) w[k] = st16<D>(v[2 * k]) | (st16<D>(v[2 * k + 1]) << 16);
-  if (valid >= 8) *reinterpret_cast<u32x4*>(y) = u32x4{w[0], w[1], w[2], w[3]};
-  if (valid >= 16) *reinterpret_cast<u32x4*>(y + 16) = u32x4{w[4], w[5], w[6], w[7]};
-}
 
 __device__ __forceinline__ uint32_t ld_u16(const uint8_t* p) {
   return *reinterpret_cast<const uint16_t*>(p);
@@ -67,180 +49,308 @@ __device__ __forceinline__ void st_u16(uint8_t* p, uint32_t v) {
   *reinterpret_cast<uint16_t*>(p) = (uint16_t)v;
 }
 
-// acc + dequant(field i).  For symmetric and fp8 codes the product code*s is
-// exact in binary32, so one fused multiply-add rounds exactly like the
-// separate add of the exact product.
+// Bytes of codes of quarter j (0..3) of a block: 8 codes = 8*b bits starting
+// at bit 8*b*j of the block's bitstring.  Returned as words with the first
+// code at bit 0: for 6-bit codes two words hold the 48 bits (quarters 1 and 3
+// start in the middle of a word).
 template <int C>
-__device__ __forceinline__ float accumulate(const SliceWords<C>& r, int i, float s,
-                                            float z, float acc) {
-  using T = CodecT<C>;
-  if constexpr (T::asym) {
-    return acc + dequant_field<C>(r, i, s, z);
-  } else if constexpr (T::fp8) {
-    return __builtin_fmaf(e4m3_dec(get_field<C>(r, i)), s, acc);
-  } else {
-    uint32_t f = get_field<C>(r, i);
-    int q = (int)(f << (32 - T::bits)) >> (32 - T::bits);
-    return __builtin_fmaf((float)q, s, acc);
+struct QuarterIO {
+  static constexpr int b = CodecT<C>::bits;
+  static constexpr int nw = (8 * b + 31) / 32;     // 1 (4-bit), 2 (6/8-bit)
+
+  __device__ static void load(const uint8_t* blk, int j, uint32_t (&w)[nw]) {
+    if constexpr (b == 4) {
+      w[0] = reinterpret_cast<const uint32_t*>(blk)[j];
+    } else if constexpr (b == 8) {
+      const u32x2 q = reinterpret_cast<const u32x2*>(blk)[j];
+      w[0] = q.x;
+      w[1] = q.y;
+    } else {                                         // 6-bit: bits [48j, 48j+48)
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(blk) + ((3 * j) >> 1);
+      const uint32_t a = p[0], c = p[1];
+      const int sh = (j & 1) * 16;
+      w[0] = __builtin_amdgcn_alignbit(c, a, sh);
+      w[1] = c >> sh;
+    }
   }
-}
+};
 
 // ---------------------------------------------------------------------------
-// stage 0
+// stage 0: one quarter block per lane, kPerLane quarters per lane
 
 template <int C, int D>
-__global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires,
-                                                       uint32_t nslices, Geo g) {
+__global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires, Geo g) {
   using T = CodecT<C>;
-  const uint32_t slice = blockIdx.x * kThreads + threadIdx.x;
-  if (slice >= nslices) return;               // nslices is even: pairs stay whole
+  constexpr int nw = (8 * T::bits + 31) / 32;
   const int r = blockIdx.y;
-  const int valid = slice_valid(slice, g.n);
-  float v[kSlice];
-  load_vals<D>(xs.p[r] + (size_t)slice * (2 * kSlice), valid, v);
-  uint32_t code[kSlice], s, z;
-  quantize_slice<C>(v, valid, code, s, z);
-  uint8_t* w = wires.p[r];
-  store_slice<C>(w + (size_t)slice * T::slice_bytes, pack_slice<C>(code));
-  if ((slice & 1u) == 0u) {
-    st_u16(w + g.off_s + (size_t)(slice >> 1) * 2, s);
-    if constexpr (T::asym) st_u16(w + g.off_z + (size_t)(slice >> 1) * 2, z);
+  const uint32_t nq = 4 * g.nb;
+  const uint32_t q0 = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
+  const uint8_t* x = xs.p[r];
+  uint8_t* wire = wires.p[r];
+
+  u32x4 raw[kPerLane];
+#pragma unroll
+  for (int u = 0; u < kPerLane; u++) {
+    const uint32_t q = q0 + u * kThreads;
+    raw[u] = u32x4{0u, 0u, 0u, 0u};
+    if (q < nq && 8 * q < g.n) raw[u] = reinterpret_cast<const u32x4*>(x)[q];
+  }
+#pragma unroll
+  for (int u = 0; u < kPerLane; u++) {
+    const uint32_t q = q0 + u * kThreads;
+    if (q >= nq) break;                 // nq is a multiple of 4: quads stay whole
+    const bool valid = 8 * q < g.n;     // this lane's 8 elements exist
+    float v[8];
+    const uint32_t rw[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      v[2 * k] = ld16<D>(rw[k] & 0xffffu);
+      v[2 * k + 1] = ld16<D>(rw[k] >> 16);
+    }
+    float mx, mn;
+    group_max_min(v, valid, mx, mn);
+    mx = fmaxf(mx, quad_perm<kSwap1>(mx));
+    mn = fminf(mn, quad_perm<kSwap1>(mn));
+    mx = fmaxf(mx, quad_perm<kSwap2>(mx));
+    mn = fminf(mn, quad_perm<kSwap2>(mn));
+    const BlockParams<C> p = block_params<C>(mx, mn);
+    uint32_t w[nw];
+    quantize_values<C, 8>(v, p, w);
+    if (!valid) {                       // slots beyond the buffer hold code 0
+#pragma unroll
+      for (int k = 0; k < nw; k++) w[k] = 0u;
+    }
+    const uint32_t blk = q >> 2;
+    const int j = q & 3;
+    uint8_t* cb = wire + (size_t)blk * T::block_bytes;
+    if constexpr (T::bits == 4) {
+      reinterpret_cast<uint32_t*>(cb)[j] = w[0];
+    } else if constexpr (T::bits == 8) {
+      reinterpret_cast<u32x2*>(cb)[j] = u32x2{w[0], w[1]};
+    } else {
+      // 6-bit: lanes 0 and 2 of the quad each write 96 bits (their own 48
+      // and their odd neighbour's 48)
+      const uint32_t o0 = quad_perm_u<kFromOdd>(w[0]);
+      const uint32_t o1 = quad_perm_u<kFromOdd>(w[1]);
+      if ((j & 1) == 0) {
+        uint32_t* d = reinterpret_cast<uint32_t*>(cb) + 3 * (j >> 1);
+        d[0] = w[0];
+        d[1] = (w[1] & 0xffffu) | (o0 << 16);
+        d[2] = (o0 >> 16) | (o1 << 16);
+      }
+    }
+    if (j == 0) {
+      st_u16(wire + g.off_s + (size_t)blk * 2, p.s);
+      if constexpr (T::asym) st_u16(wire + g.off_z + (size_t)blk * 2, p.z);
+    }
   }
 }
 
-// stages 0 and 2 of FP: dst.p[r] <- src.p[r], 32 bytes per lane
+// stages 0 and 2 of FP: dst.p[r] <- src.p[r], 16-byte chunks
 __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
-                                                   uint32_t nslices, uint32_t n) {
-  const uint32_t slice = blockIdx.x * kThreads + threadIdx.x;
-  if (slice >= nslices) return;
+                                                   uint32_t nchunks) {
+  const uint32_t base = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
   const int r = blockIdx.y;
-  const int valid = slice_valid(slice, n);
-  const uint8_t* s = src.p[r] + (size_t)slice * (2 * kSlice);
-  uint8_t* d = dst.p[r] + (size_t)slice * (2 * kSlice);
-  if (valid >= 8) *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
-  if (valid >= 16)
-    *reinterpret_cast<u32x4*>(d + 16) = *reinterpret_cast<const u32x4*>(s + 16);
+  u32x4 q[kPerLane];
+#pragma unroll
+  for (int j = 0; j < kPerLane; j++) {
+    const uint32_t c = base + j * kThreads;
+    if (c < nchunks) q[j] = reinterpret_cast<const u32x4*>(src.p[r])[c];
+  }
+#pragma unroll
+  for (int j = 0; j < kPerLane; j++) {
+    const uint32_t c = base + j * kThreads;
+    if (c < nchunks) reinterpret_cast<u32x4*>(dst.p[r])[c] = q[j];
+  }
 }
 
 // ---------------------------------------------------------------------------
-// stage 1
+// stage 1: one block per lane
 
 template <int C, int D, int W>
 __global__ __launch_bounds__(kThreads) void k_stage1(InPtrs wires, uint8_t* red,
-                                                     uint32_t slice_lo,
-                                                     uint32_t slice_hi, Geo g) {
+                                                     uint32_t blk_lo, uint32_t blk_hi,
+                                                     Geo g) {
   using T = CodecT<C>;
-  const uint32_t slice = slice_lo + blockIdx.x * kThreads + threadIdx.x;
-  if (slice >= slice_hi) return;
-  const uint32_t blk = slice >> 1;
-  const int valid = slice_valid(slice, g.n);
+  const uint32_t blk = blk_lo + blockIdx.x * kThreads + threadIdx.x;
+  if (blk >= blk_hi) return;
+  const uint32_t e0 = blk * kBlock;
+  const int L = g.n - e0 >= (uint32_t)kBlock ? kBlock : (int)(g.n - e0);
 
-  SliceWords<C> cw[W];
+  uint32_t cw[W][T::words];
   float sc[W], zc[W];
 #pragma unroll
   for (int r = 0; r < W; r++) {
-    cw[r] = load_slice<C>(wires.p[r] + (size_t)slice * T::slice_bytes);
-    sc[r] = h2f(ld_u16(wires.p[r] + g.off_s + (size_t)blk * 2));
+    const uint8_t* cb = wires.p[r] + (size_t)blk * T::block_bytes;
+    if constexpr (T::words == 6) {
+#pragma unroll
+      for (int k = 0; k < 3; k++) {
+        const u32x2 q = reinterpret_cast<const u32x2*>(cb)[k];
+        cw[r][2 * k] = q.x;
+        cw[r][2 * k + 1] = q.y;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < T::words / 4; k++) {
+        const u32x4 q = reinterpret_cast<const u32x4*>(cb)[k];
+        cw[r][4 * k] = q.x; cw[r][4 * k + 1] = q.y;
+        cw[r][4 * k + 2] = q.z; cw[r][4 * k + 3] = q.w;
+      }
+    }
+    sc[r] = h2f(ld_u16(wires.p[r] + g.off_s + (size_t)blk * 2)) * T::unpack_scale;
     zc[r] = T::asym ? h2f(ld_u16(wires.p[r] + g.off_z + (size_t)blk * 2)) : 0.0f;
   }
-  float acc[kSlice];
+  // acc = x0 + x1 + ... in rank order.  A symmetric/fp8 term cv*s is exact,
+  // so acc + cv*s is one fused multiply-add; an asymmetric term cv*s + z is
+  // rounded once (the product is exact) and then added.
+  float acc[kBlock];
 #pragma unroll
-  for (int i = 0; i < kSlice; i++) acc[i] = dequant_field<C>(cw[0], i, sc[0], zc[0]);
+  for (int r = 0; r < W; r++) {
+    float cv[kBlock];
+    code_values<C, kBlock>(cw[r], cv);
 #pragma unroll
-  for (int r = 1; r < W; r++) {
-#pragma unroll
-    for (int i = 0; i < kSlice; i++) acc[i] = accumulate<C>(cw[r], i, sc[r], zc[r], acc[i]);
+    for (int i = 0; i < kBlock; i++) {
+      if constexpr (T::asym) {
+        const float x = __builtin_fmaf(cv[i], sc[r], zc[r]);
+        acc[i] = r == 0 ? x : acc[i] + x;
+      } else {
+        acc[i] = r == 0 ? cv[i] * sc[r] : __builtin_fmaf(cv[i], sc[r], acc[i]);
+      }
+    }
   }
-  uint32_t code[kSlice], s, z;
-  quantize_slice<C>(acc, valid, code, s, z);
-  store_slice<C>(red + (size_t)slice * T::slice_bytes, pack_slice<C>(code));
-  if ((slice & 1u) == 0u) {
-    st_u16(red + g.off_s + (size_t)blk * 2, s);
-    if constexpr (T::asym) st_u16(red + g.off_z + (size_t)blk * 2, z);
+  float mx, mn, gx, gn;
+  group_max_min(acc, true, mx, mn);
+#pragma unroll
+  for (int k = 1; k < 4; k++) {
+    group_max_min(acc + 8 * k, 8 * k < L, gx, gn);
+    mx = fmaxf(mx, gx);
+    mn = fminf(mn, gn);
   }
+  const BlockParams<C> p = block_params<C>(mx, mn);
+  uint32_t w[T::words];
+  quantize_values<C, kBlock>(acc, p, w);
+  if (L < kBlock) {                               // unused slots hold code 0
+#pragma unroll
+    for (int k = 0; k < T::words; k++) {
+      const int first = L * T::bits - 32 * k;     // first unused bit in word k
+      w[k] = first <= 0 ? 0u : first >= 32 ? w[k] : w[k] & ((1u << first) - 1u);
+    }
+  }
+  uint8_t* cb = red + (size_t)blk * T::block_bytes;
+  if constexpr (T::words == 6) {
+#pragma unroll
+    for (int k = 0; k < 3; k++)
+      reinterpret_cast<u32x2*>(cb)[k] = u32x2{w[2 * k], w[2 * k + 1]};
+  } else {
+#pragma unroll
+    for (int k = 0; k < T::words / 4; k++)
+      reinterpret_cast<u32x4*>(cb)[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+  }
+  st_u16(red + g.off_s + (size_t)blk * 2, p.s);
+  if constexpr (T::asym) st_u16(red + g.off_z + (size_t)blk * 2, p.z);
 }
 
+// FP: chunks [c_lo, c_hi) of 8 elements; each lane sums kPerLane chunks
 template <int D, int W>
 __global__ __launch_bounds__(kThreads) void k_stage1_fp(InPtrs xs, uint8_t* red,
-                                                        uint32_t slice_lo,
-                                                        uint32_t slice_hi, uint32_t n) {
-  const uint32_t slice = slice_lo + blockIdx.x * kThreads + threadIdx.x;
-  if (slice >= slice_hi) return;
-  const int valid = slice_valid(slice, n);
-  const size_t off = (size_t)slice * (2 * kSlice);
-  float v[W][kSlice];
+                                                        uint32_t c_lo, uint32_t c_hi) {
+  const uint32_t base = c_lo + blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
+  u32x4 q[kPerLane][W];
 #pragma unroll
-  for (int r = 0; r < W; r++) load_vals<D>(xs.p[r] + off, valid, v[r]);
-  float acc[kSlice];
+  for (int j = 0; j < kPerLane; j++) {
+    const uint32_t c = base + j * kThreads;
 #pragma unroll
-  for (int i = 0; i < kSlice; i++) {
-    acc[i] = v[0][i];
-#pragma unroll
-    for (int r = 1; r < W; r++) acc[i] = acc[i] + v[r][i];
+    for (int r = 0; r < W; r++)
+      q[j][r] = c < c_hi ? reinterpret_cast<const u32x4*>(xs.p[r])[c] : u32x4{0u, 0u, 0u, 0u};
   }
-  store_vals<D>(red + off, valid, acc);
+#pragma unroll
+  for (int j = 0; j < kPerLane; j++) {
+    const uint32_t c = base + j * kThreads;
+    if (c >= c_hi) break;
+    uint32_t out[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      float lo = ld16<D>(q[j][0][k] & 0xffffu), hi = ld16<D>(q[j][0][k] >> 16);
+#pragma unroll
+      for (int r = 1; r < W; r++) {
+        lo = lo + ld16<D>(q[j][r][k] & 0xffffu);
+        hi = hi + ld16<D>(q[j][r][k] >> 16);
+      }
+      out[k] = st16x2<D>(lo, hi);
+    }
+    reinterpret_cast<u32x4*>(red)[c] = u32x4{out[0], out[1], out[2], out[3]};
+  }
 }
 
 // ---------------------------------------------------------------------------
-// stage 2 / dequantize
+// stage 2 / dequantize: one quarter block per lane, kPerLane quarters
 
 template <int C, int D>
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* wire, OutPtrs ys,
-                                                      uint32_t nslices, Geo g) {
+                                                      Geo g) {
   using T = CodecT<C>;
-  const uint32_t slice = blockIdx.x * kThreads + threadIdx.x;
-  if (slice >= nslices) return;
+  using IO = QuarterIO<C>;
   const int r = blockIdx.y;
-  const uint32_t blk = slice >> 1;
-  const int valid = slice_valid(slice, g.n);
-  SliceWords<C> cw = load_slice<C>(wire + (size_t)slice * T::slice_bytes);
-  float s = h2f(ld_u16(wire + g.off_s + (size_t)blk * 2));
-  float z = T::asym ? h2f(ld_u16(wire + g.off_z + (size_t)blk * 2)) : 0.0f;
-  float v[kSlice];
+  const uint32_t nq = (g.n + 7) / 8;                // quarters that hold data
+  const uint32_t q0 = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
+  uint32_t w[kPerLane][IO::nw];
+  float s[kPerLane], z[kPerLane];
 #pragma unroll
-  for (int i = 0; i < kSlice; i++) v[i] = dequant_field<C>(cw, i, s, z);
-  store_vals<D>(ys.p[r] + (size_t)slice * (2 * kSlice), valid, v);
+  for (int u = 0; u < kPerLane; u++) {
+    const uint32_t q = q0 + u * kThreads;
+    if (q < nq) {
+      const uint32_t blk = q >> 2;
+      IO::load(wire + (size_t)blk * T::block_bytes, q & 3, w[u]);
+      s[u] = h2f(ld_u16(wire + g.off_s + (size_t)blk * 2)) * T::unpack_scale;
+      z[u] = T::asym ? h2f(ld_u16(wire + g.off_z + (size_t)blk * 2)) : 0.0f;
+    }
+  }
+  uint8_t* y = ys.p[r];
+#pragma unroll
+  for (int u = 0; u < kPerLane; u++) {
+    const uint32_t q = q0 + u * kThreads;
+    if (q >= nq) break;
+    float cv[8];
+    code_values<C, 8>(w[u], cv);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      v[i] = T::asym ? __builtin_fmaf(cv[i], s[u], z[u]) : cv[i] * s[u];
+    reinterpret_cast<u32x4*>(y)[q] = u32x4{st16x2<D>(v[0], v[1]), st16x2<D>(v[2], v[3]),
+                                           st16x2<D>(v[4], v[5]), st16x2<D>(v[6], v[7])};
+  }
 }
 
 // ---------------------------------------------------------------------------
 // dispatch
 
 Geo geo(const Layout& L) {
-  return Geo{(uint32_t)L.n, (uint32_t)L.off_s, (uint32_t)L.off_z};
+  return Geo{(uint32_t)L.n, (uint32_t)L.nb, (uint32_t)L.off_s, (uint32_t)L.off_z};
 }
 
-dim3 grid_for(size_t slices, int ranks) {
-  return dim3((unsigned)((slices + kThreads - 1) / kThreads), (unsigned)ranks, 1);
-}
-
-template <int C, int D>
-void q_launch(int W, const InPtrs& xs, const OutPtrs& wires, const Layout& L,
-              hipStream_t st) {
-  hipLaunchKernelGGL((k_quantize<C, D>), grid_for(L.nslices, W), dim3(kThreads), 0,
-                     st, xs, wires, (uint32_t)L.nslices, geo(L));
-}
-
-template <int C, int D>
-void dq_launch(int W, const uint8_t* wire, const OutPtrs& ys, const Layout& L,
-               hipStream_t st) {
-  hipLaunchKernelGGL((k_dequant<C, D>), grid_for(L.nslices, W), dim3(kThreads), 0,
-                     st, wire, ys, (uint32_t)L.nslices, geo(L));
+unsigned groups(size_t items, size_t per_group) {
+  return (unsigned)((items + per_group - 1) / per_group);
 }
 
 template <int C, int D, int W>
-void s1_launch(const InPtrs& wires, uint8_t* red, uint32_t lo, uint32_t hi,
+void s1_launch(const InPtrs& wires, uint8_t* red, size_t blk_lo, size_t blk_hi,
                const Layout& L, hipStream_t st) {
   if constexpr (C == kFP) {
-    hipLaunchKernelGGL((k_stage1_fp<D, W>), grid_for(hi - lo, 1), dim3(kThreads), 0,
-                       st, wires, red, lo, hi, (uint32_t)L.n);
+    // block-granular range in 8-element chunks (a partial last block holds
+    // fewer than 4 chunks)
+    const uint32_t c_lo = (uint32_t)(4 * blk_lo);
+    const uint32_t c_hi = (uint32_t)(blk_hi * 4 < L.n / 8 ? blk_hi * 4 : L.n / 8);
+    hipLaunchKernelGGL((k_stage1_fp<D, W>), dim3(groups(c_hi - c_lo, kThreads * kPerLane)),
+                       dim3(kThreads), 0, st, wires, red, c_lo, c_hi);
   } else {
-    hipLaunchKernelGGL((k_stage1<C, D, W>), grid_for(hi - lo, 1), dim3(kThreads), 0,
-                       st, wires, red, lo, hi, geo(L));
+    hipLaunchKernelGGL((k_stage1<C, D, W>), dim3(groups(blk_hi - blk_lo, kThreads)),
+                       dim3(kThreads), 0, st, wires, red, (uint32_t)blk_lo,
+                       (uint32_t)blk_hi, geo(L));
   }
 }
 
 template <int C, int D>
-void s1_by_w(int W, const InPtrs& wires, uint8_t* red, uint32_t lo, uint32_t hi,
+void s1_by_w(int W, const InPtrs& wires, uint8_t* red, size_t lo, size_t hi,
              const Layout& L, hipStream_t st) {
   switch (W) {
     case 2: s1_launch<C, D, 2>(wires, red, lo, hi, L, st); break;
@@ -250,31 +360,15 @@ void s1_by_w(int W, const InPtrs& wires, uint8_t* red, uint32_t lo, uint32_t hi,
   }
 }
 
-// calls F<codec, dtype>::run(args...) for the runtime (codec, dtype)
-#define QR_DISPATCH(codec, dtype, FN, ...)                                    \
-  do {                                                                        \
-    const bool bf = (dtype) == kBF16;                                         \
-    switch (codec) {                                                          \
-      case kFP: bf ? FN<kFP, kBF16>(__VA_ARGS__) : FN<kFP, kF16>(__VA_ARGS__); break;     \
-      case kQ8: bf ? FN<kQ8, kBF16>(__VA_ARGS__) : FN<kQ8, kF16>(__VA_ARGS__); break;     \
-      case kQ6: bf ? FN<kQ6, kBF16>(__VA_ARGS__) : FN<kQ6, kF16>(__VA_ARGS__); break;     \
-      case kQ4: bf ? FN<kQ4, kBF16>(__VA_ARGS__) : FN<kQ4, kF16>(__VA_ARGS__); break;     \
-      case kFP8: bf ? FN<kFP8, kBF16>(__VA_ARGS__) : FN<kFP8, kF16>(__VA_ARGS__); break;  \
-      case kQ8A: bf ? FN<kQ8A, kBF16>(__VA_ARGS__) : FN<kQ8A, kF16>(__VA_ARGS__); break;  \
-      case kQ6A: bf ? FN<kQ6A, kBF16>(__VA_ARGS__) : FN<kQ6A, kF16>(__VA_ARGS__); break;  \
-      case kQ4A: bf ? FN<kQ4A, kBF16>(__VA_ARGS__) : FN<kQ4A, kF16>(__VA_ARGS__); break;  \
-      default: break;                                                         \
-    }                                                                         \
-  } while (0)
-
 template <int C, int D>
 void q_dispatch(int W, const InPtrs& xs, const OutPtrs& wires, const Layout& L,
                 hipStream_t st) {
   if constexpr (C == kFP) {
-    hipLaunchKernelGGL(k_copy, grid_for(L.nslices, W), dim3(kThreads), 0, st, xs, wires,
-                       (uint32_t)L.nslices, (uint32_t)L.n);
+    hipLaunchKernelGGL(k_copy, dim3(groups(L.n / 8, kThreads * kPerLane), W),
+                       dim3(kThreads), 0, st, xs, wires, (uint32_t)(L.n / 8));
   } else {
-    q_launch<C, D>(W, xs, wires, L, st);
+    hipLaunchKernelGGL((k_quantize<C, D>), dim3(groups(4 * L.nb, kThreads * kPerLane), W),
+                       dim3(kThreads), 0, st, xs, wires, geo(L));
   }
 }
 
@@ -284,12 +378,30 @@ void dq_dispatch(int W, const uint8_t* wire, const OutPtrs& ys, const Layout& L,
   if constexpr (C == kFP) {
     InPtrs src;
     for (int r = 0; r < kMaxRanks; r++) src.p[r] = wire;
-    hipLaunchKernelGGL(k_copy, grid_for(L.nslices, W), dim3(kThreads), 0, st, src, ys,
-                       (uint32_t)L.nslices, (uint32_t)L.n);
+    hipLaunchKernelGGL(k_copy, dim3(groups(L.n / 8, kThreads * kPerLane), W),
+                       dim3(kThreads), 0, st, src, ys, (uint32_t)(L.n / 8));
   } else {
-    dq_launch<C, D>(W, wire, ys, L, st);
+    hipLaunchKernelGGL((k_dequant<C, D>), dim3(groups(L.n / 8, kThreads * kPerLane), W),
+                       dim3(kThreads), 0, st, wire, ys, geo(L));
   }
 }
+
+// calls FN<codec, dtype>(args...) for the runtime (codec, dtype)
+#define QR_DISPATCH(codec, dtype, FN, ...)                                              \
+  do {                                                                                  \
+    const bool bf = (dtype) == kBF16;                                                   \
+    switch (codec) {                                                                    \
+      case kFP: bf ? FN<kFP, kBF16>(__VA_ARGS__) : FN<kFP, kF16>(__VA_ARGS__); break;     \
+      case kQ8: bf ? FN<kQ8, kBF16>(__VA_ARGS__) : FN<kQ8, kF16>(__VA_ARGS__); break;     \
+      case kQ6: bf ? FN<kQ6, kBF16>(__VA_ARGS__) : FN<kQ6, kF16>(__VA_ARGS__); break;     \
+      case kQ4: bf ? FN<kQ4, kBF16>(__VA_ARGS__) : FN<kQ4, kF16>(__VA_ARGS__); break;     \
+      case kFP8: bf ? FN<kFP8, kBF16>(__VA_ARGS__) : FN<kFP8, kF16>(__VA_ARGS__); break;  \
+      case kQ8A: bf ? FN<kQ8A, kBF16>(__VA_ARGS__) : FN<kQ8A, kF16>(__VA_ARGS__); break;  \
+      case kQ6A: bf ? FN<kQ6A, kBF16>(__VA_ARGS__) : FN<kQ6A, kF16>(__VA_ARGS__); break;  \
+      case kQ4A: bf ? FN<kQ4A, kBF16>(__VA_ARGS__) : FN<kQ4A, kF16>(__VA_ARGS__); break;  \
+      default: break;                                                                   \
+    }                                                                                   \
+  } while (0)
 
 }  // namespace
 
@@ -303,8 +415,7 @@ hipError_t launch_stage1(int codec, int dtype, int W, const InPtrs& wires,
                          uint8_t* reduced, size_t blk_lo, size_t blk_hi,
                          const Layout& L, hipStream_t st) {
   if (blk_hi <= blk_lo) return hipSuccess;
-  const uint32_t lo = (uint32_t)(2 * blk_lo), hi = (uint32_t)(2 * blk_hi);
-  QR_DISPATCH(codec, dtype, s1_by_w, W, wires, reduced, lo, hi, L, st);
+  QR_DISPATCH(codec, dtype, s1_by_w, W, wires, reduced, blk_lo, blk_hi, L, st);
   return hipGetLastError();
 }
 

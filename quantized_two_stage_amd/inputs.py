@@ -29,7 +29,7 @@ MB = 1024 * 1024
 CONFIGS = {
     1: dict(W=2, dtype=FP16, n=2048, codecs=(Q8,),
             desc="W=2 fp16 4 KB/rank, Q8 symmetric, N(0,1)"),
-    2: dict(W=2, dtype=FP16, n=32 * MB // 2, codecs=(FP, FP8, Q8, Q6, Q4),
+    2: dict(W=2, dtype=FP16, n=64 * MB // 2, codecs=(FP, FP8, Q8, Q6, Q4),
             desc="W=2 fp16 64 MB/rank, N(0,1) with 0.1% x50 outliers"),
     3: dict(W=4, dtype=BF16, n=None, codecs=(Q4A,),
             sizes=tuple(2 ** k for k in range(11, 26)),
@@ -37,7 +37,7 @@ CONFIGS = {
     4: dict(W=8, dtype=BF16, n=1024 * 8192, codecs=(Q6,),
             desc="W=8 bf16 16 MB/rank [1024 tokens x 8192 hidden], Q6 symmetric, "
                  "Laplace(0,1) x per-channel scale 10^U(-3,1)"),
-    5: dict(W=8, dtype=FP16, n=32 * MB // 2, codecs=ALL_CODECS,
+    5: dict(W=8, dtype=FP16, n=64 * MB // 2, codecs=ALL_CODECS,
             desc="W=8 fp16 64 MB/rank, adversarial blocks (zero/constant/spike/"
                  "+-max-finite) 1:1:1:1 interleaved with N(0,1) blocks"),
 }

@@ -30,8 +30,11 @@ def _data(cfg, n=None):
     if key not in _cache:
         _cache.clear()
         c = I.CONFIGS[cfg]
-        say("generating config", cfg, "n", n or c["n"])
-        xs_np = I.make(cfg, n=n)
+        n_ = n or c["n"]
+        xs_np = []
+        for r in range(c["W"]):
+            say("generating config", cfg, "n", n_, "rank", r)
+            xs_np.append(I.to_bits(I.draw(cfg, r, n_), c["dtype"]))
         _cache[key] = (xs_np, [dev16(x) for x in xs_np])
     return _cache[key]
 
@@ -46,6 +49,7 @@ def _check_full(qr, cfg, codec, n=None, windows=12, staged=True):
     say("full", label)
     ys = [torch.empty_like(xs[0]) for _ in range(W)]
     ws = qr.alloc_workspace(W, codec, n)
+    ws.fill_(0xA7)           # no reliance on what an earlier call left there
     qr.qr_allreduce_sim(codec, xs, ys, ws, dtype=dtype)
     torch.cuda.synchronize()
     y0 = host16(ys[0])

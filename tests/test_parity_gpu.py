@@ -46,6 +46,9 @@ def _check_case(qr, codec, dtype, xs_np, label):
     # the one-call pipeline gives the same outputs
     ys2 = [torch.empty_like(xs[0]) for _ in range(W)]
     ws = qr.alloc_workspace(W, codec, n)
+    ws.fill_(0xA7)           # no reliance on what an earlier call left there
+    for y in ys2:
+        y.fill_(0x1357)
     qr.qr_allreduce_sim(codec, xs, ys2, ws, dtype=dtype)
     torch.cuda.synchronize()
     for r in range(W):
