@@ -64,6 +64,48 @@ def algorithmic_bytes(stage, W, n, wb):
     return W * (wb + 2 * n)
 
 
+class HipEvents:
+    """HIP events recorded directly on the launch stream.  Created with
+    hipEventDisableSystemFence: an event record then adds no system-scope
+    release (no L2 write-back) between the kernels it brackets, so the time
+    between two records is the kernel's own, as a profiler sees it."""
+    FLAGS = 0x20000000          # hipEventDisableSystemFence
+
+    def __init__(self, count):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(count):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.FLAGS)
+            if rc != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed (%d)" % rc)
+            self.ev.append(e)
+
+    def record(self, i, stream):
+        rc = self.hip.hipEventRecord(self.ev[i], self.ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % rc)
+
+    def ms(self, i, j):
+        out = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(out), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return out.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
 def cpu_baseline(codecs, dtype, xs_np, sample, threads):
     """The oracle as it stands, on blocks [0, sample/32) of every rank (the
     same computation as the full buffers restricted to those blocks), split
@@ -121,19 +163,19 @@ def main():
         bufs[c] = ([qr.alloc_wire(c, n) for _ in range(W)], qr.alloc_wire(c, n), wb)
     stream = torch.cuda.current_stream()
 
-    def one_allreduce(c, ev=None):
+    def one_allreduce(c, ev=None, base=0):
         wires, red, _ = bufs[c]
         if ev is not None:
-            ev[0].record(stream)
+            ev.record(base, stream)
         qr.qr_quantize_ranks(c, xs, wires, dtype=dtype)
         if ev is not None:
-            ev[1].record(stream)
+            ev.record(base + 1, stream)
         qr.qr_reduce_stage1(c, wires, n, red, dtype)
         if ev is not None:
-            ev[2].record(stream)
+            ev.record(base + 2, stream)
         qr.qr_gather_stage2(c, red, ys, dtype=dtype)
         if ev is not None:
-            ev[3].record(stream)
+            ev.record(base + 3, stream)
 
     # check once against qr_allreduce_sim (the one-call entry point)
     ws = qr.alloc_workspace(W, codecs[0], n)
@@ -149,23 +191,23 @@ def main():
             one_allreduce(c)
     torch.cuda.synchronize()
 
-    evs = {c: [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
-               for _ in range(args.steps)] for c in codecs}
+    nc = len(codecs)
+    evs = HipEvents(4 * nc * args.steps)
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        for c in codecs:
-            one_allreduce(c, evs[c][s])
+        for ci, c in enumerate(codecs):
+            one_allreduce(c, evs, 4 * (s * nc + ci))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
     stages = ("quantize", "stage1", "stage2")
     kernels, per_codec = [], {}
-    for c in codecs:
-        d = np.array([[evs[c][s][k].elapsed_time(evs[c][s][k + 1]) for k in range(3)]
-                      for s in range(args.steps)])            # ms
+    for ci, c in enumerate(codecs):
+        d = np.array([[evs.ms(4 * (s * nc + ci) + k, 4 * (s * nc + ci) + k + 1)
+                       for k in range(3)] for s in range(args.steps)])            # ms
         avg = d.mean(axis=0)
         wb = bufs[c][2]
         us = float(avg.sum() * 1e3)
@@ -178,6 +220,7 @@ def main():
                             "us": float(avg[k] * 1e3),
                             "algorithmic_bytes": ab,
                             "gbps": ab / (avg[k] * 1e-3) / 1e9})
+    evs.close()
     total_payload = len(codecs) * 2 * n
     value = total_payload / (ms_per_step * 1e-3) / 1e9
     dom = max(kernels, key=lambda k: k["us"])
@@ -221,14 +264,15 @@ def main():
             wires, red, wb = bufs[c]
             qr.qr_quantize_ranks(c, xs, wires, dtype=dtype)
             ts = []
+            ce = HipEvents(2)
             for _ in range(5):
                 flush.sum()
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
+                ce.record(0, stream)
                 qr.qr_reduce_stage1(c, wires, n, red, dtype)
-                b.record(stream)
+                ce.record(1, stream)
                 torch.cuda.synchronize()
-                ts.append(a.elapsed_time(b))
+                ts.append(ce.ms(0, 1))
+            ce.close()
             us = float(np.median(ts) * 1e3)
             ab = algorithmic_bytes("stage1", W, n, wb)
             cold["stage1/" + I.CODEC_NAMES[c]] = {"us": us, "gbps": ab / (us * 1e-6) / 1e9,

@@ -264,10 +264,11 @@ __device__ __forceinline__ void code_values(const uint32_t* w, float (&cv)[N]) {
 // max and min of p[0..8), or (-inf, +inf) when the group holds no value
 __device__ __forceinline__ void group_max_min(const float* p, bool any, float& mx,
                                               float& mn) {
-  mx = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])),
-             fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7])));
-  mn = fminf(fminf(fminf(p[0], p[1]), fminf(p[2], p[3])),
-             fminf(fminf(p[4], p[5]), fminf(p[6], p[7])));
+  // chains, so that each pair of new values takes one v_max3/v_min3
+  mx = fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(p[0], p[1]), p[2]), p[3]), p[4]), p[5]),
+                   p[6]), p[7]);
+  mn = fminf(fminf(fminf(fminf(fminf(fminf(fminf(p[0], p[1]), p[2]), p[3]), p[4]), p[5]),
+                   p[6]), p[7]);
   mx = any ? mx : -__builtin_inff();
   mn = any ? mn : __builtin_inff();
 }

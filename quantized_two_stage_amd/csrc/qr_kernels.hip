@@ -76,77 +76,123 @@ struct QuarterIO {
 };
 
 // ---------------------------------------------------------------------------
-// stage 0: one quarter block per lane, kPerLane quarters per lane
+// stage 0: one quarter block per lane, kPerLane = 4 quarters per lane.  For
+// each u the four lanes of a quad hold the four quarters of one block, so a
+// quad covers four blocks.  Every lane reduces the max/min of all four
+// blocks across the quad, then lane j alone derives the scale (and zero) of
+// block j and hands 1/s, the zero and two flags to the others (DPP quad
+// broadcasts): each block's divisions and roundings run once, not four times.
+
+// max/min with a quad neighbour.  med3(a, b, +-inf) is max/min(a, b) for
+// non-NaN values; unlike fmaxf/fminf it needs no canonicalization of the
+// DPP-moved operand (one instruction instead of two).
+template <int Ctrl>
+__device__ __forceinline__ float quad_max(float v) {
+  return __builtin_amdgcn_fmed3f(v, quad_perm<Ctrl>(v), __builtin_inff());
+}
+template <int Ctrl>
+__device__ __forceinline__ float quad_min(float v) {
+  return __builtin_amdgcn_fmed3f(v, quad_perm<Ctrl>(v), -__builtin_inff());
+}
+
+// quad_perm [u,u,u,u]: the value of lane u of the quad
+template <int U>
+__device__ __forceinline__ float from_lane(float v) { return quad_perm<U * 0x55>(v); }
+template <int U>
+__device__ __forceinline__ uint32_t from_lane_u(uint32_t v) { return quad_perm_u<U * 0x55>(v); }
 
 template <int C, int D>
 __global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires, Geo g) {
   using T = CodecT<C>;
+  static_assert(kPerLane == 4, "one block per lane of the quad");
   constexpr int nw = (8 * T::bits + 31) / 32;
   const int r = blockIdx.y;
   const uint32_t nq = 4 * g.nb;
   const uint32_t q0 = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
+  const int j = threadIdx.x & 3;                // this lane's quarter of each block
   const uint8_t* x = xs.p[r];
   uint8_t* wire = wires.p[r];
 
-  u32x4 raw[kPerLane];
+  // quarters past the end of the buffer load quarter 0 instead (always
+  // present) and are discarded: no branch around the loads
+  u32x4 raw[4];
 #pragma unroll
-  for (int u = 0; u < kPerLane; u++) {
+  for (int u = 0; u < 4; u++) {
     const uint32_t q = q0 + u * kThreads;
-    raw[u] = u32x4{0u, 0u, 0u, 0u};
-    if (q < nq && 8 * q < g.n) raw[u] = reinterpret_cast<const u32x4*>(x)[q];
+    raw[u] = reinterpret_cast<const u32x4*>(x)[8 * q < g.n ? q : 0u];
   }
+  // every lane stays active through the quad exchanges below; quarters past
+  // the end compute on zeros and store nothing
+  float v[4][8], mx[4], mn[4];
 #pragma unroll
-  for (int u = 0; u < kPerLane; u++) {
-    const uint32_t q = q0 + u * kThreads;
-    if (q >= nq) break;                 // nq is a multiple of 4: quads stay whole
-    const bool valid = 8 * q < g.n;     // this lane's 8 elements exist
-    float v[8];
+  for (int u = 0; u < 4; u++) {
     const uint32_t rw[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      v[2 * k] = ld16<D>(rw[k] & 0xffffu);
-      v[2 * k + 1] = ld16<D>(rw[k] >> 16);
+      v[u][2 * k] = ld16<D>(rw[k] & 0xffffu);
+      v[u][2 * k + 1] = ld16<D>(rw[k] >> 16);
     }
-    float mx, mn;
-    group_max_min(v, valid, mx, mn);
-    mx = fmaxf(mx, quad_perm<kSwap1>(mx));
-    mn = fminf(mn, quad_perm<kSwap1>(mn));
-    mx = fmaxf(mx, quad_perm<kSwap2>(mx));
-    mn = fminf(mn, quad_perm<kSwap2>(mn));
-    const BlockParams<C> p = block_params<C>(mx, mn);
-    uint32_t w[nw];
-    quantize_values<C, 8>(v, p, w);
-    if (!valid) {                       // slots beyond the buffer hold code 0
+    group_max_min(v[u], 8 * (q0 + u * kThreads) < g.n, mx[u], mn[u]);
+    mx[u] = quad_max<kSwap2>(quad_max<kSwap1>(mx[u]));
+    mn[u] = quad_min<kSwap2>(quad_min<kSwap1>(mn[u]));
+  }
+  // lane j: parameters of block j of the quad
+  const float bx = j == 0 ? mx[0] : j == 1 ? mx[1] : j == 2 ? mx[2] : mx[3];
+  const float bn = j == 0 ? mn[0] : j == 1 ? mn[1] : j == 2 ? mn[2] : mn[3];
+  const BlockParams<C> p = block_params<C>(bx, bn);
+  const uint32_t own_blk = (q0 + j * kThreads) >> 2;
+  if (own_blk < g.nb && (q0 + j * kThreads) < nq) {
+    st_u16(wire + g.off_s + (size_t)own_blk * 2, p.s);
+    if constexpr (T::asym) st_u16(wire + g.off_z + (size_t)own_blk * 2, p.z);
+  }
+  const uint32_t flags = (p.sat ? 1u : 0u) | (p.s != 0u ? 2u : 0u);
+  float inv[4], tz[4];
+  uint32_t fl[4];
+  inv[0] = from_lane<0>(p.inv); inv[1] = from_lane<1>(p.inv);
+  inv[2] = from_lane<2>(p.inv); inv[3] = from_lane<3>(p.inv);
+  fl[0] = from_lane_u<0>(flags); fl[1] = from_lane_u<1>(flags);
+  fl[2] = from_lane_u<2>(flags); fl[3] = from_lane_u<3>(flags);
+  if constexpr (T::asym) {
+    tz[0] = from_lane<0>(p.tz); tz[1] = from_lane<1>(p.tz);
+    tz[2] = from_lane<2>(p.tz); tz[3] = from_lane<3>(p.tz);
+  }
 #pragma unroll
-      for (int k = 0; k < nw; k++) w[k] = 0u;
-    }
-    const uint32_t blk = q >> 2;
-    const int j = q & 3;
-    uint8_t* cb = wire + (size_t)blk * T::block_bytes;
-    if constexpr (T::bits == 4) {
-      reinterpret_cast<uint32_t*>(cb)[j] = w[0];
-    } else if constexpr (T::bits == 8) {
-      reinterpret_cast<u32x2*>(cb)[j] = u32x2{w[0], w[1]};
-    } else {
-      // 6-bit: lanes 0 and 2 of the quad each write 96 bits (their own 48
-      // and their odd neighbour's 48)
+  for (int u = 0; u < 4; u++) {
+    const uint32_t q = q0 + u * kThreads;
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) t[i] = T::asym ? (v[u][i] - tz[u]) * inv[u] : v[u][i] * inv[u];
+    uint32_t w[nw];
+    encode<C, 8>(t, (fl[u] & 1u) != 0u, w);
+    // fp8: an all-zero block gives code 0x00 even for -0 inputs; every codec:
+    // quarters beyond the buffer hold code 0
+    const bool keep = 8 * q < g.n && (!T::fp8 || (fl[u] & 2u) != 0u);
+#pragma unroll
+    for (int k = 0; k < nw; k++) w[k] = keep ? w[k] : 0u;
+    uint8_t* cb = wire + (size_t)(q >> 2) * T::block_bytes;
+    if constexpr (T::bits == 6) {
+      // lanes 0 and 2 of the quad each write 96 bits (their own 48 and their
+      // odd neighbour's 48)
       const uint32_t o0 = quad_perm_u<kFromOdd>(w[0]);
       const uint32_t o1 = quad_perm_u<kFromOdd>(w[1]);
-      if ((j & 1) == 0) {
+      if (q < nq && (j & 1) == 0) {
         uint32_t* d = reinterpret_cast<uint32_t*>(cb) + 3 * (j >> 1);
         d[0] = w[0];
         d[1] = (w[1] & 0xffffu) | (o0 << 16);
         d[2] = (o0 >> 16) | (o1 << 16);
       }
-    }
-    if (j == 0) {
-      st_u16(wire + g.off_s + (size_t)blk * 2, p.s);
-      if constexpr (T::asym) st_u16(wire + g.off_z + (size_t)blk * 2, p.z);
+    } else if (q < nq) {
+      if constexpr (T::bits == 4)
+        reinterpret_cast<uint32_t*>(cb)[j] = w[0];
+      else
+        reinterpret_cast<u32x2*>(cb)[j] = u32x2{w[0], w[1]};
     }
   }
 }
 
-// stages 0 and 2 of FP: dst.p[r] <- src.p[r], 16-byte chunks
+// stages 0 and 2 of FP: dst.p[r] <- src.p[r], 16-byte chunks (Stage only
+// names the two uses apart in profiles)
+template <int Stage>
 __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
                                                    uint32_t nchunks) {
   const uint32_t base = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
@@ -155,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
 #pragma unroll
   for (int j = 0; j < kPerLane; j++) {
     const uint32_t c = base + j * kThreads;
-    if (c < nchunks) q[j] = reinterpret_cast<const u32x4*>(src.p[r])[c];
+    q[j] = reinterpret_cast<const u32x4*>(src.p[r])[c < nchunks ? c : 0u];
   }
 #pragma unroll
   for (int j = 0; j < kPerLane; j++) {
@@ -261,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1_fp(InPtrs xs, uint8_t* red,
     const uint32_t c = base + j * kThreads;
 #pragma unroll
     for (int r = 0; r < W; r++)
-      q[j][r] = c < c_hi ? reinterpret_cast<const u32x4*>(xs.p[r])[c] : u32x4{0u, 0u, 0u, 0u};
+      q[j][r] = reinterpret_cast<const u32x4*>(xs.p[r])[c < c_hi ? c : c_lo];
   }
 #pragma unroll
   for (int j = 0; j < kPerLane; j++) {
@@ -297,13 +343,11 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* wire, OutPt
   float s[kPerLane], z[kPerLane];
 #pragma unroll
   for (int u = 0; u < kPerLane; u++) {
-    const uint32_t q = q0 + u * kThreads;
-    if (q < nq) {
-      const uint32_t blk = q >> 2;
-      IO::load(wire + (size_t)blk * T::block_bytes, q & 3, w[u]);
-      s[u] = h2f(ld_u16(wire + g.off_s + (size_t)blk * 2)) * T::unpack_scale;
-      z[u] = T::asym ? h2f(ld_u16(wire + g.off_z + (size_t)blk * 2)) : 0.0f;
-    }
+    const uint32_t q = q0 + u * kThreads < nq ? q0 + u * kThreads : 0u;  // no branch
+    const uint32_t blk = q >> 2;
+    IO::load(wire + (size_t)blk * T::block_bytes, q & 3, w[u]);
+    s[u] = h2f(ld_u16(wire + g.off_s + (size_t)blk * 2)) * T::unpack_scale;
+    z[u] = T::asym ? h2f(ld_u16(wire + g.off_z + (size_t)blk * 2)) : 0.0f;
   }
   uint8_t* y = ys.p[r];
 #pragma unroll
@@ -364,7 +408,7 @@ template <int C, int D>
 void q_dispatch(int W, const InPtrs& xs, const OutPtrs& wires, const Layout& L,
                 hipStream_t st) {
   if constexpr (C == kFP) {
-    hipLaunchKernelGGL(k_copy, dim3(groups(L.n / 8, kThreads * kPerLane), W),
+    hipLaunchKernelGGL(k_copy<0>, dim3(groups(L.n / 8, kThreads * kPerLane), W),
                        dim3(kThreads), 0, st, xs, wires, (uint32_t)(L.n / 8));
   } else {
     hipLaunchKernelGGL((k_quantize<C, D>), dim3(groups(4 * L.nb, kThreads * kPerLane), W),
@@ -378,7 +422,7 @@ void dq_dispatch(int W, const uint8_t* wire, const OutPtrs& ys, const Layout& L,
   if constexpr (C == kFP) {
     InPtrs src;
     for (int r = 0; r < kMaxRanks; r++) src.p[r] = wire;
-    hipLaunchKernelGGL(k_copy, dim3(groups(L.n / 8, kThreads * kPerLane), W),
+    hipLaunchKernelGGL(k_copy<2>, dim3(groups(L.n / 8, kThreads * kPerLane), W),
                        dim3(kThreads), 0, st, src, ys, (uint32_t)(L.n / 8));
   } else {
     hipLaunchKernelGGL((k_dequant<C, D>), dim3(groups(L.n / 8, kThreads * kPerLane), W),
