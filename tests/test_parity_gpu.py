@@ -245,3 +245,35 @@ def test_nondefault_stream(qr):
     want = O.allreduce(codec, O.FP16, xs_np)
     for r in range(W):
         assert_within_ulp(host16(ys[r]), want[r], O.FP16, "stream y")
+
+
+@pytest.mark.parametrize("dtype", (O.FP16, O.BF16), ids=("fp16", "bf16"))
+def test_fp8_every_value(qr, dtype):
+    """Every finite fp16 (bf16) value with |v| <= 448 goes through the fp8
+    encoder with t = v exactly: each block is 448 followed by 31 of the
+    values, so its scale is 448/448 = 1.  Codes (every E4M3 code but NaN
+    appears) and the decoded outputs must equal the oracle's."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = (bits.view(np.float16).astype(np.float64) if dtype == O.FP16
+            else pins.torch_bf16_to_f32(bits).astype(np.float64))
+    keep = bits[np.isfinite(vals) & (np.abs(vals) <= 448)]
+    anchor = pins.to_buf([448.0], "fp16" if dtype == O.FP16 else "bf16")[0]
+    nblk = -(-keep.size // 31)
+    x = np.zeros((nblk, 32), np.uint16)
+    x[:, 0] = anchor
+    body = np.zeros(nblk * 31, np.uint16)
+    body[:keep.size] = keep
+    x[:, 1:] = body.reshape(nblk, 31)
+    x = x.reshape(-1)
+    say("fp8 every value", dtype, x.size)
+    xd = dev16(x)
+    wire = qr.alloc_wire(O.FP8, x.size)
+    qr.qr_quantize(O.FP8, xd, wire, dtype=dtype)
+    y = torch.empty_like(xd)
+    qr.qr_dequantize(O.FP8, wire, y, dtype=dtype)
+    torch.cuda.synchronize()
+    rw = O.quantize(O.FP8, dtype, x)
+    assert_bytes_equal(hostu8(wire), rw, "fp8 wire")
+    codes = set(hostu8(wire)[:32 * nblk].tolist())
+    assert len(codes) >= 250, len(codes)
+    assert_within_ulp(host16(y), O.dequantize(O.FP8, dtype, rw, x.size), dtype, "fp8 y", ulps=0)
