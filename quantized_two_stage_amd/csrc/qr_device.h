@@ -123,6 +123,32 @@ __device__ __forceinline__ uint32_t rint_bits(float c) {
   return __builtin_bit_cast(uint32_t, c + kRoundMagic);
 }
 
+// a / D, correctly rounded, for the integer codecs' divisors (D = 127, 31,
+// 7, 255, 63, 15): q0 = a*R with R = RN(1/D), then one residual step
+// q0 + RN(a - q0*D)*R with two fused multiply-adds.  For each of these D this
+// equals the IEEE quotient for every positive binary32 a (checked
+// exhaustively on gfx950 by tests/gpu_arith_check.hip).  fp8's divisor 448
+// does not have this property for subnormal a and keeps the IEEE division.
+template <int D>
+__device__ __forceinline__ float div_by(float a) {
+  if constexpr (D == 448) {
+    return a / 448.0f;
+  } else {
+    constexpr float R = 1.0f / (float)D;
+    const float q0 = a * R;
+    return __builtin_fmaf(__builtin_fmaf(-q0, (float)D, a), R, q0);
+  }
+}
+
+// 1/s, correctly rounded, for s a positive finite binary16 value: the
+// hardware reciprocal (within 1 ulp) and one Newton step.  Equals the IEEE
+// quotient for every such s (checked exhaustively by
+// tests/gpu_arith_check.hip).
+__device__ __forceinline__ float recip_f16(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  return __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+}
+
 // value held by another lane of this lane's quad (DPP quad permute)
 template <int Ctrl>
 __device__ __forceinline__ float quad_perm(float v) {
@@ -295,19 +321,19 @@ __device__ __forceinline__ BlockParams<C> block_params(float mx, float mn) {
   if constexpr (!T::asym) {
     const float a = fmaxf(fabsf(mx), fabsf(mn));
     // a constant block takes its own magnitude as the scale
-    const float arg = (mx == mn) ? a : a / T::qmax;
+    const float arg = (mx == mn) ? a : div_by<(int)T::qmax>(a);
     p.s = a != 0.0f ? ru16(arg) : 0u;
     // all-zero block: scale +0 and codes 0 (inv = 0 gives t = +-0)
-    p.inv = a != 0.0f ? 1.0f / h2f(p.s) : 0.0f;
+    p.inv = a != 0.0f ? recip_f16(h2f(p.s)) : 0.0f;
     p.sat = p.s == 0x7bffu;
   } else {
     if (mn == 0.0f) mn = 0.0f;                // a zero minimum is +0
     p.z = rd16(mn);
     p.tz = h2f(p.z);
     const float d = mx - p.tz;
-    p.s = d > 0.0f ? ru16(d / T::qmax) : 0u;
+    p.s = d > 0.0f ? ru16(div_by<(int)T::qmax>(d)) : 0u;
     // d <= 0 (constant block): scale +0, codes 0 (inv = 0 gives t = +-0)
-    p.inv = d > 0.0f ? 1.0f / h2f(p.s) : 0.0f;
+    p.inv = d > 0.0f ? recip_f16(h2f(p.s)) : 0.0f;
     p.sat = p.s == 0x7bffu || p.z == 0xfbffu;
   }
   return p;

@@ -1,0 +1,156 @@
+// gpu_arith_check.hip -- test program: exhaustive checks, on the GPU, of the
+// arithmetic identities the kernels in quantized_two_stage_amd/csrc rely on.
+// Each device helper of qr_device.h is compared with a plain reference
+// written here, for every input in its domain:
+//   1. div_by<D>(a) == a / D (IEEE) for every positive finite binary32 a,
+//      D = 127, 31, 7, 255, 63, 15
+//   2. recip_f16(s) == 1 / s (IEEE) for every positive finite binary16 s
+//   3. rint_bits(c) holds round-half-even(c) in its low bits, |c| <= 256
+//   4. e4m3_pack2 (v_cvt_pk_fp8_f32) == nearest-even E4M3FN with saturation
+//      for every binary32 |t| <= 464, both halves of the word, both signs
+//   5. e4m3_dec<k> (v_cvt_f32_fp8) == exact E4M3FN value, all codes, k = 0..3
+//   6. f2bf (v_cvt_pk_bf16_f32) == nearest-even on the bit pattern for every
+//      non-NaN binary32
+// Prints one line per check and exits 0 only if every count is zero.
+// Grid-stride loops with explicit bounds; counters in one small array.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../quantized_two_stage_amd/csrc/qr_device.h"
+
+using namespace qr;
+
+enum { kDiv = 0, kRcp = 6, kRint = 7, kEnc = 8, kDec = 9, kBf = 10, kSlots = 12 };
+
+__device__ void miss(uint32_t* c, int slot) { atomicAdd(&c[slot], 1u); }
+
+template <int D>
+__global__ void k_div(uint32_t* c, int slot) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x + 1; i < 0x7f800000ull;
+       i += stride) {
+    const float a = __builtin_bit_cast(float, (uint32_t)i);
+    if (__builtin_bit_cast(uint32_t, div_by<D>(a)) != __builtin_bit_cast(uint32_t, a / (float)D))
+      miss(c, slot);
+  }
+}
+
+__global__ void k_rcp(uint32_t* c) {
+  const uint32_t h = blockIdx.x * blockDim.x + threadIdx.x + 1;
+  if (h >= 0x7c00u) return;
+  const float s = h2f(h);
+  if (__builtin_bit_cast(uint32_t, recip_f16(s)) != __builtin_bit_cast(uint32_t, 1.0f / s))
+    miss(c, kRcp);
+}
+
+__global__ void k_rint(uint32_t* c) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2ull * 0x43800001ull;
+       i += stride) {
+    const uint32_t u = (uint32_t)(i % 0x43800001ull) | (i >= 0x43800001ull ? 0x80000000u : 0u);
+    const float x = __builtin_bit_cast(float, u);         // |x| <= 256
+    const int want = (int)__builtin_rintf(x);
+    if ((rint_bits(x) & 0x3ffu) != ((uint32_t)want & 0x3ffu)) miss(c, kRint);
+  }
+}
+
+// reference E4M3FN encoder: nearest, ties to even, saturating at 448,
+// sign kept; from the format's value grid
+__device__ uint32_t e4m3_ref(float t) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, t);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(t);
+  if (a >= 448.0f) return sign | 0x7eu;
+  const int e = a < 0.015625f ? -6 : (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xff) - 127;
+  const float step = __builtin_ldexpf(1.0f, e - 3);       // grid spacing at a
+  const float m = __builtin_rintf(a / step);              // a/step is exact
+  const float r = m * step;                               // exact
+  if (r == 0.0f) return sign;
+  if (r < 0.015625f) return sign | (uint32_t)(r * 512.0f);
+  const int er = (int)((__builtin_bit_cast(uint32_t, r) >> 23) & 0xff) - 127;
+  const uint32_t frac = (__builtin_bit_cast(uint32_t, r) >> 20) & 7u;
+  return sign | ((uint32_t)(er + 7) << 3) | frac;
+}
+
+__global__ void k_enc(uint32_t* c) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  const uint64_t end = 0x43e80001ull;                     // |t| <= 464
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < end; i += stride) {
+    const float t = __builtin_bit_cast(float, (uint32_t)i);
+    const uint32_t lo = e4m3_pack2(t, -t, 0x5a5a0000u, false);
+    const uint32_t hi = e4m3_pack2(-t, t, 0x00003c3cu, true);
+    const uint32_t rp = e4m3_ref(t), rn = e4m3_ref(-t);
+    if (lo != (0x5a5a0000u | rp | (rn << 8)) || hi != (0x00003c3cu | (rn << 16) | (rp << 24)))
+      miss(c, kEnc);
+  }
+}
+
+__global__ void k_dec(uint32_t* c) {
+  const uint32_t code = threadIdx.x;                      // 0..255
+  if (code >= 256u || (code & 0x7fu) == 0x7fu) return;    // NaN codes
+  const uint32_t e = (code >> 3) & 0xfu, m = code & 7u;
+  float v = e == 0 ? __builtin_ldexpf((float)m, -9) : __builtin_ldexpf(1.0f + m / 8.0f, (int)e - 7);
+  v = (code & 0x80u) ? -v : v;
+  const uint32_t want = __builtin_bit_cast(uint32_t, v);
+  const uint32_t w = 0x11223344u;
+  if (__builtin_bit_cast(uint32_t, e4m3_dec<0>((w & 0xffffff00u) | code)) != want) miss(c, kDec);
+  if (__builtin_bit_cast(uint32_t, e4m3_dec<1>((w & 0xffff00ffu) | (code << 8))) != want) miss(c, kDec);
+  if (__builtin_bit_cast(uint32_t, e4m3_dec<2>((w & 0xff00ffffu) | (code << 16))) != want) miss(c, kDec);
+  if (__builtin_bit_cast(uint32_t, e4m3_dec<3>((w & 0x00ffffffu) | (code << 24))) != want) miss(c, kDec);
+}
+
+__global__ void k_bf(uint32_t* c) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32); i += stride) {
+    const uint32_t u = (uint32_t)i;
+    if ((u & 0x7fffffffu) > 0x7f800000u) continue;        // NaN
+    const uint32_t want = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    if (f2bf(__builtin_bit_cast(float, u)) != want) miss(c, kBf);
+  }
+}
+
+#define CK(x)                                                                       \
+  do {                                                                              \
+    hipError_t e_ = (x);                                                            \
+    if (e_ != hipSuccess) {                                                         \
+      printf("HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__);         \
+      return 2;                                                                     \
+    }                                                                               \
+  } while (0)
+
+int main() {
+  uint32_t* c;
+  CK(hipMalloc(&c, kSlots * sizeof(uint32_t)));
+  CK(hipMemset(c, 0, kSlots * sizeof(uint32_t)));
+  k_div<127><<<8192, 256>>>(c, kDiv + 0);
+  k_div<31><<<8192, 256>>>(c, kDiv + 1);
+  k_div<7><<<8192, 256>>>(c, kDiv + 2);
+  k_div<255><<<8192, 256>>>(c, kDiv + 3);
+  k_div<63><<<8192, 256>>>(c, kDiv + 4);
+  k_div<15><<<8192, 256>>>(c, kDiv + 5);
+  k_rcp<<<(0x7c00 + 255) / 256, 256>>>(c);
+  k_rint<<<8192, 256>>>(c);
+  k_enc<<<8192, 256>>>(c);
+  k_dec<<<1, 256>>>(c);
+  k_bf<<<8192, 256>>>(c);
+  CK(hipGetLastError());
+  CK(hipDeviceSynchronize());
+  uint32_t h[kSlots];
+  CK(hipMemcpy(h, c, sizeof h, hipMemcpyDeviceToHost));
+  CK(hipFree(c));
+  const char* div_names[6] = {"127", "31", "7", "255", "63", "15"};
+  uint32_t total = 0;
+  for (int k = 0; k < 6; k++) {
+    printf("div_by<%s>: %u mismatches over all positive finite binary32\n", div_names[k], h[kDiv + k]);
+    total += h[kDiv + k];
+  }
+  printf("recip_f16: %u mismatches over all positive finite binary16\n", h[kRcp]);
+  printf("rint_bits: %u mismatches over all |c| <= 256\n", h[kRint]);
+  printf("e4m3_pack2: %u mismatches over all |t| <= 464\n", h[kEnc]);
+  printf("e4m3_dec: %u mismatches over all non-NaN codes, 4 byte positions\n", h[kDec]);
+  printf("f2bf: %u mismatches over all non-NaN binary32\n", h[kBf]);
+  total += h[kRcp] + h[kRint] + h[kEnc] + h[kDec] + h[kBf];
+  printf("%s\n", total == 0 ? "ALL OK" : "MISMATCHES");
+  return total == 0 ? 0 : 1;
+}
