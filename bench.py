@@ -6,11 +6,21 @@ FP, fp8, Q8, Q6, Q4 symmetric), each as its three launches: quantize all
 ranks, fused stage 1, stage 2 -- exactly the launches qr_allreduce_sim makes.
 Inputs are resident in HBM before the timed region starts.
 
+Two passes of the same K steps:
+  1. the timed region: each allreduce is one qr_allreduce_sim call (its
+     three launches), nothing else on the stream; `value` and `ms_per_step`
+     come from this pass.
+  2. the instrumented pass: each allreduce as the three staged calls with a
+     HIP event recorded on the launch stream before and after every launch;
+     the per-kernel durations and the roofline come from this pass (an event
+     record between two launches costs the GPU about 2 us, which is why it
+     is kept out of pass 1).
+
 Prints one JSON line: effective GB/s = per-rank payload bytes (2n per
 allreduce) / time, per step over all codecs; per-codec microseconds and
-GB/s; per-kernel durations from HIP events recorded on the launch stream;
-the roofline of the kernel that takes the most time; a cold-cache
-measurement of stage 1; and the CPU oracle timed on a bounded sample.
+GB/s; per-kernel durations; the roofline of the kernel that takes the most
+time; a cold-cache measurement of stage 1; and the CPU oracle timed on a
+bounded sample.
 """
 import argparse
 import hashlib
@@ -177,31 +187,45 @@ def main():
         if ev is not None:
             ev.record(base + 3, stream)
 
-    # check once against qr_allreduce_sim (the one-call entry point)
-    ws = qr.alloc_workspace(W, codecs[0], n)
+    # one workspace per codec for the one-call entry point
+    wss = {c: qr.alloc_workspace(W, c, n) for c in codecs}
+
+    # check once: the staged calls give what the one-call entry point gives
     ys_ref = [torch.empty_like(xs[0]) for _ in range(W)]
-    qr.qr_allreduce_sim(codecs[0], xs, ys_ref, ws, dtype=dtype)
+    qr.qr_allreduce_sim(codecs[0], xs, ys_ref, wss[codecs[0]], dtype=dtype)
     one_allreduce(codecs[0])
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(ys, ys_ref)), "staged != one-call"
-    del ws, ys_ref
+    del ys_ref
 
     for _ in range(args.warmup):
         for c in codecs:
+            qr.qr_allreduce_sim(c, xs, ys, wss[c], dtype=dtype)
             one_allreduce(c)
     torch.cuda.synchronize()
 
-    nc = len(codecs)
-    evs = HipEvents(4 * nc * args.steps)
+    # pass 1: the timed region
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        for ci, c in enumerate(codecs):
-            one_allreduce(c, evs, 4 * (s * nc + ci))
+        for c in codecs:
+            qr.qr_allreduce_sim(c, xs, ys, wss[c], dtype=dtype)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+
+    # pass 2: the same steps, staged, with events around every launch
+    nc = len(codecs)
+    evs = HipEvents(4 * nc * args.steps)
+    print("bench: instrumented pass, %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for s in range(args.steps):
+        for ci, c in enumerate(codecs):
+            one_allreduce(c, evs, 4 * (s * nc + ci))
+    torch.cuda.synchronize()
+    ms_per_step_instr = (time.perf_counter() - t1) * 1e3 / args.steps
 
     stages = ("quantize", "stage1", "stage2")
     kernels, per_codec = [], {}
@@ -289,6 +313,7 @@ def main():
     out = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "ms_per_step_instrumented": ms_per_step_instr,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": "W=%d simulated ranks, %s, %d elements (%d MB) per rank, "

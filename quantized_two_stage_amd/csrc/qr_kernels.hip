@@ -35,6 +35,39 @@ constexpr int kThreads = 256;
 constexpr int kPerLane = 4;        // quarters / chunks per lane (k_quantize,
                                    // k_dequant and the FP kernels)
 
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X):
+// QR_NT_STORE bit mask of the stages (1 = stage 0, 2 = stage 1, 4 = stage 2)
+//             whose streamed outputs are written with non-temporal stores.
+//             Default 5: the wire images of stage 0 (read once, by another
+//             rank) and the outputs of stage 2 (the result).  Lines written
+//             through the caches stay dirty there and the next kernel pays
+//             for their write-back; stage 1's reduced image is kept cached
+//             because stage 2 reads it W times.
+// QR_NT_LOAD  bit mask of the stages whose read-once inputs are loaded with
+//             non-temporal loads (default none: no gain measured).
+#ifndef QR_NT_STORE
+#define QR_NT_STORE 5
+#endif
+#ifndef QR_NT_LOAD
+#define QR_NT_LOAD 0
+#endif
+constexpr int kStage0 = 1, kStage1 = 2, kStage2 = 4;
+
+template <int Stage, typename V>
+__device__ __forceinline__ void st_out(V* p, V v) {
+  if constexpr ((QR_NT_STORE & Stage) != 0)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+template <int Stage, typename V>
+__device__ __forceinline__ V ld_in(const V* p) {
+  if constexpr ((QR_NT_LOAD & Stage) != 0)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
 struct Geo {
   uint32_t n;        // elements per rank
   uint32_t nb;       // blocks per rank
@@ -101,37 +134,25 @@ __device__ __forceinline__ float from_lane(float v) { return quad_perm<U * 0x55>
 template <int U>
 __device__ __forceinline__ uint32_t from_lane_u(uint32_t v) { return quad_perm_u<U * 0x55>(v); }
 
-template <int C, int D>
-__global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires, Geo g) {
+// Quantizes 4 quarters per lane (quarter q0 + 256u, u = 0..3; a quad of lanes
+// holds the 4 quarters of 4 blocks) from their values v[u][0..8): block
+// statistics through quad permutes, lane j computes the parameters of the
+// quad's block j and stores its scale (and zero), then every lane encodes
+// and stores its own quarters.  Quarters at or past q_end store nothing;
+// quarters holding no element (8q >= n) are left out of the statistics and
+// get code 0.  q_end is a multiple of 4, so a quad is wholly in or out.
+template <int C, int Stage>
+__device__ __forceinline__ void quantize_quarters(float (&v)[4][8], uint32_t q0,
+                                                  uint32_t q_end, uint8_t* wire,
+                                                  const Geo& g) {
   using T = CodecT<C>;
-  static_assert(kPerLane == 4, "one block per lane of the quad");
   constexpr int nw = (8 * T::bits + 31) / 32;
-  const int r = blockIdx.y;
-  const uint32_t nq = 4 * g.nb;
-  const uint32_t q0 = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
   const int j = threadIdx.x & 3;                // this lane's quarter of each block
-  const uint8_t* x = xs.p[r];
-  uint8_t* wire = wires.p[r];
-
-  // quarters past the end of the buffer load quarter 0 instead (always
-  // present) and are discarded: no branch around the loads
-  u32x4 raw[4];
-#pragma unroll
-  for (int u = 0; u < 4; u++) {
-    const uint32_t q = q0 + u * kThreads;
-    raw[u] = reinterpret_cast<const u32x4*>(x)[8 * q < g.n ? q : 0u];
-  }
   // every lane stays active through the quad exchanges below; quarters past
-  // the end compute on zeros and store nothing
-  float v[4][8], mx[4], mn[4];
+  // the end compute on stand-in data and store nothing
+  float mx[4], mn[4];
 #pragma unroll
   for (int u = 0; u < 4; u++) {
-    const uint32_t rw[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      v[u][2 * k] = ld16<D>(rw[k] & 0xffffu);
-      v[u][2 * k + 1] = ld16<D>(rw[k] >> 16);
-    }
     group_max_min(v[u], 8 * (q0 + u * kThreads) < g.n, mx[u], mn[u]);
     mx[u] = quad_max<kSwap2>(quad_max<kSwap1>(mx[u]));
     mn[u] = quad_min<kSwap2>(quad_min<kSwap1>(mn[u]));
@@ -140,8 +161,9 @@ __global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires,
   const float bx = j == 0 ? mx[0] : j == 1 ? mx[1] : j == 2 ? mx[2] : mx[3];
   const float bn = j == 0 ? mn[0] : j == 1 ? mn[1] : j == 2 ? mn[2] : mn[3];
   const BlockParams<C> p = block_params<C>(bx, bn);
-  const uint32_t own_blk = (q0 + j * kThreads) >> 2;
-  if (own_blk < g.nb && (q0 + j * kThreads) < nq) {
+  const uint32_t own_q = q0 + j * kThreads;
+  if (own_q < q_end) {
+    const uint32_t own_blk = own_q >> 2;
     st_u16(wire + g.off_s + (size_t)own_blk * 2, p.s);
     if constexpr (T::asym) st_u16(wire + g.off_z + (size_t)own_blk * 2, p.z);
   }
@@ -175,19 +197,54 @@ __global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires,
       // odd neighbour's 48)
       const uint32_t o0 = quad_perm_u<kFromOdd>(w[0]);
       const uint32_t o1 = quad_perm_u<kFromOdd>(w[1]);
-      if (q < nq && (j & 1) == 0) {
+      if (q < q_end && (j & 1) == 0) {
         uint32_t* d = reinterpret_cast<uint32_t*>(cb) + 3 * (j >> 1);
-        d[0] = w[0];
-        d[1] = (w[1] & 0xffffu) | (o0 << 16);
-        d[2] = (o0 >> 16) | (o1 << 16);
+        st_out<Stage>(d, w[0]);
+        st_out<Stage>(d + 1, (w[1] & 0xffffu) | (o0 << 16));
+        st_out<Stage>(d + 2, (o0 >> 16) | (o1 << 16));
       }
-    } else if (q < nq) {
+    } else if (q < q_end) {
       if constexpr (T::bits == 4)
-        reinterpret_cast<uint32_t*>(cb)[j] = w[0];
+        st_out<Stage>(reinterpret_cast<uint32_t*>(cb) + j, w[0]);
       else
-        reinterpret_cast<u32x2*>(cb)[j] = u32x2{w[0], w[1]};
+        st_out<Stage>(reinterpret_cast<u32x2*>(cb) + j, u32x2{w[0], w[1]});
     }
   }
+}
+
+template <int C, int D>
+__device__ __forceinline__ void quantize_tile(const u32x4 (&raw)[4], uint32_t q0,
+                                              uint8_t* wire, const Geo& g) {
+  float v[4][8];
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const uint32_t rw[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      v[u][2 * k] = ld16<D>(rw[k] & 0xffffu);
+      v[u][2 * k + 1] = ld16<D>(rw[k] >> 16);
+    }
+  }
+  quantize_quarters<C, kStage0>(v, q0, 4 * g.nb, wire, g);
+}
+
+__device__ __forceinline__ void load_tile(const uint8_t* x, uint32_t q0, uint32_t n,
+                                          u32x4 (&raw)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const uint32_t q = q0 + u * kThreads;
+    raw[u] = ld_in<kStage0>(reinterpret_cast<const u32x4*>(x) + (8 * q < n ? q : 0u));
+  }
+}
+
+template <int C, int D>
+__global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires, Geo g) {
+  static_assert(kPerLane == 4, "one block per lane of the quad");
+  const int r = blockIdx.y;
+  const uint32_t q0 = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
+  u32x4 raw[4];
+  load_tile(xs.p[r], q0, g.n, raw);
+  quantize_tile<C, D>(raw, q0, wires.p[r], g);
 }
 
 // stages 0 and 2 of FP: dst.p[r] <- src.p[r], 16-byte chunks (Stage only
@@ -195,57 +252,67 @@ __global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires,
 template <int Stage>
 __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
                                                    uint32_t nchunks) {
-  const uint32_t base = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
+  constexpr int kS = Stage == 0 ? kStage0 : kStage2;
   const int r = blockIdx.y;
+  const u32x4* s = reinterpret_cast<const u32x4*>(src.p[r]);
+  u32x4* d = reinterpret_cast<u32x4*>(dst.p[r]);
+  const uint32_t base = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
   u32x4 q[kPerLane];
 #pragma unroll
   for (int j = 0; j < kPerLane; j++) {
     const uint32_t c = base + j * kThreads;
-    q[j] = reinterpret_cast<const u32x4*>(src.p[r])[c < nchunks ? c : 0u];
+    q[j] = ld_in<kS>(s + (c < nchunks ? c : 0u));
   }
 #pragma unroll
   for (int j = 0; j < kPerLane; j++) {
     const uint32_t c = base + j * kThreads;
-    if (c < nchunks) reinterpret_cast<u32x4*>(dst.p[r])[c] = q[j];
+    if (c < nchunks) st_out<kS>(d + c, q[j]);
   }
 }
 
 // ---------------------------------------------------------------------------
 // stage 1: one block per lane
 
-template <int C, int D, int W>
-__global__ __launch_bounds__(kThreads) void k_stage1(InPtrs wires, uint8_t* red,
-                                                     uint32_t blk_lo, uint32_t blk_hi,
-                                                     Geo g) {
-  using T = CodecT<C>;
-  const uint32_t blk = blk_lo + blockIdx.x * kThreads + threadIdx.x;
-  if (blk >= blk_hi) return;
-  const uint32_t e0 = blk * kBlock;
-  const int L = g.n - e0 >= (uint32_t)kBlock ? kBlock : (int)(g.n - e0);
-
-  uint32_t cw[W][T::words];
+// the W code blocks and scales (and zeros) of one block index
+template <int C, int W>
+struct S1In {
+  uint32_t cw[W][CodecT<C>::words];
   float sc[W], zc[W];
+};
+
+template <int C, int W>
+__device__ __forceinline__ void s1_load(const InPtrs& wires, uint32_t blk, const Geo& g,
+                                        S1In<C, W>& in) {
+  using T = CodecT<C>;
 #pragma unroll
   for (int r = 0; r < W; r++) {
     const uint8_t* cb = wires.p[r] + (size_t)blk * T::block_bytes;
     if constexpr (T::words == 6) {
 #pragma unroll
       for (int k = 0; k < 3; k++) {
-        const u32x2 q = reinterpret_cast<const u32x2*>(cb)[k];
-        cw[r][2 * k] = q.x;
-        cw[r][2 * k + 1] = q.y;
+        const u32x2 q = ld_in<kStage1>(reinterpret_cast<const u32x2*>(cb) + k);
+        in.cw[r][2 * k] = q.x;
+        in.cw[r][2 * k + 1] = q.y;
       }
     } else {
 #pragma unroll
       for (int k = 0; k < T::words / 4; k++) {
-        const u32x4 q = reinterpret_cast<const u32x4*>(cb)[k];
-        cw[r][4 * k] = q.x; cw[r][4 * k + 1] = q.y;
-        cw[r][4 * k + 2] = q.z; cw[r][4 * k + 3] = q.w;
+        const u32x4 q = ld_in<kStage1>(reinterpret_cast<const u32x4*>(cb) + k);
+        in.cw[r][4 * k] = q.x; in.cw[r][4 * k + 1] = q.y;
+        in.cw[r][4 * k + 2] = q.z; in.cw[r][4 * k + 3] = q.w;
       }
     }
-    sc[r] = h2f(ld_u16(wires.p[r] + g.off_s + (size_t)blk * 2)) * T::unpack_scale;
-    zc[r] = T::asym ? h2f(ld_u16(wires.p[r] + g.off_z + (size_t)blk * 2)) : 0.0f;
+    in.sc[r] = h2f(ld_u16(wires.p[r] + g.off_s + (size_t)blk * 2)) * T::unpack_scale;
+    in.zc[r] = T::asym ? h2f(ld_u16(wires.p[r] + g.off_z + (size_t)blk * 2)) : 0.0f;
   }
+}
+
+template <int C, int W>
+__device__ __forceinline__ void s1_reduce_store(const S1In<C, W>& in, uint8_t* red,
+                                                uint32_t blk, const Geo& g) {
+  using T = CodecT<C>;
+  const uint32_t e0 = blk * kBlock;
+  const int L = g.n - e0 >= (uint32_t)kBlock ? kBlock : (int)(g.n - e0);
   // acc = x0 + x1 + ... in rank order.  A symmetric/fp8 term cv*s is exact,
   // so acc + cv*s is one fused multiply-add; an asymmetric term cv*s + z is
   // rounded once (the product is exact) and then added.
@@ -253,14 +320,14 @@ __global__ __launch_bounds__(kThreads) void k_stage1(InPtrs wires, uint8_t* red,
 #pragma unroll
   for (int r = 0; r < W; r++) {
     float cv[kBlock];
-    code_values<C, kBlock>(cw[r], cv);
+    code_values<C, kBlock>(in.cw[r], cv);
 #pragma unroll
     for (int i = 0; i < kBlock; i++) {
       if constexpr (T::asym) {
-        const float x = __builtin_fmaf(cv[i], sc[r], zc[r]);
+        const float x = __builtin_fmaf(cv[i], in.sc[r], in.zc[r]);
         acc[i] = r == 0 ? x : acc[i] + x;
       } else {
-        acc[i] = r == 0 ? cv[i] * sc[r] : __builtin_fmaf(cv[i], sc[r], acc[i]);
+        acc[i] = r == 0 ? cv[i] * in.sc[r] : __builtin_fmaf(cv[i], in.sc[r], acc[i]);
       }
     }
   }
@@ -286,17 +353,29 @@ __global__ __launch_bounds__(kThreads) void k_stage1(InPtrs wires, uint8_t* red,
   if constexpr (T::words == 6) {
 #pragma unroll
     for (int k = 0; k < 3; k++)
-      reinterpret_cast<u32x2*>(cb)[k] = u32x2{w[2 * k], w[2 * k + 1]};
+      st_out<kStage1>(reinterpret_cast<u32x2*>(cb) + k, u32x2{w[2 * k], w[2 * k + 1]});
   } else {
 #pragma unroll
     for (int k = 0; k < T::words / 4; k++)
-      reinterpret_cast<u32x4*>(cb)[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+      st_out<kStage1>(reinterpret_cast<u32x4*>(cb) + k,
+                      u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]});
   }
   st_u16(red + g.off_s + (size_t)blk * 2, p.s);
   if constexpr (T::asym) st_u16(red + g.off_z + (size_t)blk * 2, p.z);
 }
 
-// FP: chunks [c_lo, c_hi) of 8 elements; each lane sums kPerLane chunks
+// one lane per block
+template <int C, int D, int W>
+__global__ __launch_bounds__(kThreads) void k_stage1(InPtrs wires, uint8_t* red,
+                                                     uint32_t blk_lo, uint32_t blk_hi,
+                                                     Geo g) {
+  const uint32_t blk = blk_lo + blockIdx.x * kThreads + threadIdx.x;
+  if (blk >= blk_hi) return;
+  S1In<C, W> in;
+  s1_load<C, W>(wires, blk, g, in);
+  s1_reduce_store<C, W>(in, red, blk, g);
+}
+
 template <int D, int W>
 __global__ __launch_bounds__(kThreads) void k_stage1_fp(InPtrs xs, uint8_t* red,
                                                         uint32_t c_lo, uint32_t c_hi) {
@@ -307,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1_fp(InPtrs xs, uint8_t* red,
     const uint32_t c = base + j * kThreads;
 #pragma unroll
     for (int r = 0; r < W; r++)
-      q[j][r] = reinterpret_cast<const u32x4*>(xs.p[r])[c < c_hi ? c : c_lo];
+      q[j][r] = ld_in<kStage1>(reinterpret_cast<const u32x4*>(xs.p[r]) + (c < c_hi ? c : c_lo));
   }
 #pragma unroll
   for (int j = 0; j < kPerLane; j++) {
@@ -324,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1_fp(InPtrs xs, uint8_t* red,
       }
       out[k] = st16x2<D>(lo, hi);
     }
-    reinterpret_cast<u32x4*>(red)[c] = u32x4{out[0], out[1], out[2], out[3]};
+    st_out<kStage1>(reinterpret_cast<u32x4*>(red) + c, u32x4{out[0], out[1], out[2], out[3]});
   }
 }
 
@@ -360,8 +439,9 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* wire, OutPt
 #pragma unroll
     for (int i = 0; i < 8; i++)
       v[i] = T::asym ? __builtin_fmaf(cv[i], s[u], z[u]) : cv[i] * s[u];
-    reinterpret_cast<u32x4*>(y)[q] = u32x4{st16x2<D>(v[0], v[1]), st16x2<D>(v[2], v[3]),
-                                           st16x2<D>(v[4], v[5]), st16x2<D>(v[6], v[7])};
+    st_out<kStage2>(reinterpret_cast<u32x4*>(y) + q,
+                    u32x4{st16x2<D>(v[0], v[1]), st16x2<D>(v[2], v[3]),
+                          st16x2<D>(v[4], v[5]), st16x2<D>(v[6], v[7])});
   }
 }
 
@@ -411,7 +491,8 @@ void q_dispatch(int W, const InPtrs& xs, const OutPtrs& wires, const Layout& L,
     hipLaunchKernelGGL(k_copy<0>, dim3(groups(L.n / 8, kThreads * kPerLane), W),
                        dim3(kThreads), 0, st, xs, wires, (uint32_t)(L.n / 8));
   } else {
-    hipLaunchKernelGGL((k_quantize<C, D>), dim3(groups(4 * L.nb, kThreads * kPerLane), W),
+    hipLaunchKernelGGL((k_quantize<C, D>),
+                       dim3(groups(4 * L.nb, kThreads * kPerLane), W),
                        dim3(kThreads), 0, st, xs, wires, geo(L));
   }
 }
