@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=1 << 25,
                    help="elements per rank of the oracle's sample")
     p.add_argument("--no-cold", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the other workloads (size sweep, W=8)")
     return p.parse_args()
 
 
@@ -114,6 +116,80 @@ class HipEvents:
     def close(self):
         for e in self.ev:
             self.hip.hipEventDestroy(e)
+
+
+def time_each(fn, iters, stream):
+    """Microseconds of each of `iters` calls of fn(), from a pair of HIP
+    events recorded on the launch stream around each call."""
+    ev = HipEvents(2 * iters)
+    for i in range(iters):
+        ev.record(2 * i, stream)
+        fn()
+        ev.record(2 * i + 1, stream)
+    import torch
+    torch.cuda.synchronize()
+    us = [ev.ms(2 * i, 2 * i + 1) * 1e3 for i in range(iters)]
+    ev.close()
+    return us
+
+
+def measure_workload(qr, I, torch, stream, config, n=None, codecs=None, iters=20,
+                     kernels=True, cold=True):
+    """One workload of inputs.CONFIGS: per codec, the simulated allreduce
+    (qr_allreduce_sim) timed call by call (median and min us, effective GB/s
+    = 2n bytes / time); optionally the three kernels timed one by one through
+    the staged calls (us, algorithmic GB/s, fraction of HBM peak) and stage 1
+    after a cache flush."""
+    cfg = I.CONFIGS[config]
+    W, dtype = cfg["W"], cfg["dtype"]
+    n = cfg["n"] if n is None else n
+    codecs = cfg["codecs"] if codecs is None else codecs
+    xs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in I.make(config, n=n)]
+    ys = [torch.empty_like(xs[0]) for _ in range(W)]
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda") if cold else None
+    out = {}
+    for c in codecs:
+        wb = qr.qr_wire_bytes(c, n)
+        ws = qr.alloc_workspace(W, c, n)
+        for _ in range(3):
+            qr.qr_allreduce_sim(c, xs, ys, ws, dtype=dtype)
+        us = time_each(lambda: qr.qr_allreduce_sim(c, xs, ys, ws, dtype=dtype), iters, stream)
+        med = float(np.median(us))
+        r = {"us_median": med, "us_min": float(min(us)),
+             "effective_gbps": 2 * n / (med * 1e-6) / 1e9}
+        if kernels or cold:
+            wires = [qr.alloc_wire(c, n) for _ in range(W)]
+            red = qr.alloc_wire(c, n)
+            launches = {
+                "quantize": lambda: qr.qr_quantize_ranks(c, xs, wires, dtype=dtype),
+                "stage1": lambda: qr.qr_reduce_stage1(c, wires, n, red, dtype),
+                "stage2": lambda: qr.qr_gather_stage2(c, red, ys, dtype=dtype)}
+            for f in launches.values():
+                f()
+        if kernels:
+            r["kernels"] = {}
+            for st, f in launches.items():
+                t = float(np.median(time_each(f, iters, stream)))
+                ab = algorithmic_bytes(st, W, n, wb)
+                r["kernels"][st] = {"us": t, "gbps": ab / (t * 1e-6) / 1e9,
+                                    "frac": ab / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        if cold:
+            ts = []
+            launches["quantize"]()
+            for _ in range(5):
+                flush.sum()
+                ts += time_each(launches["stage1"], 1, stream)
+            t = float(np.median(ts))
+            ab = algorithmic_bytes("stage1", W, n, wb)
+            r["stage1_cold"] = {"us": t, "gbps": ab / (t * 1e-6) / 1e9,
+                                "frac": ab / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        if kernels or cold:
+            del wires, red
+        del ws
+        out[I.CODEC_NAMES[c]] = r
+    del xs, ys, flush
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(codecs, dtype, xs_np, sample, threads):
@@ -303,6 +379,26 @@ def main():
                                                   "frac": ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
         del flush
 
+    extra = None
+    if not args.no_extra:
+        extra = {}
+        for cid in (5, 4):
+            c = I.CONFIGS[cid]
+            print("bench: config %d (%s)" % (cid, c["desc"]), file=sys.stderr, flush=True)
+            extra["config%d" % cid] = {
+                "workload": c["desc"], "W": c["W"], "elements_per_rank": c["n"],
+                "per_codec": measure_workload(qr, I, torch, stream, cid, cold=not args.no_cold)}
+        c = I.CONFIGS[3]
+        print("bench: config 3 size sweep (%s)" % c["desc"], file=sys.stderr, flush=True)
+        sweep = {}
+        for size in c["sizes"]:
+            iters = 100 if 2 * size <= (1 << 20) else 20
+            r = measure_workload(qr, I, torch, stream, 3, n=size, iters=iters,
+                                 kernels=False, cold=False)
+            sweep["%d" % (2 * size)] = r[I.CODEC_NAMES[c["codecs"][0]]]
+        extra["config3_sweep"] = {"workload": c["desc"], "W": c["W"],
+                                  "key": "bytes per rank buffer", "per_size": sweep}
+
     cpu = None
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
@@ -328,6 +424,7 @@ def main():
         "per_codec": per_codec,
         "kernels": kernels,
         "stage1_cold": cold,
+        "other_workloads": extra,
         "device_copy_gbps": copy_gbps,
         "kernel_source_sha": kernel_source_sha(),
     }
