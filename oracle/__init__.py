@@ -59,6 +59,7 @@ def _declare(L):
         "ref_stage1": (i32, [i32, i32, i32, P, sz, P, sz, sz]),
         "ref_stage2": (i32, [i32, i32, i32, P, sz, P, sz, sz]),
         "ref_allreduce": (i32, [i32, i32, i32, P, P, sz, sz, sz]),
+        "ref_oneshot": (i32, [i32, i32, P, P, sz, sz, sz]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -199,4 +200,15 @@ def allreduce(codec, dtype, xs, lo=0, hi=ALL, ys=None, L=None):
         ys = [np.zeros(n, np.uint16) for _ in xs]
     _check((L or lib()).ref_allreduce(len(xs), dtype, codec, _ptrs(xs), _ptrs(ys),
                                       n, lo, hi), "allreduce")
+    return ys
+
+
+def oneshot(dtype, xs, lo=0, hi=ALL, ys=None, L=None):
+    """The one-stage (one-shot) FP allreduce of W raw buffers."""
+    xs = [np.ascontiguousarray(x, dtype=np.uint16) for x in xs]
+    n = xs[0].size
+    if ys is None:
+        ys = [np.zeros(n, np.uint16) for _ in xs]
+    _check((L or lib()).ref_oneshot(len(xs), dtype, _ptrs(xs), _ptrs(ys), n, lo, hi),
+           "oneshot")
     return ys

@@ -14,6 +14,10 @@
  *   - vLLM API docs, vllm.distributed.device_communicators.quick_all_reduce,
  *     QuickReduceRegime (FP=0, INT8=1, INT6=2, INT4=3, NONE=4) and
  *     QuickAllReduce.quick_all_reduce (out-of-place; input never modified).
+ *   - PR #18473's description item 2 and its tp2 timing table name a second,
+ *     one-stage ("1stage", f16 only) allreduce; the review thread of the same
+ *     PR describes it as the one-shot kind (every rank reads every rank's
+ *     buffer and reduces locally), to be used for small buffers.
  *
  * The pages name the formats only.  The readings taken where they are silent
  * (all stated again next to the code that implements them):
@@ -492,4 +496,23 @@ int ref_allreduce(int W, int dtype, int c, const uint16_t* const* xs,
   free(wires);
   free(red);
   return rc;
+}
+
+/* the one-stage (one-shot) allreduce of PR #18473 ("1stage", f16): every
+ * rank reads all W buffers and rounds their binary32 sum, taken in rank
+ * order 0..W-1, once to the buffer type; no wire format is involved.  On
+ * the elements of blocks [blk_lo, blk_hi) (32-element blocks, used here only
+ * as the unit of the range). */
+int ref_oneshot(int W, int dtype, const uint16_t* const* xs, uint16_t* const* ys,
+                size_t n, size_t blk_lo, size_t blk_hi) {
+  if ((dtype != T_FP16 && dtype != T_BF16) || n == 0 || W < 1) return -1;
+  blk_hi = clamp_hi(n, blk_hi);
+  size_t e_lo = blk_lo * BLK, e_hi = blk_hi * BLK < n ? blk_hi * BLK : n;
+  for (size_t i = e_lo; i < e_hi; i++) {
+    float acc = ld(dtype, xs[0][i]);
+    for (int r = 1; r < W; r++) acc = acc + ld(dtype, xs[r][i]);
+    uint16_t y = st(dtype, acc);
+    for (int r = 0; r < W; r++) ys[r][i] = y;
+  }
+  return 0;
 }

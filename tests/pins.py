@@ -365,17 +365,19 @@ def check_constants_exhaustive(L, codecs=QUANT):
             assert bad.size == 0, (codec, dtype, bad[:4], x[bad[:4]], y[bad[:4]])
 
 
-def check_fp_closed_form(L):
-    """FP codec: output = the binary32 sum in rank order 0..W-1, rounded once
-    (numpy float32 additions in that order, then numpy/torch casts)."""
-    g = np.random.default_rng(5)
+def _fp_cases(seed):
+    """Raw inputs of every W in (1, 2, 3, 4, 8) and both buffer types, with
+    the expected allreduce: the binary32 sum in rank order 0..W-1 (numpy
+    float32 additions in that order), rounded once by numpy/torch casts.
+    For W >= 3 a quarter of the elements cancel: one rank holds +2^15, a later
+    one -2^15 and an earlier one 2^-9, so the binary32 sum depends on the
+    order; magnitudes up to 2^10 * N(0,1) also reach the binary16 overflow."""
+    g = np.random.default_rng(seed)
     for W in (1, 2, 3, 4, 8):
         for dtype in (O.FP16, O.BF16):
             n = 8 * int(g.integers(1, 200))
             xs64 = [g.standard_normal(n) * 2.0 ** g.uniform(-10, 10, n) for _ in range(W)]
             if W >= 3:
-                # cancellation: one rank holds +2^15, a later one -2^15 and an
-                # earlier one 2^-9, so the binary32 sum depends on the order
                 idx = g.choice(n, n // 4, replace=False)
                 for e in idx:
                     r = sorted(g.choice(W, 3, replace=False))
@@ -396,9 +398,34 @@ def check_fp_closed_form(L):
                 acc = (acc + v).astype(np.float32)
             want = acc.astype(np.float16).view(np.uint16) if dtype == O.FP16 else \
                 torch_f32_to_bf16(acc)
-            ys = O.allreduce(O.FP, dtype, xs, L=L)
-            for y in ys:
-                assert np.array_equal(y, want), (W, dtype)
+            yield W, dtype, xs, want
+
+
+def check_fp_closed_form(L):
+    """FP codec: output = the binary32 sum in rank order 0..W-1, rounded once."""
+    for W, dtype, xs, want in _fp_cases(5):
+        ys = O.allreduce(O.FP, dtype, xs, L=L)
+        for y in ys:
+            assert np.array_equal(y, want), (W, dtype)
+
+
+def check_oneshot_closed_form(L):
+    """One-stage allreduce: every rank's output = the binary32 sum in rank
+    order 0..W-1, rounded once; also on block sub-ranges (elements outside
+    the range untouched)."""
+    for W, dtype, xs, want in _fp_cases(6):
+        ys = O.oneshot(dtype, xs, L=L)
+        for y in ys:
+            assert np.array_equal(y, want), (W, dtype)
+        n = xs[0].size
+        nb = (n + 31) // 32
+        lo, hi = nb // 3, max(nb // 3 + 1, (2 * nb) // 3)
+        sentinel = [np.full(n, 0xABCD, np.uint16) for _ in range(W)]
+        O.oneshot(dtype, xs, lo, hi, ys=sentinel, L=L)
+        e_lo, e_hi = 32 * lo, min(n, 32 * hi)
+        for y in sentinel:
+            assert np.array_equal(y[e_lo:e_hi], want[e_lo:e_hi]), (W, dtype, "range")
+            assert np.all(y[:e_lo] == 0xABCD) and np.all(y[e_hi:] == 0xABCD), (W, dtype)
 
 
 def _planes(codec, n, wire, L=None):
@@ -565,4 +592,5 @@ def check_golden(L):
 QUICK_CHECKS = [check_golden, check_layout, check_chunks, check_zero_blocks,
                 check_f2h, check_ru_rd, check_e4m3, check_bf16,
                 check_block_codes, check_error_bound, check_idempotent,
-                check_fp_closed_form, check_end_to_end_bound, check_owner_split]
+                check_fp_closed_form, check_oneshot_closed_form, check_end_to_end_bound,
+                check_owner_split]

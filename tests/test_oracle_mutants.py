@@ -65,6 +65,15 @@ MUTANTS = {
     "rd16_negative_rounds_toward_zero": [
         ("if (a < 0.0) return 0x8000 | ref_ru16((float)-a);",
          "if (a < 0.0) return 0x8000 | ref_rd16((float)-a);")],
+    "oneshot_sum_in_reverse_rank_order": [
+        ("float acc = ld(dtype, xs[0][i]);\n    for (int r = 1; r < W; r++) acc = acc + ld(dtype, xs[r][i]);",
+         "float acc = ld(dtype, xs[W - 1][i]);\n    for (int r = W - 2; r >= 0; r--) acc = acc + ld(dtype, xs[r][i]);")],
+    "oneshot_rounds_every_add": [
+        ("for (int r = 1; r < W; r++) acc = acc + ld(dtype, xs[r][i]);",
+         "for (int r = 1; r < W; r++) acc = ld(dtype, st(dtype, acc + ld(dtype, xs[r][i])));")],
+    "oneshot_range_in_elements": [
+        ("size_t e_lo = blk_lo * BLK, e_hi = blk_hi * BLK < n ? blk_hi * BLK : n;",
+         "size_t e_lo = blk_lo, e_hi = blk_hi < n ? blk_hi : n;")],
     "zero_plane_overlaps_scales": [
         ("return align256(ref_scale_offset(c, n) + 2 * nblocks(n));",
          "return align256(ref_scale_offset(c, n));")],
