@@ -134,12 +134,14 @@ def time_each(fn, iters, stream):
 
 
 def measure_workload(qr, I, torch, stream, config, n=None, codecs=None, iters=20,
-                     kernels=True, cold=True):
+                     kernels=True, cold=True, oneshot=True):
     """One workload of inputs.CONFIGS: per codec, the simulated allreduce
     (qr_allreduce_sim) timed call by call (median and min us, effective GB/s
     = 2n bytes / time); optionally the three kernels timed one by one through
     the staged calls (us, algorithmic GB/s, fraction of HBM peak) and stage 1
-    after a cache flush."""
+    after a cache flush; and the one-stage allreduce (qr_allreduce_oneshot,
+    key "1stage"), whose algorithmic bytes are W*(W+1)*2n: every rank reads
+    the W buffers and writes its own."""
     cfg = I.CONFIGS[config]
     W, dtype = cfg["W"], cfg["dtype"]
     n = cfg["n"] if n is None else n
@@ -187,6 +189,19 @@ def measure_workload(qr, I, torch, stream, config, n=None, codecs=None, iters=20
             del wires, red
         del ws
         out[I.CODEC_NAMES[c]] = r
+    if oneshot:
+        # the one-stage allreduce: one launch; every simulated rank reads all
+        # W buffers and writes its own output
+        for _ in range(3):
+            qr.qr_allreduce_oneshot(xs, ys, dtype=dtype)
+        us = time_each(lambda: qr.qr_allreduce_oneshot(xs, ys, dtype=dtype), iters, stream)
+        med = float(np.median(us))
+        ab = W * (W + 1) * 2 * n
+        out["1stage"] = {"us_median": med, "us_min": float(min(us)),
+                         "effective_gbps": 2 * n / (med * 1e-6) / 1e9,
+                         "kernels": {"oneshot": {"us": med, "gbps": ab / (med * 1e-6) / 1e9,
+                                                 "frac": ab / (med * 1e-6) / 1e9 /
+                                                 HBM_PEAK_GBPS}}}
     del xs, ys, flush
     torch.cuda.empty_cache()
     return out
@@ -382,7 +397,7 @@ def main():
     extra = None
     if not args.no_extra:
         extra = {}
-        for cid in (5, 4):
+        for cid in (2, 5, 4):
             c = I.CONFIGS[cid]
             print("bench: config %d (%s)" % (cid, c["desc"]), file=sys.stderr, flush=True)
             extra["config%d" % cid] = {
@@ -395,7 +410,7 @@ def main():
             iters = 100 if 2 * size <= (1 << 20) else 20
             r = measure_workload(qr, I, torch, stream, 3, n=size, iters=iters,
                                  kernels=False, cold=False)
-            sweep["%d" % (2 * size)] = r[I.CODEC_NAMES[c["codecs"][0]]]
+            sweep["%d" % (2 * size)] = r
         extra["config3_sweep"] = {"workload": c["desc"], "W": c["W"],
                                   "key": "bytes per rank buffer", "per_size": sweep}
 

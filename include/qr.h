@@ -148,6 +148,18 @@ int qr_allreduce_sim(int W, qr_dtype dtype, qr_codec codec,
                      const void* const* xs, void* const* ys, size_t n,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/* The one-stage (one-shot) allreduce without a wire format ("1stage", f16,
+ * in PR #18473's description item 2 and its tp2 timing table; the review
+ * thread of that PR proposes it for small buffers, the two-stage one for
+ * large): every rank r reads all W buffers and writes
+ *     ys[r][i] = round_to_dtype(((x_0[i] + x_1[i]) + ...) + x_{W-1}[i]),
+ * the sum taken in binary32 in rank order and rounded once (round to nearest
+ * even; overflow -> inf) -- the same values as qr_allreduce_sim with QR_FP.
+ * One launch on `stream`; W in {2,4,8}; n, alignment and overlap rules as
+ * for every entry point (no workspace). */
+int qr_allreduce_oneshot(int W, qr_dtype dtype, const void* const* xs,
+                         void* const* ys, size_t n, void* stream);
+
 /* Message for the last error returned on this thread ("" if none). */
 const char* qr_last_error(void);
 

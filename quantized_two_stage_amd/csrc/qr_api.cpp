@@ -284,4 +284,25 @@ int qr_allreduce_sim(int W, qr_dtype dtype, qr_codec codec, const void* const* x
                     "stage-2 launch");
 }
 
+int qr_allreduce_oneshot(int W, qr_dtype dtype, const void* const* xs, void* const* ys,
+                         size_t n, void* stream) {
+  QR_TRY(check_kind(QR_FP, dtype, n));
+  if (!w_sim(W)) return fail(QR_ERR_UNSUPPORTED, "W = %d not in {2,4,8}", W);
+  if (xs == nullptr || ys == nullptr) return fail(QR_ERR_ARG, "NULL pointer array");
+  for (int r = 0; r < W; r++) {
+    QR_TRY(check_ptr(xs[r], "xs", r));
+    QR_TRY(check_ptr(ys[r], "ys", r));
+  }
+  QR_TRY(check_disjoint(xs, W, 2 * n, (const void* const*)ys, W, 2 * n));
+  qr::InPtrs in{};
+  qr::OutPtrs out{};
+  for (int r = 0; r < W; r++) {
+    in.p[r] = static_cast<const uint8_t*>(xs[r]);
+    out.p[r] = static_cast<uint8_t*>(ys[r]);
+  }
+  (void)hipGetLastError();
+  return hip_status(qr::launch_oneshot(dtype, W, in, out, n, as_stream(stream)),
+                    "one-stage launch");
+}
+
 }  // extern "C"

@@ -3,7 +3,8 @@
 //   k_quantize   stage 0: binary16/bfloat16 -> codes + scale (+ zero)
 //   k_stage1     stage 1: W wire blocks -> dequantize -> binary32 sum in rank
 //                order -> requantize (one pass over HBM per byte)
-//   k_stage1_fp  stage 1 of the FP codec: sum of the raw buffers, rounded once
+//   k_sum_fp     stage 1 of the FP codec, and the one-stage allreduce: sum of
+//                the raw buffers, rounded once
 //   k_dequant    stage 2 / dequantize: codes -> binary16/bfloat16, W outputs
 //   k_copy       stages 0 and 2 of the FP codec (the wire is the raw data)
 //
@@ -376,9 +377,14 @@ __global__ __launch_bounds__(kThreads) void k_stage1(InPtrs wires, uint8_t* red,
   s1_reduce_store<C, W>(in, red, blk, g);
 }
 
-template <int D, int W>
-__global__ __launch_bounds__(kThreads) void k_stage1_fp(InPtrs xs, uint8_t* red,
-                                                        uint32_t c_lo, uint32_t c_hi) {
+// Sum of W raw buffers over 16-byte chunks [c_lo, c_hi): the binary32 sum
+// in rank order 0..W-1, rounded once to D, into outs.p[blockIdx.y].  Stage 1
+// of the FP codec (one output: the reduced image) and the one-stage
+// allreduce (gridDim.y = W: every rank reads all W buffers and writes its
+// own output).  Stage selects the store policy of the outputs.
+template <int D, int W, int Stage>
+__global__ __launch_bounds__(kThreads) void k_sum_fp(InPtrs xs, OutPtrs outs,
+                                                     uint32_t c_lo, uint32_t c_hi) {
   const uint32_t base = c_lo + blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
   u32x4 q[kPerLane][W];
 #pragma unroll
@@ -388,6 +394,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1_fp(InPtrs xs, uint8_t* red,
     for (int r = 0; r < W; r++)
       q[j][r] = ld_in<kStage1>(reinterpret_cast<const u32x4*>(xs.p[r]) + (c < c_hi ? c : c_lo));
   }
+  u32x4* out_p = reinterpret_cast<u32x4*>(outs.p[blockIdx.y]);
 #pragma unroll
   for (int j = 0; j < kPerLane; j++) {
     const uint32_t c = base + j * kThreads;
@@ -403,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1_fp(InPtrs xs, uint8_t* red,
       }
       out[k] = st16x2<D>(lo, hi);
     }
-    st_out<kStage1>(reinterpret_cast<u32x4*>(red) + c, u32x4{out[0], out[1], out[2], out[3]});
+    st_out<Stage>(out_p + c, u32x4{out[0], out[1], out[2], out[3]});
   }
 }
 
@@ -464,8 +471,10 @@ void s1_launch(const InPtrs& wires, uint8_t* red, size_t blk_lo, size_t blk_hi,
     // fewer than 4 chunks)
     const uint32_t c_lo = (uint32_t)(4 * blk_lo);
     const uint32_t c_hi = (uint32_t)(blk_hi * 4 < L.n / 8 ? blk_hi * 4 : L.n / 8);
-    hipLaunchKernelGGL((k_stage1_fp<D, W>), dim3(groups(c_hi - c_lo, kThreads * kPerLane)),
-                       dim3(kThreads), 0, st, wires, red, c_lo, c_hi);
+    OutPtrs out{};
+    out.p[0] = red;
+    hipLaunchKernelGGL((k_sum_fp<D, W, kStage1>), dim3(groups(c_hi - c_lo, kThreads * kPerLane)),
+                       dim3(kThreads), 0, st, wires, out, c_lo, c_hi);
   } else {
     hipLaunchKernelGGL((k_stage1<C, D, W>), dim3(groups(blk_hi - blk_lo, kThreads)),
                        dim3(kThreads), 0, st, wires, red, (uint32_t)blk_lo,
@@ -547,6 +556,31 @@ hipError_t launch_stage1(int codec, int dtype, int W, const InPtrs& wires,
 hipError_t launch_dequantize(int codec, int dtype, int W, const uint8_t* wire,
                              const OutPtrs& ys, const Layout& L, hipStream_t st) {
   QR_DISPATCH(codec, dtype, dq_dispatch, W, wire, ys, L, st);
+  return hipGetLastError();
+}
+
+template <int D, int W>
+void oneshot_launch(const InPtrs& xs, const OutPtrs& ys, size_t n, hipStream_t st) {
+  const uint32_t nc = (uint32_t)(n / 8);
+  hipLaunchKernelGGL((k_sum_fp<D, W, kStage2>), dim3(groups(nc, kThreads * kPerLane), W),
+                     dim3(kThreads), 0, st, xs, ys, 0u, nc);
+}
+
+template <int D>
+void oneshot_by_w(int W, const InPtrs& xs, const OutPtrs& ys, size_t n, hipStream_t st) {
+  switch (W) {
+    case 2: oneshot_launch<D, 2>(xs, ys, n, st); break;
+    case 4: oneshot_launch<D, 4>(xs, ys, n, st); break;
+    case 8: oneshot_launch<D, 8>(xs, ys, n, st); break;
+  }
+}
+
+hipError_t launch_oneshot(int dtype, int W, const InPtrs& xs, const OutPtrs& ys, size_t n,
+                          hipStream_t st) {
+  if (dtype == kBF16)
+    oneshot_by_w<kBF16>(W, xs, ys, n, st);
+  else
+    oneshot_by_w<kF16>(W, xs, ys, n, st);
   return hipGetLastError();
 }
 

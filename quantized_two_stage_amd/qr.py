@@ -45,6 +45,7 @@ def _load():
         "qr_reduce_stage1": (i32, [i32, i32, i32, PP, sz, i32, P, P]),
         "qr_gather_stage2": (i32, [i32, i32, i32, P, sz, PP, P]),
         "qr_allreduce_sim": (i32, [i32, i32, i32, PP, PP, sz, P, sz, P]),
+        "qr_allreduce_oneshot": (i32, [i32, i32, PP, PP, sz, P]),
         "qr_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -56,7 +57,7 @@ def _load():
 LIB = _load()
 EXPORTS = ("qr_wire_bytes", "qr_sim_workspace_bytes", "qr_quantize", "qr_dequantize",
            "qr_quantize_ranks", "qr_reduce_stage1", "qr_gather_stage2",
-           "qr_allreduce_sim", "qr_last_error")
+           "qr_allreduce_sim", "qr_allreduce_oneshot", "qr_last_error")
 
 
 def _check(rc):
@@ -140,6 +141,13 @@ def qr_allreduce_sim(codec, xs, ys, workspace, dtype=None, stream=None):
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(LIB.qr_allreduce_sim(len(xs), _dtype_of(xs[0], dtype), codec, _ptrs(xs),
                                 _ptrs(ys), n, _ptr(workspace), ws_bytes, _stream(stream)))
+    return ys
+
+
+def qr_allreduce_oneshot(xs, ys, dtype=None, stream=None):
+    """ys[r] = the one-stage allreduce of xs: every rank sums all W buffers."""
+    _check(LIB.qr_allreduce_oneshot(len(xs), _dtype_of(xs[0], dtype), _ptrs(xs), _ptrs(ys),
+                                    _n16(xs[0]), _stream(stream)))
     return ys
 
 

@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ("qr_quantize", "qr_dequantize", "qr_reduce_stage1", "qr_gather_stage2",
                  "qr_allreduce_sim", "qr_wire_bytes", "qr_sim_workspace_bytes",
-                 "qr_last_error", "qr_quantize_ranks"):
+                 "qr_last_error", "qr_quantize_ranks", "qr_allreduce_oneshot"):
         assert must in names
 
 
@@ -132,3 +132,26 @@ def test_stage_entry_points_reject():
     assert L.qr_quantize_ranks(1, 0, 2, _pp([FAKE, FAKE + 0x1000]), 2048,
                                _pp([FAKE + 0x2000000, FAKE + 0x2000010]), None) == -1
     assert "overlap" in L.qr_last_error().decode()
+
+
+def _call_oneshot(W=2, dtype=0, xs=None, ys=None, n=2048):
+    qr = _lib()
+    xs = xs if xs is not None else [FAKE + i * 0x100000 for i in range(W)]
+    ys = ys if ys is not None else [FAKE + 0x10000000 + i * 0x100000 for i in range(W)]
+    return qr.LIB.qr_allreduce_oneshot(W, dtype, _pp(xs), _pp(ys), n, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=3), -2), (dict(W=1), -2), (dict(W=16), -2), (dict(dtype=2), -2),
+    (dict(n=0), -3), (dict(n=2044), -3), (dict(n=(1 << 30) + 8), -3),
+    (dict(xs=[FAKE + 4, FAKE + 0x100000]), -4),
+    (dict(ys=[FAKE + 0x10000000, FAKE + 0x10000008]), -4),
+    (dict(xs=[0, FAKE + 0x100000]), -1),
+    (dict(ys=[FAKE + 0x100000 + 16, FAKE + 0x10000000]), -1),  # y overlaps x
+    (dict(ys=[FAKE + 0x10000000, FAKE + 0x10000000]), -1),     # two ys alias
+])
+def test_allreduce_oneshot_rejects(kw, code):
+    qr = _lib()
+    assert _call_oneshot(**kw) == code
+    assert qr.LIB.qr_last_error().decode() != ""
+    assert qr.LIB.qr_allreduce_oneshot(2, 0, None, _pp([FAKE, FAKE]), 2048, None) == -1
