@@ -49,7 +49,9 @@
  * asymmetric variants are added (asymmetric = symmetric | 8). */
 enum { C_FP = 0, C_Q8 = 1, C_Q6 = 2, C_Q4 = 3, C_FP8 = 5,
        C_Q8A = 9, C_Q6A = 10, C_Q4A = 11 };
-enum { T_FP16 = 0, T_BF16 = 1 };
+/* buffer types; T_BF16_VIA_FP16 = bfloat16 buffers that are converted to
+ * binary16 on entry and back on exit (see ld/st below) */
+enum { T_FP16 = 0, T_BF16 = 1, T_BF16_VIA_FP16 = 2 };
 
 #define BLK 32
 
@@ -339,12 +341,22 @@ float ref_dequant_code(int c, uint32_t code, uint16_t s, uint16_t z) {
 
 /* ------------------------------------------------------------------ */
 /* element conversion for the buffer type */
+/* The bf16 -> fp16 cast option of the vLLM quick_all_reduce docs page
+ * (QuickAllReduce.init_quick_all_reduce, VLLM_ROCM_QUICK_REDUCE_CAST_BF16_TO_FP16:
+ * bf16 inputs are converted to fp16 and the fp16 kernels run).  Reading
+ * taken: each bf16 input is rounded to binary16 (nearest even, overflow to
+ * inf), the whole allreduce then runs exactly as for binary16 buffers (the FP
+ * wire holds binary16), and each binary16 result is rounded to bfloat16. */
 static float ld(int dtype, uint16_t x) {
+  if (dtype == T_BF16_VIA_FP16) return ref_h2f(ref_f2h(ref_bf2f(x)));
   return dtype == T_BF16 ? ref_bf2f(x) : ref_h2f(x);
 }
 static uint16_t st(int dtype, float v) {
+  if (dtype == T_BF16_VIA_FP16) return ref_f2bf(ref_h2f(ref_f2h(v)));
   return dtype == T_BF16 ? ref_f2bf(v) : ref_f2h(v);
 }
+/* type of the raw values in an FP wire image */
+static int wire_type(int dtype) { return dtype == T_BF16_VIA_FP16 ? T_FP16 : dtype; }
 
 /* write one quantized block k of a wire image from binary32 values */
 static void wire_put_block(int c, uint8_t* wire, size_t n, size_t k,
@@ -380,7 +392,7 @@ static size_t clamp_hi(size_t n, size_t hi) {
   return hi > nb ? nb : hi;
 }
 static int args_ok(int c, int dtype, size_t n) {
-  return codec_valid(c) && (dtype == T_FP16 || dtype == T_BF16) && n > 0;
+  return codec_valid(c) && dtype >= T_FP16 && dtype <= T_BF16_VIA_FP16 && n > 0;
 }
 
 /* ------------------------------------------------------------------ */
@@ -394,7 +406,9 @@ int ref_quantize(int c, int dtype, const uint16_t* x, size_t n, uint8_t* wire,
   for (size_t k = blk_lo; k < blk_hi; k++) {
     int L = block_len(n, k);
     if (c == C_FP) {                          /* FP: the wire is the raw data */
-      memcpy(wire + 2 * k * BLK, x + k * BLK, 2 * (size_t)L);
+      uint16_t* w = (uint16_t*)wire + k * BLK;
+      for (int i = 0; i < L; i++)
+        w[i] = st(wire_type(dtype), ld(dtype, x[k * BLK + i]));
       continue;
     }
     float v[BLK];
@@ -412,7 +426,8 @@ int ref_dequantize(int c, int dtype, const uint8_t* wire, size_t n,
   for (size_t k = blk_lo; k < blk_hi; k++) {
     int L = block_len(n, k);
     if (c == C_FP) {
-      memcpy(y + k * BLK, wire + 2 * k * BLK, 2 * (size_t)L);
+      const uint16_t* w = (const uint16_t*)wire + k * BLK;
+      for (int i = 0; i < L; i++) y[k * BLK + i] = st(dtype, ld(wire_type(dtype), w[i]));
       continue;
     }
     float v[BLK];
@@ -446,7 +461,7 @@ int ref_stage1(int c, int dtype, int W, const uint8_t* const* wires, size_t n,
     for (int r = 0; r < W; r++) {
       if (c == C_FP) {
         const uint16_t* xr = (const uint16_t*)wires[r] + k * BLK;
-        for (int i = 0; i < L; i++) v[i] = ld(dtype, xr[i]);
+        for (int i = 0; i < L; i++) v[i] = ld(wire_type(dtype), xr[i]);
       } else {
         wire_get_block(c, wires[r], n, k, v, L);
       }
@@ -454,7 +469,7 @@ int ref_stage1(int c, int dtype, int W, const uint8_t* const* wires, size_t n,
     }
     if (c == C_FP) {
       uint16_t* out = (uint16_t*)reduced + k * BLK;
-      for (int i = 0; i < L; i++) out[i] = st(dtype, acc[i]);
+      for (int i = 0; i < L; i++) out[i] = st(wire_type(dtype), acc[i]);
     } else {
       wire_put_block(c, reduced, n, k, acc, L);
     }
@@ -505,7 +520,7 @@ int ref_allreduce(int W, int dtype, int c, const uint16_t* const* xs,
  * as the unit of the range). */
 int ref_oneshot(int W, int dtype, const uint16_t* const* xs, uint16_t* const* ys,
                 size_t n, size_t blk_lo, size_t blk_hi) {
-  if ((dtype != T_FP16 && dtype != T_BF16) || n == 0 || W < 1) return -1;
+  if (dtype < T_FP16 || dtype > T_BF16_VIA_FP16 || n == 0 || W < 1) return -1;
   blk_hi = clamp_hi(n, blk_hi);
   size_t e_lo = blk_lo * BLK, e_hi = blk_hi * BLK < n ? blk_hi * BLK : n;
   for (size_t i = e_lo; i < e_hi; i++) {

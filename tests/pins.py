@@ -428,6 +428,41 @@ def check_oneshot_closed_form(L):
             assert np.all(y[:e_lo] == 0xABCD) and np.all(y[e_hi:] == 0xABCD), (W, dtype)
 
 
+def check_cast_option(L):
+    """bf16 buffers through binary16 (dtype 2): the allreduce, the one-stage
+    allreduce and every wire image equal those of the binary16 pipeline run on
+    the binary16 roundings of the inputs (numpy's cast of the bf16 values),
+    with the binary16 results rounded to bf16 (torch's cast).  Inputs span
+    binary16 subnormals, values that flush to zero, ties of the bf16 grid, and
+    (FP paths only) magnitudes that overflow binary16."""
+    g = np.random.default_rng(9)
+    CAST = 2
+    for W in (1, 2, 4, 8):
+        n = 8 * int(g.integers(4, 120))
+        for codec in (O.FP, O.FP8, O.Q8, O.Q6, O.Q4, O.Q8A, O.Q6A, O.Q4A):
+            hi = 17.0 if codec == O.FP else 15.0            # 2^17 overflows binary16
+            xs64 = [g.standard_normal(n) * 2.0 ** g.uniform(-30, hi, n) for _ in range(W)]
+            # overflows are all positive: +inf + -inf (a NaN) is outside the contract
+            xs64 = [np.where(np.abs(x) > 60000.0, np.abs(x), x) for x in xs64]
+            xs = [torch_f32_to_bf16(np.clip(x, -65000.0, 65000.0).astype(np.float32))
+                  if codec != O.FP else torch_f32_to_bf16(x.astype(np.float32)) for x in xs64]
+            xs16 = [torch_bf16_to_f32(x).astype(np.float16).view(np.uint16) for x in xs]
+            want = [torch_f32_to_bf16(y.view(np.float16).astype(np.float32))
+                    for y in O.allreduce(codec, O.FP16, xs16, L=L)]
+            got = O.allreduce(codec, CAST, xs, L=L)
+            for r in range(W):
+                assert np.array_equal(got[r], want[r]), (W, codec, r)
+            for r in range(W):
+                assert np.array_equal(O.quantize(codec, CAST, xs[r], L=L),
+                                      O.quantize(codec, O.FP16, xs16[r], L=L)), (W, codec)
+            if codec == O.FP:
+                got1 = O.oneshot(CAST, xs, L=L)
+                want1 = [torch_f32_to_bf16(y.view(np.float16).astype(np.float32))
+                         for y in O.oneshot(O.FP16, xs16, L=L)]
+                for r in range(W):
+                    assert np.array_equal(got1[r], want1[r]), (W, "oneshot")
+
+
 def _planes(codec, n, wire, L=None):
     nb = (n + 31) // 32
     cb = nb * 32 * BITS[codec] // 8
@@ -592,5 +627,6 @@ def check_golden(L):
 QUICK_CHECKS = [check_golden, check_layout, check_chunks, check_zero_blocks,
                 check_f2h, check_ru_rd, check_e4m3, check_bf16,
                 check_block_codes, check_error_bound, check_idempotent,
-                check_fp_closed_form, check_oneshot_closed_form, check_end_to_end_bound,
+                check_fp_closed_form, check_oneshot_closed_form, check_cast_option,
+                check_end_to_end_bound,
                 check_owner_split]

@@ -74,6 +74,15 @@ MUTANTS = {
     "oneshot_range_in_elements": [
         ("size_t e_lo = blk_lo * BLK, e_hi = blk_hi * BLK < n ? blk_hi * BLK : n;",
          "size_t e_lo = blk_lo, e_hi = blk_hi < n ? blk_hi : n;")],
+    "cast_input_not_rounded_to_fp16": [
+        ("if (dtype == T_BF16_VIA_FP16) return ref_h2f(ref_f2h(ref_bf2f(x)));",
+         "if (dtype == T_BF16_VIA_FP16) return ref_bf2f(x);")],
+    "cast_output_skips_fp16": [
+        ("if (dtype == T_BF16_VIA_FP16) return ref_f2bf(ref_h2f(ref_f2h(v)));",
+         "if (dtype == T_BF16_VIA_FP16) return ref_f2bf(v);")],
+    "cast_fp_wire_kept_bf16": [
+        ("static int wire_type(int dtype) { return dtype == T_BF16_VIA_FP16 ? T_FP16 : dtype; }",
+         "static int wire_type(int dtype) { return dtype == T_BF16_VIA_FP16 ? T_BF16 : dtype; }")],
     "zero_plane_overlaps_scales": [
         ("return align256(ref_scale_offset(c, n) + 2 * nblocks(n));",
          "return align256(ref_scale_offset(c, n));")],
