@@ -134,7 +134,7 @@ def time_each(fn, iters, stream):
 
 
 def measure_workload(qr, I, torch, stream, config, n=None, codecs=None, iters=20,
-                     kernels=True, cold=True, oneshot=True):
+                     kernels=True, cold=True, oneshot=True, dtype=None):
     """One workload of inputs.CONFIGS: per codec, the simulated allreduce
     (qr_allreduce_sim) timed call by call (median and min us, effective GB/s
     = 2n bytes / time); optionally the three kernels timed one by one through
@@ -143,7 +143,8 @@ def measure_workload(qr, I, torch, stream, config, n=None, codecs=None, iters=20
     key "1stage"), whose algorithmic bytes are W*(W+1)*2n: every rank reads
     the W buffers and writes its own."""
     cfg = I.CONFIGS[config]
-    W, dtype = cfg["W"], cfg["dtype"]
+    W = cfg["W"]
+    dtype = cfg["dtype"] if dtype is None else dtype
     n = cfg["n"] if n is None else n
     codecs = cfg["codecs"] if codecs is None else codecs
     xs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in I.make(config, n=n)]
@@ -403,6 +404,14 @@ def main():
             extra["config%d" % cid] = {
                 "workload": c["desc"], "W": c["W"], "elements_per_rank": c["n"],
                 "per_codec": measure_workload(qr, I, torch, stream, cid, cold=not args.no_cold)}
+        # the bf16 -> fp16 cast option (buffer type 2) on the bf16 workload
+        c = I.CONFIGS[4]
+        print("bench: config 4 with the bf16->fp16 cast", file=sys.stderr, flush=True)
+        extra["config4_cast"] = {
+            "workload": c["desc"] + "; bf16 buffers through binary16 (cast option)",
+            "W": c["W"], "elements_per_rank": c["n"],
+            "per_codec": measure_workload(qr, I, torch, stream, 4, cold=False,
+                                          dtype=qr.QR_BF16_VIA_FP16)}
         c = I.CONFIGS[3]
         print("bench: config 3 size sweep (%s)" % c["desc"], file=sys.stderr, flush=True)
         sweep = {}

@@ -74,8 +74,18 @@
 extern "C" {
 #endif
 
-/* element type of the rank buffers */
-typedef enum { QR_FP16 = 0, QR_BF16 = 1 } qr_dtype;
+/* element type of the rank buffers.  QR_BF16_VIA_FP16 is the bf16 -> fp16
+ * cast option of the vLLM quick_all_reduce docs page (QuickAllReduce.
+ * init_quick_all_reduce and quick_all_reduce, VLLM_ROCM_QUICK_REDUCE_CAST_
+ * BF16_TO_FP16: bf16 inputs are converted to fp16 and the fp16 kernels run).
+ * Reading taken: the buffers hold bfloat16; every input element is rounded
+ * to binary16 (nearest even, overflow -> inf), the allreduce then runs
+ * exactly as for QR_FP16 buffers holding those values (an FP wire holds
+ * binary16), and every binary16 result is rounded to bfloat16 (nearest
+ * even).  Inputs beyond the binary16 range are outside the contract for the
+ * quantized codecs (they become inf); FP and the one-stage allreduce carry
+ * the inf through. */
+typedef enum { QR_FP16 = 0, QR_BF16 = 1, QR_BF16_VIA_FP16 = 2 } qr_dtype;
 
 /* wire format; 0..3 follow QuickReduceRegime on the vLLM quick_all_reduce
  * docs page (FP=0, INT8=1, INT6=2, INT4=3; its NONE=4 is rejected here),

@@ -16,7 +16,7 @@ import numpy as np
 from . import build as _build
 
 FP, Q8, Q6, Q4, FP8, Q8A, Q6A, Q4A = 0, 1, 2, 3, 5, 9, 10, 11
-FP16, BF16 = 0, 1
+FP16, BF16, BF16_VIA_FP16 = 0, 1, 2
 BLK = 32
 ALL = ctypes.c_size_t(-1).value
 

@@ -78,7 +78,7 @@ bool w_sim(int W) { return W == 2 || W == 4 || W == 8; }
 int check_kind(int codec, int dtype, size_t n) {
   if (!qr::codec_valid(codec))
     return fail(QR_ERR_UNSUPPORTED, "unsupported codec %d", codec);
-  if (dtype != QR_FP16 && dtype != QR_BF16)
+  if (dtype != QR_FP16 && dtype != QR_BF16 && dtype != QR_BF16_VIA_FP16)
     return fail(QR_ERR_UNSUPPORTED, "unsupported dtype %d", dtype);
   if (n == 0) return fail(QR_ERR_SIZE, "n must be > 0");
   if (n % 8 != 0)

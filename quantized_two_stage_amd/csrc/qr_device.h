@@ -31,7 +31,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum Codec { kFP = 0, kQ8 = 1, kQ6 = 2, kQ4 = 3, kFP8 = 5,
              kQ8A = 9, kQ6A = 10, kQ4A = 11 };
-enum DType { kF16 = 0, kBF16 = 1 };
+// buffer types; kBF16H = bfloat16 buffers converted to binary16 on entry
+// and back on exit (the bf16 -> fp16 cast option)
+enum DType { kF16 = 0, kBF16 = 1, kBF16H = 2 };
 
 constexpr int kBlock = 32;   // elements per block
 constexpr int kQuarter = 8;  // elements per lane in the four-lane layout
@@ -71,12 +73,18 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// a buffer element as binary32; with the cast option, the bfloat16 input is
+// first rounded to binary16
 template <int D>
 __device__ __forceinline__ float ld16(uint32_t bits) {
+  if constexpr (D == kBF16H) return h2f(f2h(bf2f(bits)));
   return D == kBF16 ? bf2f(bits) : h2f(bits);
 }
+// a binary32 result as a buffer element; with the cast option, rounded to
+// binary16 and that to bfloat16
 template <int D>
 __device__ __forceinline__ uint32_t st16(float v) {
+  if constexpr (D == kBF16H) return f2bf(h2f(f2h(v)));
   return D == kBF16 ? f2bf(v) : f2h(v);
 }
 // two 16-bit values of a packed word

@@ -250,7 +250,10 @@ __global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires,
 
 // stages 0 and 2 of FP: dst.p[r] <- src.p[r], 16-byte chunks (Stage only
 // names the two uses apart in profiles)
-template <int Stage>
+// stages 0 and 2 of FP: dst.p[r] <- src.p[r], 16-byte chunks, four per
+// lane; Din != Dout converts every element (the cast option: bfloat16 into a
+// binary16 wire at stage 0, binary16 back to bfloat16 at stage 2)
+template <int Stage, int Din, int Dout>
 __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
                                                    uint32_t nchunks) {
   constexpr int kS = Stage == 0 ? kStage0 : kStage2;
@@ -267,6 +270,11 @@ __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
 #pragma unroll
   for (int j = 0; j < kPerLane; j++) {
     const uint32_t c = base + j * kThreads;
+    if constexpr (Din != Dout) {
+#pragma unroll
+      for (int k = 0; k < 4; k++)
+        q[j][k] = st16x2<Dout>(ld16<Din>(q[j][k] & 0xffffu), ld16<Din>(q[j][k] >> 16));
+    }
     if (c < nchunks) st_out<kS>(d + c, q[j]);
   }
 }
@@ -482,14 +490,20 @@ void s1_launch(const InPtrs& wires, uint8_t* red, size_t blk_lo, size_t blk_hi,
   }
 }
 
+// stage 1 depends on the buffer type only through the FP wire's element
+// type (binary16 under the cast option); the other codecs' wires hold codes
 template <int C, int D>
 void s1_by_w(int W, const InPtrs& wires, uint8_t* red, size_t lo, size_t hi,
              const Layout& L, hipStream_t st) {
-  switch (W) {
-    case 2: s1_launch<C, D, 2>(wires, red, lo, hi, L, st); break;
-    case 4: s1_launch<C, D, 4>(wires, red, lo, hi, L, st); break;
-    case 8: s1_launch<C, D, 8>(wires, red, lo, hi, L, st); break;
-    default: break;
+  if constexpr (D == kBF16H || (C != kFP && D != kF16)) {
+    s1_by_w<C, kF16>(W, wires, red, lo, hi, L, st);
+  } else {
+    switch (W) {
+      case 2: s1_launch<C, D, 2>(wires, red, lo, hi, L, st); break;
+      case 4: s1_launch<C, D, 4>(wires, red, lo, hi, L, st); break;
+      case 8: s1_launch<C, D, 8>(wires, red, lo, hi, L, st); break;
+      default: break;
+    }
   }
 }
 
@@ -497,7 +511,10 @@ template <int C, int D>
 void q_dispatch(int W, const InPtrs& xs, const OutPtrs& wires, const Layout& L,
                 hipStream_t st) {
   if constexpr (C == kFP) {
-    hipLaunchKernelGGL(k_copy<0>, dim3(groups(L.n / 8, kThreads * kPerLane), W),
+    // the FP wire holds the buffer's raw elements (binary16 under the cast)
+    constexpr int Dw = D == kBF16H ? kF16 : D;
+    constexpr int Din = D == kBF16H ? kBF16 : D;
+    hipLaunchKernelGGL((k_copy<0, Din, Dw>), dim3(groups(L.n / 8, kThreads * kPerLane), W),
                        dim3(kThreads), 0, st, xs, wires, (uint32_t)(L.n / 8));
   } else {
     hipLaunchKernelGGL((k_quantize<C, D>),
@@ -512,7 +529,9 @@ void dq_dispatch(int W, const uint8_t* wire, const OutPtrs& ys, const Layout& L,
   if constexpr (C == kFP) {
     InPtrs src;
     for (int r = 0; r < kMaxRanks; r++) src.p[r] = wire;
-    hipLaunchKernelGGL(k_copy<2>, dim3(groups(L.n / 8, kThreads * kPerLane), W),
+    constexpr int Dw = D == kBF16H ? kF16 : D;
+    constexpr int Dout = D == kBF16H ? kBF16 : D;
+    hipLaunchKernelGGL((k_copy<2, Dw, Dout>), dim3(groups(L.n / 8, kThreads * kPerLane), W),
                        dim3(kThreads), 0, st, src, ys, (uint32_t)(L.n / 8));
   } else {
     hipLaunchKernelGGL((k_dequant<C, D>), dim3(groups(L.n / 8, kThreads * kPerLane), W),
@@ -521,18 +540,20 @@ void dq_dispatch(int W, const uint8_t* wire, const OutPtrs& ys, const Layout& L,
 }
 
 // calls FN<codec, dtype>(args...) for the runtime (codec, dtype)
+#define QR_BY_DTYPE(C, dtype, FN, ...)                                                  \
+  ((dtype) == kBF16H ? FN<C, kBF16H>(__VA_ARGS__)                                       \
+                     : (dtype) == kBF16 ? FN<C, kBF16>(__VA_ARGS__) : FN<C, kF16>(__VA_ARGS__))
 #define QR_DISPATCH(codec, dtype, FN, ...)                                              \
   do {                                                                                  \
-    const bool bf = (dtype) == kBF16;                                                   \
     switch (codec) {                                                                    \
-      case kFP: bf ? FN<kFP, kBF16>(__VA_ARGS__) : FN<kFP, kF16>(__VA_ARGS__); break;     \
-      case kQ8: bf ? FN<kQ8, kBF16>(__VA_ARGS__) : FN<kQ8, kF16>(__VA_ARGS__); break;     \
-      case kQ6: bf ? FN<kQ6, kBF16>(__VA_ARGS__) : FN<kQ6, kF16>(__VA_ARGS__); break;     \
-      case kQ4: bf ? FN<kQ4, kBF16>(__VA_ARGS__) : FN<kQ4, kF16>(__VA_ARGS__); break;     \
-      case kFP8: bf ? FN<kFP8, kBF16>(__VA_ARGS__) : FN<kFP8, kF16>(__VA_ARGS__); break;  \
-      case kQ8A: bf ? FN<kQ8A, kBF16>(__VA_ARGS__) : FN<kQ8A, kF16>(__VA_ARGS__); break;  \
-      case kQ6A: bf ? FN<kQ6A, kBF16>(__VA_ARGS__) : FN<kQ6A, kF16>(__VA_ARGS__); break;  \
-      case kQ4A: bf ? FN<kQ4A, kBF16>(__VA_ARGS__) : FN<kQ4A, kF16>(__VA_ARGS__); break;  \
+      case kFP: QR_BY_DTYPE(kFP, dtype, FN, __VA_ARGS__); break;                        \
+      case kQ8: QR_BY_DTYPE(kQ8, dtype, FN, __VA_ARGS__); break;                        \
+      case kQ6: QR_BY_DTYPE(kQ6, dtype, FN, __VA_ARGS__); break;                        \
+      case kQ4: QR_BY_DTYPE(kQ4, dtype, FN, __VA_ARGS__); break;                        \
+      case kFP8: QR_BY_DTYPE(kFP8, dtype, FN, __VA_ARGS__); break;                      \
+      case kQ8A: QR_BY_DTYPE(kQ8A, dtype, FN, __VA_ARGS__); break;                      \
+      case kQ6A: QR_BY_DTYPE(kQ6A, dtype, FN, __VA_ARGS__); break;                      \
+      case kQ4A: QR_BY_DTYPE(kQ4A, dtype, FN, __VA_ARGS__); break;                      \
       default: break;                                                                   \
     }                                                                                   \
   } while (0)
@@ -577,7 +598,9 @@ void oneshot_by_w(int W, const InPtrs& xs, const OutPtrs& ys, size_t n, hipStrea
 
 hipError_t launch_oneshot(int dtype, int W, const InPtrs& xs, const OutPtrs& ys, size_t n,
                           hipStream_t st) {
-  if (dtype == kBF16)
+  if (dtype == kBF16H)
+    oneshot_by_w<kBF16H>(W, xs, ys, n, st);
+  else if (dtype == kBF16)
     oneshot_by_w<kBF16>(W, xs, ys, n, st);
   else
     oneshot_by_w<kF16>(W, xs, ys, n, st);

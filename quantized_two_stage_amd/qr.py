@@ -12,7 +12,7 @@ import torch
 
 QR_FP, QR_Q8, QR_Q6, QR_Q4, QR_FP8 = 0, 1, 2, 3, 5
 QR_Q8_ASYM, QR_Q6_ASYM, QR_Q4_ASYM = 9, 10, 11
-QR_FP16, QR_BF16 = 0, 1
+QR_FP16, QR_BF16, QR_BF16_VIA_FP16 = 0, 1, 2
 CODECS = (QR_FP, QR_FP8, QR_Q8, QR_Q6, QR_Q4, QR_Q8_ASYM, QR_Q6_ASYM, QR_Q4_ASYM)
 CODEC_NAMES = {QR_FP: "fp", QR_Q8: "q8", QR_Q6: "q6", QR_Q4: "q4", QR_FP8: "fp8",
                QR_Q8_ASYM: "q8a", QR_Q6_ASYM: "q6a", QR_Q4_ASYM: "q4a"}

@@ -11,6 +11,9 @@
 //   5. e4m3_dec<k> (v_cvt_f32_fp8) == exact E4M3FN value, all codes, k = 0..3
 //   6. f2bf (v_cvt_pk_bf16_f32) == nearest-even on the bit pattern for every
 //      non-NaN binary32
+//   7. f2h (v_cvt_f16_f32) == nearest-even binary16 (subnormals, overflow to
+//      inf) for every non-NaN binary32, against an integer conversion written
+//      from the two formats' definitions
 // Prints one line per check and exits 0 only if every count is zero.
 // Grid-stride loops with explicit bounds; counters in one small array.
 #include <hip/hip_runtime.h>
@@ -21,7 +24,7 @@
 
 using namespace qr;
 
-enum { kDiv = 0, kRcp = 6, kRint = 7, kEnc = 8, kDec = 9, kBf = 10, kSlots = 12 };
+enum { kDiv = 0, kRcp = 6, kRint = 7, kEnc = 8, kDec = 9, kBf = 10, kF2h = 11, kSlots = 12 };
 
 __device__ void miss(uint32_t* c, int slot) { atomicAdd(&c[slot], 1u); }
 
@@ -110,6 +113,39 @@ __global__ void k_bf(uint32_t* c) {
   }
 }
 
+// reference binary32 -> binary16, round to nearest even, from the formats:
+// binary16 normals start at 2^-14 (binary32 biased exponent 113), its
+// subnormals are multiples of 2^-24, and magnitudes from 65520 up round to inf
+__device__ uint32_t f2h_ref(uint32_t u) {
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a >= 0x477ff000u) return sign | 0x7c00u;
+  const uint32_t e = a >> 23;
+  if (e >= 113u) {
+    const uint32_t m = a & 0x7fffffu;
+    uint32_t h = ((e - 112u) << 10) | (m >> 13);
+    const uint32_t rest = m & 0x1fffu;
+    if (rest > 0x1000u || (rest == 0x1000u && (h & 1u))) h += 1u;
+    return sign | h;
+  }
+  if (e < 102u) return sign;                              // below 2^-25
+  const uint32_t mant = (a & 0x7fffffu) | 0x800000u;     // value = mant * 2^(e-150)
+  const uint32_t sh = 126u - e;                           // 14 .. 24
+  uint32_t q = mant >> sh;                                // value / 2^-24, truncated
+  const uint32_t rest = mant & ((1u << sh) - 1u), half = 1u << (sh - 1u);
+  if (rest > half || (rest == half && (q & 1u))) q += 1u;
+  return sign | q;
+}
+
+__global__ void k_f2h(uint32_t* c) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32); i += stride) {
+    const uint32_t u = (uint32_t)i;
+    if ((u & 0x7fffffffu) > 0x7f800000u) continue;        // NaN
+    if (f2h(__builtin_bit_cast(float, u)) != f2h_ref(u)) miss(c, kF2h);
+  }
+}
+
 #define CK(x)                                                                       \
   do {                                                                              \
     hipError_t e_ = (x);                                                            \
@@ -134,6 +170,7 @@ int main() {
   k_enc<<<8192, 256>>>(c);
   k_dec<<<1, 256>>>(c);
   k_bf<<<8192, 256>>>(c);
+  k_f2h<<<8192, 256>>>(c);
   CK(hipGetLastError());
   CK(hipDeviceSynchronize());
   uint32_t h[kSlots];
@@ -150,7 +187,8 @@ int main() {
   printf("e4m3_pack2: %u mismatches over all |t| <= 464\n", h[kEnc]);
   printf("e4m3_dec: %u mismatches over all non-NaN codes, 4 byte positions\n", h[kDec]);
   printf("f2bf: %u mismatches over all non-NaN binary32\n", h[kBf]);
-  total += h[kRcp] + h[kRint] + h[kEnc] + h[kDec] + h[kBf];
+  printf("f2h: %u mismatches over all non-NaN binary32\n", h[kF2h]);
+  total += h[kRcp] + h[kRint] + h[kEnc] + h[kDec] + h[kBf] + h[kF2h];
   printf("%s\n", total == 0 ? "ALL OK" : "MISMATCHES");
   return total == 0 ? 0 : 1;
 }

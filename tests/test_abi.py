@@ -86,7 +86,7 @@ def _call_sim(W=2, dtype=0, codec=1, xs=None, ys=None, n=2048, ws=None, ws_bytes
 
 @pytest.mark.parametrize("kw,code", [
     (dict(W=3), -2), (dict(W=1), -2), (dict(W=16), -2),
-    (dict(dtype=2), -2), (dict(codec=4), -2), (dict(codec=7), -2), (dict(codec=12), -2),
+    (dict(dtype=3), -2), (dict(codec=4), -2), (dict(codec=7), -2), (dict(codec=12), -2),
     (dict(n=0), -3), (dict(n=2044), -3), (dict(n=(1 << 30) + 8), -3),
     (dict(ws_bytes=100), -5),
     (dict(xs=[FAKE + 4, FAKE + 0x100000]), -4),
@@ -142,7 +142,7 @@ def _call_oneshot(W=2, dtype=0, xs=None, ys=None, n=2048):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(W=3), -2), (dict(W=1), -2), (dict(W=16), -2), (dict(dtype=2), -2),
+    (dict(W=3), -2), (dict(W=1), -2), (dict(W=16), -2), (dict(dtype=3), -2),
     (dict(n=0), -3), (dict(n=2044), -3), (dict(n=(1 << 30) + 8), -3),
     (dict(xs=[FAKE + 4, FAKE + 0x100000]), -4),
     (dict(ys=[FAKE + 0x10000000, FAKE + 0x10000008]), -4),

@@ -23,7 +23,10 @@ def qr():
     return q
 
 
-GENS = {O.FP16: (1, 2, 5), O.BF16: (3, 4, 5)}
+# dtype 2 = bf16 buffers through binary16: generator 5's +-max-finite blocks
+# become +-inf there, and +inf + -inf (a NaN) is outside the contract; the
+# edge test covers same-signed overflow
+GENS = {O.FP16: (1, 2, 5), O.BF16: (3, 4, 5), O.BF16_VIA_FP16: (3, 4)}
 SIZES = (8, 24, 40, 3 * 8192 + 24, 65536 + 8)
 
 
@@ -59,12 +62,14 @@ def _check(qr, xs_np, dtype, label):
 
 
 @pytest.mark.parametrize("W", (2, 4, 8))
-@pytest.mark.parametrize("dtype", (O.FP16, O.BF16), ids=("fp16", "bf16"))
+@pytest.mark.parametrize("dtype", (O.FP16, O.BF16, O.BF16_VIA_FP16),
+                         ids=("fp16", "bf16", "bf16viafp16"))
 def test_oneshot_parity(qr, dtype, W):
     for cfg in GENS[dtype]:
         for n in SIZES:
-            _check(qr, _inputs(cfg, W, n, dtype), dtype,
-                   "W%d n%d gen%d %s" % (W, n, cfg, "bf16" if dtype else "fp16"))
+            # the cast option's inputs are bf16 buffers
+            _check(qr, _inputs(cfg, W, n, O.BF16 if dtype == O.BF16_VIA_FP16 else dtype), dtype,
+                   "W%d n%d gen%d dtype%d" % (W, n, cfg, dtype))
 
 
 @pytest.mark.parametrize("dtype", (O.FP16, O.BF16), ids=("fp16", "bf16"))
@@ -82,11 +87,14 @@ def test_oneshot_equals_two_stage_fp(qr, dtype):
             _assert_equal(host16(ys[r]), host16(ys2[r]), "oneshot vs sim W%d y[%d]" % (W, r))
 
 
-@pytest.mark.parametrize("dtype", (O.FP16, O.BF16), ids=("fp16", "bf16"))
+@pytest.mark.parametrize("dtype", (O.FP16, O.BF16, O.BF16_VIA_FP16),
+                         ids=("fp16", "bf16", "bf16viafp16"))
 def test_oneshot_edge_values(qr, dtype):
     """zeros of both signs, sums that overflow to inf, subnormals, identical
-    ranks, and cancellation across ranks"""
+    ranks, and cancellation across ranks (dtype 2: bf16 buffers, whose
+    largest values become inf in binary16)"""
     W, n = 4, 32 * 10 + 8
+    gen_t = O.FP16 if dtype == O.FP16 else O.BF16      # type of the buffers
     one = pins.to_buf([1.0], "fp16" if dtype == O.FP16 else "bf16")[0]
     big = 0x7BFF if dtype == O.FP16 else 0x7F7F
     cases = {
@@ -97,11 +105,11 @@ def test_oneshot_edge_values(qr, dtype):
         "overflow": [np.full(n, big, np.uint16)] * W,
         "overflow_neg": [np.full(n, big | 0x8000, np.uint16)] * W,
         "tiny": [np.full(n, 1, np.uint16) | (np.arange(n, dtype=np.uint16) & 1) * 0x8000] * W,
-        "identical": [I.to_bits(I.draw(1, 0, n), dtype)] * W,
-        "cancel": [I.to_bits(I.draw(1, 0, n), dtype),
-                   I.to_bits(I.draw(1, 0, n), dtype) ^ 0x8000,
-                   I.to_bits(I.draw(1, 1, n), dtype),
-                   I.to_bits(I.draw(1, 1, n), dtype) ^ 0x8000],
+        "identical": [I.to_bits(I.draw(1, 0, n), gen_t)] * W,
+        "cancel": [I.to_bits(I.draw(1, 0, n), gen_t),
+                   I.to_bits(I.draw(1, 0, n), gen_t) ^ 0x8000,
+                   I.to_bits(I.draw(1, 1, n), gen_t),
+                   I.to_bits(I.draw(1, 1, n), gen_t) ^ 0x8000],
     }
     for name, xs_np in cases.items():
         _check(qr, [x.copy() for x in xs_np], dtype, "edge %s" % name)

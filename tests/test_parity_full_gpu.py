@@ -39,13 +39,14 @@ def _data(cfg, n=None):
     return _cache[key]
 
 
-def _check_full(qr, cfg, codec, n=None, windows=12, staged=True):
+def _check_full(qr, cfg, codec, n=None, windows=12, staged=True, dtype=None):
     c = I.CONFIGS[cfg]
-    W, dtype = c["W"], c["dtype"]
+    W = c["W"]
+    dtype = c["dtype"] if dtype is None else dtype
     xs_np, xs = _data(cfg, n)
     n = xs_np[0].size
     nb = (n + 31) // 32
-    label = "cfg%d %s W%d n%d" % (cfg, I.CODEC_NAMES[codec], W, n)
+    label = "cfg%d %s W%d n%d dtype%d" % (cfg, I.CODEC_NAMES[codec], W, n, dtype)
     say("full", label)
     ys = [torch.empty_like(xs[0]) for _ in range(W)]
     ws = qr.alloc_workspace(W, codec, n)
@@ -153,3 +154,12 @@ def test_max_size(qr, codec):
         assert torch.equal(ys[1][e0:e1], ys[0][e0:e1])
     del xs, ys, ws
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg,codec", [(4, O.Q6), (3, O.Q4A), (4, O.FP), (3, O.Q8)],
+                         ids=("cfg4-q6", "cfg3-q4a", "cfg4-fp", "cfg3-q8"))
+def test_cast_option_full(qr, cfg, codec):
+    """the bf16 workloads with the bf16 -> fp16 cast option (buffer type 2):
+    64 MB (configuration 3's largest size) and 16 MB W=8"""
+    _check_full(qr, cfg, codec, n=(1 << 25) if cfg == 3 else None, windows=8,
+                dtype=O.BF16_VIA_FP16)

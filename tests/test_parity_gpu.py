@@ -72,6 +72,41 @@ def test_parity_small(qr, codec, dtype, W):
                 codec, "bf16" if dtype else "fp16", W, n, cfg))
 
 
+CAST = O.BF16_VIA_FP16                 # bf16 buffers through binary16
+
+
+def _cast_edges(W, n, salt):
+    """bf16 inputs where the cast to binary16 rounds: a bf16 value in the
+    binary16 normal range converts exactly, so the inputs spread over every
+    binade from 2^-27 to 2^15, with binary16 subnormals, values that underflow
+    to +-0, exact ties k*2^-25 (k odd) between binary16 subnormals, and +-0."""
+    g = np.random.default_rng(100 + salt)
+    out = []
+    for r in range(W):
+        e = g.uniform(-27.0, 15.5, n)
+        v = g.choice([-1.0, 1.0], n) * 2.0 ** e * g.uniform(1.0, 2.0, n)
+        ties = g.random(n) < 0.1
+        v[ties] = g.choice([-1.0, 1.0], int(ties.sum())) * \
+            (2 * g.integers(0, 64, int(ties.sum())) + 1) * 2.0 ** -25
+        v[g.random(n) < 0.05] = 0.0
+        out.append(pins.torch_f32_to_bf16(np.clip(v, -60000, 60000).astype(np.float32)))
+    return out
+
+
+@pytest.mark.parametrize("W", (2, 4, 8))
+@pytest.mark.parametrize("codec", CODECS, ids=[I.CODEC_NAMES[c] for c in CODECS])
+def test_parity_cast(qr, codec, W):
+    """the bf16 -> fp16 cast option: every wire plane bit-exact and every
+    output within 1 ulp of the oracle, on the bf16 workloads' generators and
+    on inputs spread over binary16's whole range (subnormals, underflow)"""
+    for n in SIZES:
+        for cfg in (3, 4):
+            _check_case(qr, codec, CAST, _inputs(cfg, W, n, O.BF16),
+                        "cast c%d W%d n%d gen%d" % (codec, W, n, cfg))
+        _check_case(qr, codec, CAST, _cast_edges(W, n, codec * 10 + W),
+                    "cast edges c%d W%d n%d" % (codec, W, n))
+
+
 def test_golden_fixtures_gpu(qr):
     """The hand-worked examples through the HIP path."""
     for case in pins.golden_cases():
