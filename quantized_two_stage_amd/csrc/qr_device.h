@@ -80,10 +80,21 @@ __device__ __forceinline__ float ld16(uint32_t bits) {
   if constexpr (D == kBF16H) return h2f(f2h(bf2f(bits)));
   return D == kBF16 ? bf2f(bits) : h2f(bits);
 }
-// a binary32 result as a buffer element; with the cast option, rounded to
-// binary16 and that to bfloat16
+// A binary32 value the compiler must produce as such.  Without it, an fma
+// (or add) followed by a conversion to binary16 may be merged into one
+// mixed-precision instruction (v_fma_mixlo_f16) that rounds the exact result
+// once, straight to binary16; the definition rounds to binary32 first, and the
+// two differ when the binary32 value lands on a binary16 midpoint.
+__device__ __forceinline__ float as_f32(float v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
+// a binary32 result as a buffer element (rounded from the binary32 value);
+// with the cast option, rounded to binary16 and that to bfloat16
 template <int D>
 __device__ __forceinline__ uint32_t st16(float v) {
+  v = as_f32(v);
   if constexpr (D == kBF16H) return f2bf(h2f(f2h(v)));
   return D == kBF16 ? f2bf(v) : f2h(v);
 }
@@ -96,6 +107,7 @@ __device__ __forceinline__ uint32_t st16x2(float lo, float hi) {
 // least binary16 >= v (v >= 0), saturated at 65504: round to nearest, then
 // step up one unit where that fell below v
 __device__ __forceinline__ uint32_t ru16(float v) {
+  v = as_f32(v);
   uint32_t h = f2h(v);
   if (h2f(h) < v) h += 1u;
   return h >= 0x7c00u ? 0x7bffu : h;
@@ -103,6 +115,7 @@ __device__ __forceinline__ uint32_t ru16(float v) {
 
 // greatest binary16 <= v, saturated at -65504
 __device__ __forceinline__ uint32_t rd16(float v) {
+  v = as_f32(v);
   uint32_t h = f2h(v);
   if (h2f(h) > v) h = (h & 0x8000u) ? h + 1u : (h == 0u ? 0x8001u : h - 1u);
   return (h & 0x7fffu) >= 0x7c00u ? (h & 0x8000u) | 0x7bffu : h;
@@ -305,6 +318,18 @@ __device__ __forceinline__ void group_max_min(const float* p, bool any, float& m
                    p[6]), p[7]);
   mx = any ? mx : -__builtin_inff();
   mn = any ? mn : __builtin_inff();
+}
+
+// max and min of a whole block p[0..32): one chain each, so that every pair
+// of new values takes one v_max3/v_min3
+__device__ __forceinline__ void block_max_min(const float* p, float& mx, float& mn) {
+  mx = fmaxf(p[0], p[1]);
+  mn = fminf(p[0], p[1]);
+#pragma unroll
+  for (int i = 2; i < kBlock; i++) {
+    mx = fmaxf(mx, p[i]);
+    mn = fminf(mn, p[i]);
+  }
 }
 
 // Scale and zero of a block from its max and min, and the parameters that

@@ -117,16 +117,36 @@ struct QuarterIO {
 // block j and hands 1/s, the zero and two flags to the others (DPP quad
 // broadcasts): each block's divisions and roundings run once, not four times.
 
-// max/min with a quad neighbour.  med3(a, b, +-inf) is max/min(a, b) for
-// non-NaN values; unlike fmaxf/fminf it needs no canonicalization of the
-// DPP-moved operand (one instruction instead of two).
+// max/min with a quad neighbour in one instruction: the DPP permute is the
+// first source of v_max_f32/v_min_f32 itself.  (Written as a permute and an
+// fmaxf, or as med3 with an infinite bound, the compiler emits a permute, a
+// canonicalizing v_max of the permuted value and the max: three
+// instructions; the values here are never NaN, for which canonicalizing is a
+// no-op.)  The s_nop gives the two wait states a DPP read needs after a VALU
+// write of its source, which the compiler does not insert for inline asm.
 template <int Ctrl>
 __device__ __forceinline__ float quad_max(float v) {
-  return __builtin_amdgcn_fmed3f(v, quad_perm<Ctrl>(v), __builtin_inff());
+  static_assert(Ctrl == kSwap1 || Ctrl == kSwap2, "quad swaps only");
+  float r;
+  if constexpr (Ctrl == kSwap1)
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "=&v"(r) : "v"(v));
+  else
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+        : "=&v"(r) : "v"(v));
+  return r;
 }
 template <int Ctrl>
 __device__ __forceinline__ float quad_min(float v) {
-  return __builtin_amdgcn_fmed3f(v, quad_perm<Ctrl>(v), -__builtin_inff());
+  static_assert(Ctrl == kSwap1 || Ctrl == kSwap2, "quad swaps only");
+  float r;
+  if constexpr (Ctrl == kSwap1)
+    asm("s_nop 1\n\tv_min_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "=&v"(r) : "v"(v));
+  else
+    asm("s_nop 1\n\tv_min_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+        : "=&v"(r) : "v"(v));
+  return r;
 }
 
 // quad_perm [u,u,u,u]: the value of lane u of the quad
@@ -142,7 +162,9 @@ __device__ __forceinline__ uint32_t from_lane_u(uint32_t v) { return quad_perm_u
 // and stores its own quarters.  Quarters at or past q_end store nothing;
 // quarters holding no element (8q >= n) are left out of the statistics and
 // get code 0.  q_end is a multiple of 4, so a quad is wholly in or out.
-template <int C, int Stage>
+// Full: the caller guarantees that every quarter of the workgroup holds 8
+// elements and lies below q_end (no range checks are made).
+template <int C, int Stage, bool Full>
 __device__ __forceinline__ void quantize_quarters(float (&v)[4][8], uint32_t q0,
                                                   uint32_t q_end, uint8_t* wire,
                                                   const Geo& g) {
@@ -154,7 +176,7 @@ __device__ __forceinline__ void quantize_quarters(float (&v)[4][8], uint32_t q0,
   float mx[4], mn[4];
 #pragma unroll
   for (int u = 0; u < 4; u++) {
-    group_max_min(v[u], 8 * (q0 + u * kThreads) < g.n, mx[u], mn[u]);
+    group_max_min(v[u], Full || 8 * (q0 + u * kThreads) < g.n, mx[u], mn[u]);
     mx[u] = quad_max<kSwap2>(quad_max<kSwap1>(mx[u]));
     mn[u] = quad_min<kSwap2>(quad_min<kSwap1>(mn[u]));
   }
@@ -163,7 +185,7 @@ __device__ __forceinline__ void quantize_quarters(float (&v)[4][8], uint32_t q0,
   const float bn = j == 0 ? mn[0] : j == 1 ? mn[1] : j == 2 ? mn[2] : mn[3];
   const BlockParams<C> p = block_params<C>(bx, bn);
   const uint32_t own_q = q0 + j * kThreads;
-  if (own_q < q_end) {
+  if (Full || own_q < q_end) {
     const uint32_t own_blk = own_q >> 2;
     st_u16(wire + g.off_s + (size_t)own_blk * 2, p.s);
     if constexpr (T::asym) st_u16(wire + g.off_z + (size_t)own_blk * 2, p.z);
@@ -189,7 +211,7 @@ __device__ __forceinline__ void quantize_quarters(float (&v)[4][8], uint32_t q0,
     encode<C, 8>(t, (fl[u] & 1u) != 0u, w);
     // fp8: an all-zero block gives code 0x00 even for -0 inputs; every codec:
     // quarters beyond the buffer hold code 0
-    const bool keep = 8 * q < g.n && (!T::fp8 || (fl[u] & 2u) != 0u);
+    const bool keep = (Full || 8 * q < g.n) && (!T::fp8 || (fl[u] & 2u) != 0u);
 #pragma unroll
     for (int k = 0; k < nw; k++) w[k] = keep ? w[k] : 0u;
     uint8_t* cb = wire + (size_t)(q >> 2) * T::block_bytes;
@@ -198,13 +220,13 @@ __device__ __forceinline__ void quantize_quarters(float (&v)[4][8], uint32_t q0,
       // odd neighbour's 48)
       const uint32_t o0 = quad_perm_u<kFromOdd>(w[0]);
       const uint32_t o1 = quad_perm_u<kFromOdd>(w[1]);
-      if (q < q_end && (j & 1) == 0) {
+      if ((Full || q < q_end) && (j & 1) == 0) {
         uint32_t* d = reinterpret_cast<uint32_t*>(cb) + 3 * (j >> 1);
         st_out<Stage>(d, w[0]);
         st_out<Stage>(d + 1, (w[1] & 0xffffu) | (o0 << 16));
         st_out<Stage>(d + 2, (o0 >> 16) | (o1 << 16));
       }
-    } else if (q < q_end) {
+    } else if (Full || q < q_end) {
       if constexpr (T::bits == 4)
         st_out<Stage>(reinterpret_cast<uint32_t*>(cb) + j, w[0]);
       else
@@ -213,7 +235,7 @@ __device__ __forceinline__ void quantize_quarters(float (&v)[4][8], uint32_t q0,
   }
 }
 
-template <int C, int D>
+template <int C, int D, bool Full>
 __device__ __forceinline__ void quantize_tile(const u32x4 (&raw)[4], uint32_t q0,
                                               uint8_t* wire, const Geo& g) {
   float v[4][8];
@@ -226,16 +248,24 @@ __device__ __forceinline__ void quantize_tile(const u32x4 (&raw)[4], uint32_t q0
       v[u][2 * k + 1] = ld16<D>(rw[k] >> 16);
     }
   }
-  quantize_quarters<C, kStage0>(v, q0, 4 * g.nb, wire, g);
+  quantize_quarters<C, kStage0, Full>(v, q0, 4 * g.nb, wire, g);
 }
 
+template <bool Full>
 __device__ __forceinline__ void load_tile(const uint8_t* x, uint32_t q0, uint32_t n,
                                           u32x4 (&raw)[4]) {
 #pragma unroll
   for (int u = 0; u < 4; u++) {
     const uint32_t q = q0 + u * kThreads;
-    raw[u] = ld_in<kStage0>(reinterpret_cast<const u32x4*>(x) + (8 * q < n ? q : 0u));
+    raw[u] = ld_in<kStage0>(reinterpret_cast<const u32x4*>(x) + (Full || 8 * q < n ? q : 0u));
   }
+}
+
+// true when every quarter of workgroup `wg` (quarters wg*1024 .. +1023) holds
+// 8 elements of an n-element buffer: a uniform branch to the path without
+// per-quarter range checks
+__device__ __forceinline__ bool tile_full(uint32_t wg, uint32_t n) {
+  return 8ull * ((uint64_t)wg + 1ull) * (kThreads * kPerLane) <= (uint64_t)n;
 }
 
 template <int C, int D>
@@ -244,8 +274,13 @@ __global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires,
   const int r = blockIdx.y;
   const uint32_t q0 = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
   u32x4 raw[4];
-  load_tile(xs.p[r], q0, g.n, raw);
-  quantize_tile<C, D>(raw, q0, wires.p[r], g);
+  if (tile_full(blockIdx.x, g.n)) {
+    load_tile<true>(xs.p[r], q0, g.n, raw);
+    quantize_tile<C, D, true>(raw, q0, wires.p[r], g);
+  } else {
+    load_tile<false>(xs.p[r], q0, g.n, raw);
+    quantize_tile<C, D, false>(raw, q0, wires.p[r], g);
+  }
 }
 
 // stages 0 and 2 of FP: dst.p[r] <- src.p[r], 16-byte chunks (Stage only
@@ -316,12 +351,13 @@ __device__ __forceinline__ void s1_load(const InPtrs& wires, uint32_t blk, const
   }
 }
 
-template <int C, int W>
+// Full: the block holds 32 elements (no partial-block handling)
+template <int C, int W, bool Full>
 __device__ __forceinline__ void s1_reduce_store(const S1In<C, W>& in, uint8_t* red,
                                                 uint32_t blk, const Geo& g) {
   using T = CodecT<C>;
   const uint32_t e0 = blk * kBlock;
-  const int L = g.n - e0 >= (uint32_t)kBlock ? kBlock : (int)(g.n - e0);
+  const int L = Full || g.n - e0 >= (uint32_t)kBlock ? kBlock : (int)(g.n - e0);
   // acc = x0 + x1 + ... in rank order.  A symmetric/fp8 term cv*s is exact,
   // so acc + cv*s is one fused multiply-add; an asymmetric term cv*s + z is
   // rounded once (the product is exact) and then added.
@@ -340,18 +376,23 @@ __device__ __forceinline__ void s1_reduce_store(const S1In<C, W>& in, uint8_t* r
       }
     }
   }
-  float mx, mn, gx, gn;
-  group_max_min(acc, true, mx, mn);
+  float mx, mn;
+  if constexpr (Full) {
+    block_max_min(acc, mx, mn);
+  } else {
+    float gx, gn;
+    group_max_min(acc, true, mx, mn);
 #pragma unroll
-  for (int k = 1; k < 4; k++) {
-    group_max_min(acc + 8 * k, 8 * k < L, gx, gn);
-    mx = fmaxf(mx, gx);
-    mn = fminf(mn, gn);
+    for (int k = 1; k < 4; k++) {
+      group_max_min(acc + 8 * k, 8 * k < L, gx, gn);
+      mx = fmaxf(mx, gx);
+      mn = fminf(mn, gn);
+    }
   }
   const BlockParams<C> p = block_params<C>(mx, mn);
   uint32_t w[T::words];
   quantize_values<C, kBlock>(acc, p, w);
-  if (L < kBlock) {                               // unused slots hold code 0
+  if (!Full && L < kBlock) {                      // unused slots hold code 0
 #pragma unroll
     for (int k = 0; k < T::words; k++) {
       const int first = L * T::bits - 32 * k;     // first unused bit in word k
@@ -379,10 +420,18 @@ __global__ __launch_bounds__(kThreads) void k_stage1(InPtrs wires, uint8_t* red,
                                                      uint32_t blk_lo, uint32_t blk_hi,
                                                      Geo g) {
   const uint32_t blk = blk_lo + blockIdx.x * kThreads + threadIdx.x;
+  // uniform: every block of the workgroup is in range and holds 32 elements
+  const uint32_t wg_end = blk_lo + (blockIdx.x + 1) * kThreads;
+  if (wg_end <= blk_hi && (uint64_t)wg_end * kBlock <= (uint64_t)g.n) {
+    S1In<C, W> in;
+    s1_load<C, W>(wires, blk, g, in);
+    s1_reduce_store<C, W, true>(in, red, blk, g);
+    return;
+  }
   if (blk >= blk_hi) return;
   S1In<C, W> in;
   s1_load<C, W>(wires, blk, g, in);
-  s1_reduce_store<C, W>(in, red, blk, g);
+  s1_reduce_store<C, W, false>(in, red, blk, g);
 }
 
 // Sum of W raw buffers over 16-byte chunks [c_lo, c_hi): the binary32 sum
@@ -425,29 +474,26 @@ __global__ __launch_bounds__(kThreads) void k_sum_fp(InPtrs xs, OutPtrs outs,
 // ---------------------------------------------------------------------------
 // stage 2 / dequantize: one quarter block per lane, kPerLane quarters
 
-template <int C, int D>
-__global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* wire, OutPtrs ys,
-                                                      Geo g) {
+// quarters q0 + 256u (u = 0..3) of the wire -> y; Full: all hold 8 elements
+template <int C, int D, bool Full>
+__device__ __forceinline__ void dequant_tile(const uint8_t* wire, uint8_t* y, uint32_t q0,
+                                             uint32_t nq, const Geo& g) {
   using T = CodecT<C>;
   using IO = QuarterIO<C>;
-  const int r = blockIdx.y;
-  const uint32_t nq = (g.n + 7) / 8;                // quarters that hold data
-  const uint32_t q0 = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
   uint32_t w[kPerLane][IO::nw];
   float s[kPerLane], z[kPerLane];
 #pragma unroll
   for (int u = 0; u < kPerLane; u++) {
-    const uint32_t q = q0 + u * kThreads < nq ? q0 + u * kThreads : 0u;  // no branch
+    const uint32_t q = Full || q0 + u * kThreads < nq ? q0 + u * kThreads : 0u;  // no branch
     const uint32_t blk = q >> 2;
     IO::load(wire + (size_t)blk * T::block_bytes, q & 3, w[u]);
     s[u] = h2f(ld_u16(wire + g.off_s + (size_t)blk * 2)) * T::unpack_scale;
     z[u] = T::asym ? h2f(ld_u16(wire + g.off_z + (size_t)blk * 2)) : 0.0f;
   }
-  uint8_t* y = ys.p[r];
 #pragma unroll
   for (int u = 0; u < kPerLane; u++) {
     const uint32_t q = q0 + u * kThreads;
-    if (q >= nq) break;
+    if (!Full && q >= nq) break;
     float cv[8];
     code_values<C, 8>(w[u], cv);
     float v[8];
@@ -458,6 +504,18 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* wire, OutPt
                     u32x4{st16x2<D>(v[0], v[1]), st16x2<D>(v[2], v[3]),
                           st16x2<D>(v[4], v[5]), st16x2<D>(v[6], v[7])});
   }
+}
+
+template <int C, int D>
+__global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* wire, OutPtrs ys,
+                                                      Geo g) {
+  const int r = blockIdx.y;
+  const uint32_t nq = (g.n + 7) / 8;                // quarters that hold data
+  const uint32_t q0 = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
+  if (tile_full(blockIdx.x, g.n))
+    dequant_tile<C, D, true>(wire, ys.p[r], q0, nq, g);
+  else
+    dequant_tile<C, D, false>(wire, ys.p[r], q0, nq, g);
 }
 
 // ---------------------------------------------------------------------------

@@ -76,10 +76,14 @@ def _is_inf(bits, dtype):
     return (bits & 0x7FFF) == (0x7C00 if dtype == O.FP16 else 0x7F80)
 
 
-def assert_within_ulp(got, want, dtype, what, ulps=1):
+def assert_within_ulp(got, want, dtype, what, ulps=0):
     """outputs within `ulps` units in the last place of the buffer type
     (ordered-integer distance; +0 and -0 equal; inf only equals inf of the
-    same sign); returns how many elements are not bit-identical."""
+    same sign); returns how many elements are not bit-identical.  The default
+    is 0: the kernels round exactly as the definition does (binary32, then
+    the buffer type), so any 1-ulp difference is a rounding-order bug (one
+    such, a binary32 result rounded straight to binary16 by a merged
+    instruction, differed by exactly 1 ulp on rare elements)."""
     got, want = np.asarray(got, np.uint16), np.asarray(want, np.uint16)
     assert got.shape == want.shape
     assert np.array_equal(_is_nan(got, dtype), _is_nan(want, dtype)), what

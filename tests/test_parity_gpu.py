@@ -107,6 +107,87 @@ def test_parity_cast(qr, codec, W):
                     "cast edges c%d W%d n%d" % (codec, W, n))
 
 
+def _pack_codes(codes, bits):
+    """b-bit codes of 32-element blocks into the little-endian bitstream of
+    each block (code i at bits [b*i, b*i+b))"""
+    c = np.asarray(codes, np.uint64).reshape(-1, 32)
+    if bits == 8:
+        return c.astype(np.uint8).reshape(-1)
+    out = np.zeros((c.shape[0], 32 * bits // 8), np.uint8)
+    for i in range(32):
+        for j in range(bits):
+            bit = bits * i + j
+            out[:, bit // 8] |= (((c[:, i] >> np.uint64(j)) & np.uint64(1))
+                                 << np.uint64(bit % 8)).astype(np.uint8)
+    return out.reshape(-1)
+
+
+def _rounding_wire(codec, nb, seed):
+    """An asymmetric wire image of nb blocks in which every other block has a
+    scale s, zero z and code u such that u*s + z, rounded to binary32, lands
+    exactly on the midpoint between two binary16 neighbours while the exact
+    value does not; returns the wire and how many elements round differently
+    when the exact value is rounded straight to binary16."""
+    qu = {O.Q8A: 255, O.Q6A: 63, O.Q4A: 15}[codec]
+    bits = {O.Q8A: 8, O.Q6A: 6, O.Q4A: 4}[codec]
+    g = np.random.default_rng(seed)
+    sv = np.arange(1, 0x7c00, dtype=np.uint16)
+    sf = sv.view(np.float16).astype(np.float64)
+    triples = []                    # (u, scale bits, binade e of the zero)
+    for u in range(1, qu + 1):
+        for e in range(0, 15):
+            m, half = 2.0 ** (e - 11), 2.0 ** (e - 24)
+            hit = (np.abs(u * sf - m) < half) & (u * sf != m)
+            triples += [(u, int(b), e) for b in sv[hit]]
+    codes = g.integers(0, qu + 1, (nb, 32))
+    scale = g.integers(0x0400, 0x3000, nb).astype(np.uint16)      # random normal scales
+    zero = (g.standard_normal(nb) * 4).astype(np.float16).view(np.uint16)
+    if triples:
+        for k in range(0, nb, 2):
+            u, sb, e = triples[g.integers(len(triples))]
+            codes[k, :] = u
+            scale[k] = sb
+            zero[k] = np.float16(2.0 ** e * (1.0 + g.integers(0, 1024) / 1024.0)).view(np.uint16)
+    n = 32 * nb
+    wire = np.zeros(O.wire_bytes(codec, n), np.uint8)
+    wire[:nb * 32 * bits // 8] = _pack_codes(codes, bits)
+    so, zo = O.scale_offset(codec, n), O.zero_offset(codec, n)
+    wire[so:so + 2 * nb] = scale.view(np.uint8)
+    wire[zo:zo + 2 * nb] = zero.view(np.uint8)
+    exact = codes * scale.view(np.float16).astype(np.float64)[:, None] + \
+        zero.view(np.float16).astype(np.float64)[:, None]          # exact in binary64
+    twice = exact.astype(np.float32).astype(np.float16)
+    once = exact.astype(np.float16)
+    return wire, int(np.count_nonzero(twice.view(np.uint16) != once.view(np.uint16)))
+
+
+@pytest.mark.parametrize("codec", (O.Q8A, O.Q6A, O.Q4A), ids=("q8a", "q6a", "q4a"))
+def test_dequant_rounds_through_binary32(qr, codec):
+    """asymmetric dequantization rounds code*scale + zero to binary32 first and
+    then to the buffer type, as the definition does; built wires put many
+    binary32 values exactly on binary16 midpoints that the exact values are not
+    on (none exist for Q4A: a 4-bit code times a binary16 scale is too short)"""
+    nb = 4096
+    wire_np, diverging = _rounding_wire(codec, nb, 7 + codec)
+    if codec != O.Q4A:
+        assert diverging >= 1000, diverging
+    n = 32 * nb
+    wire = torch.from_numpy(wire_np).cuda()
+    for dtype in (O.FP16, O.BF16, O.BF16_VIA_FP16):
+        say("double rounding", codec, dtype, diverging)
+        y = torch.empty(n, dtype=torch.int16, device="cuda")
+        qr.qr_dequantize(codec, wire, y, dtype=dtype)
+        ys = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(2)]
+        qr.qr_gather_stage2(codec, wire, ys, dtype=dtype)
+        torch.cuda.synchronize()
+        want = O.dequantize(codec, dtype, wire_np, n)
+        for got, what in ((y, "dequantize"), (ys[0], "stage 2"), (ys[1], "stage 2")):
+            g_ = host16(got)
+            bad = np.nonzero(g_ != want)[0]
+            assert bad.size == 0, "%s dtype %d: %d elements differ, first %d got %04x want %04x" % (
+                what, dtype, bad.size, bad[0], g_[bad[0]], want[bad[0]])
+
+
 def test_golden_fixtures_gpu(qr):
     """The hand-worked examples through the HIP path."""
     for case in pins.golden_cases():
