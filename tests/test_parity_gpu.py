@@ -1,6 +1,6 @@
 """Parity of the HIP path with the oracle, element by element, through the C
-ABI: every wire plane (codes, scales, zeros) bit-exact, every output within
-1 ulp of the buffer type (in practice identical), for every codec x buffer
+ABI: every wire plane (codes, scales, zeros) and every output bit-exact (+0
+and -0 compare equal in outputs), for every codec x buffer
 type x W in {2,4,8}, at sizes that span several 256-lane workgroups and end in
 a ragged partial block; plus the hand-worked fixtures, owner-restricted
 stage 1, edge cases, guard bands and the no-write-on-error rule."""
@@ -96,8 +96,8 @@ def _cast_edges(W, n, salt):
 @pytest.mark.parametrize("W", (2, 4, 8))
 @pytest.mark.parametrize("codec", CODECS, ids=[I.CODEC_NAMES[c] for c in CODECS])
 def test_parity_cast(qr, codec, W):
-    """the bf16 -> fp16 cast option: every wire plane bit-exact and every
-    output within 1 ulp of the oracle, on the bf16 workloads' generators and
+    """the bf16 -> fp16 cast option: every wire plane and every output
+    bit-exact against the oracle, on the bf16 workloads' generators and
     on inputs spread over binary16's whole range (subnormals, underflow)"""
     for n in SIZES:
         for cfg in (3, 4):
