@@ -151,9 +151,14 @@ int qr_gather_stage2(qr_codec codec, qr_dtype dtype, int W,
                      void* stream);
 
 /* The whole simulated allreduce: ys[r] = stage2(stage1(quantize(xs[0..W-1])))
- * for every r.  Three launches on `stream`.  `workspace` is caller-owned
- * device memory of at least qr_sim_workspace_bytes(W, codec, n) bytes that
- * must not overlap any x or y. */
+ * for every r.  `workspace` is caller-owned device memory of at least
+ * qr_sim_workspace_bytes(W, codec, n) bytes that must not overlap any x or y;
+ * it receives the W wire images and the reduced image, as the staged calls
+ * would write them.  Launches on `stream`: for W <= 4 and 2n <= 4 MiB, one
+ * (each workgroup takes its tile of blocks through all three stages, reading
+ * the wire and reduced images back from the workspace); otherwise three, the
+ * kernels of qr_quantize_ranks, qr_reduce_stage1 and qr_gather_stage2.  Both
+ * give the same outputs and workspace contents. */
 int qr_allreduce_sim(int W, qr_dtype dtype, qr_codec codec,
                      const void* const* xs, void* const* ys, size_t n,
                      void* workspace, size_t ws_bytes, void* stream);

@@ -38,6 +38,12 @@ hipError_t launch_stage1(int codec, int dtype, int W, const InPtrs& wires,
 // stage 2 / dequantize for W outputs: ys.p[r] <- dequant(wire)
 hipError_t launch_dequantize(int codec, int dtype, int W, const uint8_t* wire,
                              const OutPtrs& ys, const Layout& L, hipStream_t st);
+// the three stages in one launch (each workgroup runs all three for its
+// tile of blocks): wires.p[r] <- quantize(xs.p[r]), reduced <- stage 1,
+// ys.p[r] <- dequant(reduced); same results and workspace as the three
+// separate launches
+hipError_t launch_fused(int codec, int dtype, int W, const InPtrs& xs, const OutPtrs& wires,
+                        uint8_t* reduced, const OutPtrs& ys, const Layout& L, hipStream_t st);
 // one-stage allreduce: ys.p[r] <- round(sum of xs.p[0..W-1] in rank order), all r
 hipError_t launch_oneshot(int dtype, int W, const InPtrs& xs, const OutPtrs& ys, size_t n,
                           hipStream_t st);

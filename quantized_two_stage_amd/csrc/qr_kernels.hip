@@ -53,6 +53,7 @@ constexpr int kPerLane = 4;        // quarters / chunks per lane (k_quantize,
 #define QR_NT_LOAD 0
 #endif
 constexpr int kStage0 = 1, kStage1 = 2, kStage2 = 4;
+constexpr int kKeep = 0;           // store policy: always through the caches
 
 template <int Stage, typename V>
 __device__ __forceinline__ void st_out(V* p, V v) {
@@ -235,7 +236,7 @@ __device__ __forceinline__ void quantize_quarters(float (&v)[4][8], uint32_t q0,
   }
 }
 
-template <int C, int D, bool Full>
+template <int C, int D, bool Full, int Stage = kStage0>
 __device__ __forceinline__ void quantize_tile(const u32x4 (&raw)[4], uint32_t q0,
                                               uint8_t* wire, const Geo& g) {
   float v[4][8];
@@ -248,7 +249,7 @@ __device__ __forceinline__ void quantize_tile(const u32x4 (&raw)[4], uint32_t q0
       v[u][2 * k + 1] = ld16<D>(rw[k] >> 16);
     }
   }
-  quantize_quarters<C, kStage0, Full>(v, q0, 4 * g.nb, wire, g);
+  quantize_quarters<C, Stage, Full>(v, q0, 4 * g.nb, wire, g);
 }
 
 template <bool Full>
@@ -475,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void k_sum_fp(InPtrs xs, OutPtrs outs,
 // stage 2 / dequantize: one quarter block per lane, kPerLane quarters
 
 // quarters q0 + 256u (u = 0..3) of the wire -> y; Full: all hold 8 elements
-template <int C, int D, bool Full>
+template <int C, int D, bool Full, int Stage = kStage2>
 __device__ __forceinline__ void dequant_tile(const uint8_t* wire, uint8_t* y, uint32_t q0,
                                              uint32_t nq, const Geo& g) {
   using T = CodecT<C>;
@@ -500,9 +501,9 @@ __device__ __forceinline__ void dequant_tile(const uint8_t* wire, uint8_t* y, ui
 #pragma unroll
     for (int i = 0; i < 8; i++)
       v[i] = T::asym ? __builtin_fmaf(cv[i], s[u], z[u]) : cv[i] * s[u];
-    st_out<kStage2>(reinterpret_cast<u32x4*>(y) + q,
-                    u32x4{st16x2<D>(v[0], v[1]), st16x2<D>(v[2], v[3]),
-                          st16x2<D>(v[4], v[5]), st16x2<D>(v[6], v[7])});
+    st_out<Stage>(reinterpret_cast<u32x4*>(y) + q,
+                  u32x4{st16x2<D>(v[0], v[1]), st16x2<D>(v[2], v[3]),
+                        st16x2<D>(v[4], v[5]), st16x2<D>(v[6], v[7])});
   }
 }
 
@@ -516,6 +517,127 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* wire, OutPt
     dequant_tile<C, D, true>(wire, ys.p[r], q0, nq, g);
   else
     dequant_tile<C, D, false>(wire, ys.p[r], q0, nq, g);
+}
+
+// ---------------------------------------------------------------------------
+// the whole simulated allreduce in one launch, for buffers small enough that
+// three launches cost more than their work.  Workgroup T runs the three
+// stages for blocks [256T, 256T+256) of every rank: stage 0 writes each
+// rank's wire blocks to the workspace, stage 1 reads them back from there
+// and writes the reduced blocks, stage 2 reads those back and writes every
+// rank's output, with a workgroup barrier between the stages.  A block's
+// three stages never need another block, so no workgroup waits for another,
+// and the workspace and outputs are those of the three separate kernels.
+// The wire and reduced images are stored through the caches (the same
+// workgroup reads them next).
+
+template <int C, int D, int W, bool Full>
+__device__ __forceinline__ void fused_stage0(const InPtrs& xs, const OutPtrs& wires,
+                                             uint32_t q0, const Geo& g) {
+  u32x4 raw[W][4];
+#pragma unroll
+  for (int r = 0; r < W; r++) load_tile<Full>(xs.p[r], q0, g.n, raw[r]);
+#pragma unroll
+  for (int r = 0; r < W; r++) quantize_tile<C, D, Full, kKeep>(raw[r], q0, wires.p[r], g);
+}
+
+template <int C, int D, int W>
+__global__ __launch_bounds__(kThreads) void k_fused(InPtrs xs, OutPtrs wires, uint8_t* red,
+                                                    OutPtrs ys, Geo g) {
+  const uint32_t T = blockIdx.x;
+  const uint32_t q0 = T * (kThreads * kPerLane) + threadIdx.x;   // this lane's quarters
+  const uint32_t blk = T * kThreads + threadIdx.x;               // this lane's block
+  const bool full = tile_full(T, g.n);                           // uniform
+  InPtrs win;
+#pragma unroll
+  for (int r = 0; r < W; r++) win.p[r] = wires.p[r];
+  // every rank's loads are issued before any is quantized: at the small sizes
+  // this kernel serves, the memory round trips are the time
+  if (full)
+    fused_stage0<C, D, W, true>(xs, wires, q0, g);
+  else
+    fused_stage0<C, D, W, false>(xs, wires, q0, g);
+  __syncthreads();
+  if (full) {
+    S1In<C, W> in;
+    s1_load<C, W>(win, blk, g, in);
+    s1_reduce_store<C, W, true>(in, red, blk, g);
+  } else if (blk < g.nb) {
+    S1In<C, W> in;
+    s1_load<C, W>(win, blk, g, in);
+    s1_reduce_store<C, W, false>(in, red, blk, g);
+  }
+  __syncthreads();
+  const uint32_t nq = (g.n + 7) / 8;
+#pragma unroll
+  for (int r = 0; r < W; r++) {
+    if (full)
+      dequant_tile<C, D, true>(red, ys.p[r], q0, nq, g);
+    else
+      dequant_tile<C, D, false>(red, ys.p[r], q0, nq, g);
+  }
+}
+
+// the FP codec in one launch: copy (converting under the cast option), sum,
+// copy back, over the 1024 chunks of 16 bytes of workgroup T
+template <int D, int W>
+__global__ __launch_bounds__(kThreads) void k_fused_fp(InPtrs xs, OutPtrs wires, uint8_t* red,
+                                                       OutPtrs ys, uint32_t nchunks) {
+  constexpr int Dw = D == kBF16H ? kF16 : D;      // the wire's element type
+  constexpr int Dx = D == kBF16H ? kBF16 : D;     // the buffers' element type
+  const uint32_t c0 = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
+#pragma unroll
+  for (int r = 0; r < W; r++) {
+#pragma unroll
+    for (int j = 0; j < kPerLane; j++) {
+      const uint32_t c = c0 + j * kThreads;
+      if (c >= nchunks) break;
+      u32x4 q = reinterpret_cast<const u32x4*>(xs.p[r])[c];
+      if constexpr (Dx != Dw) {
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+          q[k] = st16x2<Dw>(ld16<Dx>(q[k] & 0xffffu), ld16<Dx>(q[k] >> 16));
+      }
+      reinterpret_cast<u32x4*>(wires.p[r])[c] = q;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPerLane; j++) {
+    const uint32_t c = c0 + j * kThreads;
+    if (c >= nchunks) break;
+    u32x4 q[W];
+#pragma unroll
+    for (int r = 0; r < W; r++) q[r] = reinterpret_cast<const u32x4*>(wires.p[r])[c];
+    uint32_t out[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      float lo = ld16<Dw>(q[0][k] & 0xffffu), hi = ld16<Dw>(q[0][k] >> 16);
+#pragma unroll
+      for (int r = 1; r < W; r++) {
+        lo = lo + ld16<Dw>(q[r][k] & 0xffffu);
+        hi = hi + ld16<Dw>(q[r][k] >> 16);
+      }
+      out[k] = st16x2<Dw>(lo, hi);
+    }
+    reinterpret_cast<u32x4*>(red)[c] = u32x4{out[0], out[1], out[2], out[3]};
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < W; r++) {
+#pragma unroll
+    for (int j = 0; j < kPerLane; j++) {
+      const uint32_t c = c0 + j * kThreads;
+      if (c >= nchunks) break;
+      u32x4 q = reinterpret_cast<const u32x4*>(red)[c];
+      if constexpr (Dx != Dw) {
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+          q[k] = st16x2<Dx>(ld16<Dw>(q[k] & 0xffffu), ld16<Dw>(q[k] >> 16));
+      }
+      st_out<kStage2>(reinterpret_cast<u32x4*>(ys.p[r]) + c, q);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -597,6 +719,30 @@ void dq_dispatch(int W, const uint8_t* wire, const OutPtrs& ys, const Layout& L,
   }
 }
 
+template <int C, int D, int W>
+void fused_launch(const InPtrs& xs, const OutPtrs& wires, uint8_t* red, const OutPtrs& ys,
+                  const Layout& L, hipStream_t st) {
+  if constexpr (C == kFP) {
+    const uint32_t nc = (uint32_t)(L.n / 8);
+    hipLaunchKernelGGL((k_fused_fp<D, W>), dim3(groups(nc, kThreads * kPerLane)),
+                       dim3(kThreads), 0, st, xs, wires, red, ys, nc);
+  } else {
+    hipLaunchKernelGGL((k_fused<C, D, W>), dim3(groups(L.nb, kThreads)), dim3(kThreads), 0,
+                       st, xs, wires, red, ys, geo(L));
+  }
+}
+
+template <int C, int D>
+void fused_by_w(int W, const InPtrs& xs, const OutPtrs& wires, uint8_t* red, const OutPtrs& ys,
+                const Layout& L, hipStream_t st) {
+  switch (W) {
+    case 2: fused_launch<C, D, 2>(xs, wires, red, ys, L, st); break;
+    case 4: fused_launch<C, D, 4>(xs, wires, red, ys, L, st); break;
+    case 8: fused_launch<C, D, 8>(xs, wires, red, ys, L, st); break;
+    default: break;
+  }
+}
+
 // calls FN<codec, dtype>(args...) for the runtime (codec, dtype)
 #define QR_BY_DTYPE(C, dtype, FN, ...)                                                  \
   ((dtype) == kBF16H ? FN<C, kBF16H>(__VA_ARGS__)                                       \
@@ -617,6 +763,12 @@ void dq_dispatch(int W, const uint8_t* wire, const OutPtrs& ys, const Layout& L,
   } while (0)
 
 }  // namespace
+
+hipError_t launch_fused(int codec, int dtype, int W, const InPtrs& xs, const OutPtrs& wires,
+                        uint8_t* reduced, const OutPtrs& ys, const Layout& L, hipStream_t st) {
+  QR_DISPATCH(codec, dtype, fused_by_w, W, xs, wires, reduced, ys, L, st);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(int codec, int dtype, int W, const InPtrs& xs,
                            const OutPtrs& wires, const Layout& L, hipStream_t st) {

@@ -163,3 +163,18 @@ def test_cast_option_full(qr, cfg, codec):
     64 MB (configuration 3's largest size) and 16 MB W=8"""
     _check_full(qr, cfg, codec, n=(1 << 25) if cfg == 3 else None, windows=8,
                 dtype=O.BF16_VIA_FP16)
+
+
+FUSED_EDGE = 2 * 1024 * 1024          # elements: 4 MiB per rank, the single-launch limit
+
+
+@pytest.mark.parametrize("n", (FUSED_EDGE, FUSED_EDGE + 8), ids=("4MiB-one-launch", "above"))
+@pytest.mark.parametrize("codec", (O.FP, O.FP8, O.Q8, O.Q6, O.Q4, O.Q8A, O.Q6A, O.Q4A),
+                         ids=[I.CODEC_NAMES[c] for c in (O.FP, O.FP8, O.Q8, O.Q6, O.Q4, O.Q8A,
+                                                           O.Q6A, O.Q4A)])
+def test_sim_launch_paths(qr, codec, n):
+    """qr_allreduce_sim at the size where it switches from one launch to
+    three, W=2 fp16 and W=4 bf16: every element equals the staged calls',
+    sampled blocks equal the oracle's"""
+    _check_full(qr, 2, codec, n=n, windows=6)
+    _check_full(qr, 3, codec, n=n, windows=6)

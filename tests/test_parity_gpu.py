@@ -53,6 +53,20 @@ def _check_case(qr, codec, dtype, xs_np, label):
     torch.cuda.synchronize()
     for r in range(W):
         assert_within_ulp(host16(ys2[r]), r_ys[r], dtype, "%s sim y[%d]" % (label, r))
+    # the workspace holds the W wire images and the reduced image (whichever
+    # launch path the call took), and the padding between planes is untouched
+    wb = qr.qr_wire_bytes(codec, n)
+    stride = (wb + 255) // 256 * 256
+    wsh = hostu8(ws)
+    planes = plane_slices(codec, n)
+    for r in range(W + 1):
+        img = wsh[r * stride:r * stride + wb]
+        want = r_wires[r] if r < W else r_red
+        keep = np.ones(wb, bool)
+        for name, (a, e) in planes.items():
+            assert_bytes_equal(img[a:e], want[a:e], "%s sim workspace %d %s" % (label, r, name))
+            keep[a:e] = False
+        assert np.all(img[keep] == 0xA7), (label, "workspace padding written", r)
     # inputs are never modified
     for r in range(W):
         assert np.array_equal(host16(xs[r]), xs_np[r]), label
