@@ -154,9 +154,9 @@ int qr_gather_stage2(qr_codec codec, qr_dtype dtype, int W,
  * for every r.  `workspace` is caller-owned device memory of at least
  * qr_sim_workspace_bytes(W, codec, n) bytes that must not overlap any x or y;
  * it receives the W wire images and the reduced image, as the staged calls
- * would write them.  Launches on `stream`: for W <= 4 and 2n <= 4 MiB, one
- * (each workgroup takes its tile of blocks through all three stages, reading
- * the wire and reduced images back from the workspace); otherwise three, the
+ * would write them.  Launches on `stream`: for 2n <= 4 MiB, one (each
+ * workgroup takes its tile of blocks through all three stages, reading the
+ * wire and reduced images back from the workspace); above, three, the
  * kernels of qr_quantize_ranks, qr_reduce_stage1 and qr_gather_stage2.  Both
  * give the same outputs and workspace contents. */
 int qr_allreduce_sim(int W, qr_dtype dtype, qr_codec codec,

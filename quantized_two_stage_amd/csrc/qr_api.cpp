@@ -51,11 +51,10 @@ Layout make_layout(int codec, size_t n) {
 }  // namespace qr
 
 // qr_allreduce_sim runs its three stages as one launch (each workgroup
-// carrying its tile of blocks through all three) for W <= 4 up to this many
-// bytes per rank buffer, and as three launches otherwise.  Measured on
-// MI355X: the single launch saves 3-4 us per call at W=2 and 1-2 us at W=4
-// up to 4 MiB; at W=8 one workgroup's serial work on eight ranks costs more
-// than the two launches it saves.
+// carrying its tile of blocks through all three) up to this many bytes per
+// rank buffer, and as three launches above.  Measured on MI355X: up to 4 MiB
+// the single launch halves the time of a call (about 4.5-6 us instead of
+// 9-11 us at W = 2, 4 and 8); above, the launches are no longer the cost.
 #ifndef QR_FUSED_MAX_BYTES
 #define QR_FUSED_MAX_BYTES ((size_t)4 << 20)
 #endif
@@ -286,7 +285,7 @@ int qr_allreduce_sim(int W, qr_dtype dtype, qr_codec codec, const void* const* x
   uint8_t* reduced = ws + (size_t)W * stride;
   hipStream_t st = as_stream(stream);
   (void)hipGetLastError();
-  if (W <= 4 && 2 * n <= QR_FUSED_MAX_BYTES)
+  if (2 * n <= QR_FUSED_MAX_BYTES)
     return hip_status(qr::launch_fused(codec, dtype, W, in, wires_out, reduced, out, L, st),
                       "fused launch");
   QR_TRY(hip_status(qr::launch_quantize(codec, dtype, W, in, wires_out, L, st),

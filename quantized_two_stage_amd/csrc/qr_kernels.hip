@@ -156,55 +156,72 @@ __device__ __forceinline__ float from_lane(float v) { return quad_perm<U * 0x55>
 template <int U>
 __device__ __forceinline__ uint32_t from_lane_u(uint32_t v) { return quad_perm_u<U * 0x55>(v); }
 
-// Quantizes 4 quarters per lane (quarter q0 + 256u, u = 0..3; a quad of lanes
-// holds the 4 quarters of 4 blocks) from their values v[u][0..8): block
-// statistics through quad permutes, lane j computes the parameters of the
-// quad's block j and stores its scale (and zero), then every lane encodes
-// and stores its own quarters.  Quarters at or past q_end store nothing;
-// quarters holding no element (8q >= n) are left out of the statistics and
-// get code 0.  q_end is a multiple of 4, so a quad is wholly in or out.
-// Full: the caller guarantees that every quarter of the workgroup holds 8
-// elements and lies below q_end (no range checks are made).
-template <int C, int Stage, bool Full>
-__device__ __forceinline__ void quantize_quarters(float (&v)[4][8], uint32_t q0,
-                                                  uint32_t q_end, uint8_t* wire,
-                                                  const Geo& g) {
+// Quantizes U slots of 8 values per lane (U = 1, 2 or 4): slot u holds
+// quarter q[u] of the wire image wire[u], and in every slot the four lanes of
+// a quad hold the four quarters of one block (lane j quarter j).  Block
+// statistics come through quad permutes; lane j derives the parameters of
+// slot (j mod U)'s block, lane j < U stores that block's scale (and zero) and
+// hands 1/s, the zero and two flags to the quad; every lane then encodes and
+// stores its own quarter of every slot.  own_wire and own_q are wire[j mod U]
+// and q[j mod U], which the caller can form more cheaply than a select.
+// Quarters at or past q_end store nothing; quarters holding no element
+// (8q >= n) are left out of the statistics and get code 0.  q_end is a
+// multiple of 4, so a quad is wholly in or out.  Full: the caller guarantees
+// that every quarter holds 8 elements and lies below q_end (no range checks
+// are made).
+template <int C, int Stage, bool Full, int U>
+__device__ __forceinline__ void quantize_core(float (&v)[U][8], uint8_t* const (&wire)[U],
+                                              const uint32_t (&q)[U], uint8_t* own_wire,
+                                              uint32_t own_q, uint32_t q_end, const Geo& g) {
+  static_assert(U == 1 || U == 2 || U == 4, "slots per lane");
   using T = CodecT<C>;
   constexpr int nw = (8 * T::bits + 31) / 32;
   const int j = threadIdx.x & 3;                // this lane's quarter of each block
   // every lane stays active through the quad exchanges below; quarters past
   // the end compute on stand-in data and store nothing
-  float mx[4], mn[4];
+  float mx[U], mn[U];
 #pragma unroll
-  for (int u = 0; u < 4; u++) {
-    group_max_min(v[u], Full || 8 * (q0 + u * kThreads) < g.n, mx[u], mn[u]);
+  for (int u = 0; u < U; u++) {
+    group_max_min(v[u], Full || 8 * q[u] < g.n, mx[u], mn[u]);
     mx[u] = quad_max<kSwap2>(quad_max<kSwap1>(mx[u]));
     mn[u] = quad_min<kSwap2>(quad_min<kSwap1>(mn[u]));
   }
-  // lane j: parameters of block j of the quad
-  const float bx = j == 0 ? mx[0] : j == 1 ? mx[1] : j == 2 ? mx[2] : mx[3];
-  const float bn = j == 0 ? mn[0] : j == 1 ? mn[1] : j == 2 ? mn[2] : mn[3];
+  // lane j: parameters of slot j mod U
+  float bx = mx[0], bn = mn[0];
+#pragma unroll
+  for (int u = 1; u < U; u++) {
+    if (j % U == u) {
+      bx = mx[u];
+      bn = mn[u];
+    }
+  }
   const BlockParams<C> p = block_params<C>(bx, bn);
-  const uint32_t own_q = q0 + j * kThreads;
-  if (Full || own_q < q_end) {
+  if (j < U && (Full || own_q < q_end)) {
     const uint32_t own_blk = own_q >> 2;
-    st_u16(wire + g.off_s + (size_t)own_blk * 2, p.s);
-    if constexpr (T::asym) st_u16(wire + g.off_z + (size_t)own_blk * 2, p.z);
+    st_u16(own_wire + g.off_s + (size_t)own_blk * 2, p.s);
+    if constexpr (T::asym) st_u16(own_wire + g.off_z + (size_t)own_blk * 2, p.z);
   }
   const uint32_t flags = (p.sat ? 1u : 0u) | (p.s != 0u ? 2u : 0u);
-  float inv[4], tz[4];
-  uint32_t fl[4];
-  inv[0] = from_lane<0>(p.inv); inv[1] = from_lane<1>(p.inv);
-  inv[2] = from_lane<2>(p.inv); inv[3] = from_lane<3>(p.inv);
-  fl[0] = from_lane_u<0>(flags); fl[1] = from_lane_u<1>(flags);
-  fl[2] = from_lane_u<2>(flags); fl[3] = from_lane_u<3>(flags);
-  if constexpr (T::asym) {
-    tz[0] = from_lane<0>(p.tz); tz[1] = from_lane<1>(p.tz);
-    tz[2] = from_lane<2>(p.tz); tz[3] = from_lane<3>(p.tz);
+  float inv[U], tz[U];
+  uint32_t fl[U];
+  inv[0] = from_lane<0>(p.inv);
+  fl[0] = from_lane_u<0>(flags);
+  if constexpr (T::asym) tz[0] = from_lane<0>(p.tz);
+  if constexpr (U > 1) {
+    inv[1] = from_lane<1>(p.inv);
+    fl[1] = from_lane_u<1>(flags);
+    if constexpr (T::asym) tz[1] = from_lane<1>(p.tz);
+  }
+  if constexpr (U > 2) {
+    inv[2] = from_lane<2>(p.inv); inv[3] = from_lane<3>(p.inv);
+    fl[2] = from_lane_u<2>(flags); fl[3] = from_lane_u<3>(flags);
+    if constexpr (T::asym) {
+      tz[2] = from_lane<2>(p.tz);
+      tz[3] = from_lane<3>(p.tz);
+    }
   }
 #pragma unroll
-  for (int u = 0; u < 4; u++) {
-    const uint32_t q = q0 + u * kThreads;
+  for (int u = 0; u < U; u++) {
     float t[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) t[i] = T::asym ? (v[u][i] - tz[u]) * inv[u] : v[u][i] * inv[u];
@@ -212,28 +229,39 @@ __device__ __forceinline__ void quantize_quarters(float (&v)[4][8], uint32_t q0,
     encode<C, 8>(t, (fl[u] & 1u) != 0u, w);
     // fp8: an all-zero block gives code 0x00 even for -0 inputs; every codec:
     // quarters beyond the buffer hold code 0
-    const bool keep = (Full || 8 * q < g.n) && (!T::fp8 || (fl[u] & 2u) != 0u);
+    const bool keep = (Full || 8 * q[u] < g.n) && (!T::fp8 || (fl[u] & 2u) != 0u);
 #pragma unroll
     for (int k = 0; k < nw; k++) w[k] = keep ? w[k] : 0u;
-    uint8_t* cb = wire + (size_t)(q >> 2) * T::block_bytes;
+    uint8_t* cb = wire[u] + (size_t)(q[u] >> 2) * T::block_bytes;
     if constexpr (T::bits == 6) {
       // lanes 0 and 2 of the quad each write 96 bits (their own 48 and their
       // odd neighbour's 48)
       const uint32_t o0 = quad_perm_u<kFromOdd>(w[0]);
       const uint32_t o1 = quad_perm_u<kFromOdd>(w[1]);
-      if ((Full || q < q_end) && (j & 1) == 0) {
+      if ((Full || q[u] < q_end) && (j & 1) == 0) {
         uint32_t* d = reinterpret_cast<uint32_t*>(cb) + 3 * (j >> 1);
         st_out<Stage>(d, w[0]);
         st_out<Stage>(d + 1, (w[1] & 0xffffu) | (o0 << 16));
         st_out<Stage>(d + 2, (o0 >> 16) | (o1 << 16));
       }
-    } else if (Full || q < q_end) {
+    } else if (Full || q[u] < q_end) {
       if constexpr (T::bits == 4)
         st_out<Stage>(reinterpret_cast<uint32_t*>(cb) + j, w[0]);
       else
         st_out<Stage>(reinterpret_cast<u32x2*>(cb) + j, u32x2{w[0], w[1]});
     }
   }
+}
+
+// four quarters q0 + 256u (u = 0..3) of one wire image: a quad holds the
+// quarters of four blocks, one per slot
+template <int C, int Stage, bool Full>
+__device__ __forceinline__ void quantize_quarters(float (&v)[4][8], uint32_t q0,
+                                                  uint32_t q_end, uint8_t* wire,
+                                                  const Geo& g) {
+  uint8_t* const wp[4] = {wire, wire, wire, wire};
+  const uint32_t qs[4] = {q0, q0 + kThreads, q0 + 2 * kThreads, q0 + 3 * kThreads};
+  quantize_core<C, Stage, Full, 4>(v, wp, qs, wire, q0 + (threadIdx.x & 3) * kThreads, q_end, g);
 }
 
 template <int C, int D, bool Full, int Stage = kStage0>
@@ -521,77 +549,140 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* wire, OutPt
 
 // ---------------------------------------------------------------------------
 // the whole simulated allreduce in one launch, for buffers small enough that
-// three launches cost more than their work.  Workgroup T runs the three
-// stages for blocks [256T, 256T+256) of every rank: stage 0 writes each
-// rank's wire blocks to the workspace, stage 1 reads them back from there
-// and writes the reduced blocks, stage 2 reads those back and writes every
-// rank's output, with a workgroup barrier between the stages.  A block's
-// three stages never need another block, so no workgroup waits for another,
-// and the workspace and outputs are those of the three separate kernels.
-// The wire and reduced images are stored through the caches (the same
-// workgroup reads them next).
+// three launches cost more than their work.  A block's three stages need no
+// other block, so workgroup T takes blocks [64T, 64T+64) of every rank
+// through all three with workgroup barriers in between, and no workgroup
+// waits for another.  Lane l holds quarter 256T + l (a quad of lanes = one
+// block):
+//   stage 0  the lane's quarter of every rank, four ranks at a time as the
+//            four slots of quantize_core (lane j of the quad derives the
+//            scale of rank j's block), written to the rank's wire image;
+//   stage 1  the W wire quarters read back, dequantized and summed in rank
+//            order, quantized as one slot into the reduced image;
+//   stage 2  the reduced quarter read back, dequantized once and stored to
+//            every rank's output (each rank's output is the same function of
+//            the same reduced block).
+// The arithmetic is that of the three separate kernels, element for element,
+// so the outputs and the workspace are theirs.  The wire and reduced images
+// are stored through the caches: the same workgroup reads them next.
 
 template <int C, int D, int W, bool Full>
-__device__ __forceinline__ void fused_stage0(const InPtrs& xs, const OutPtrs& wires,
-                                             uint32_t q0, const Geo& g) {
-  u32x4 raw[W][4];
+__device__ __forceinline__ void fused_tile(const InPtrs& xs, const OutPtrs& wires, uint8_t* red,
+                                           const OutPtrs& ys, uint32_t q, const Geo& g) {
+  using T = CodecT<C>;
+  using IO = QuarterIO<C>;
+  constexpr int U = W < 4 ? W : 4;                 // ranks per quantize_core call
+  const uint32_t q_end = 4 * g.nb;
+  const uint32_t nq = (g.n + 7) / 8;               // quarters that hold data
+  const bool has = Full || q < nq;
+  const uint32_t ql = has ? q : 0u;                // stand-in for loads past the data
+  const int j = threadIdx.x & 3;
+
+  // stage 0: every rank's quarter is loaded before any is quantized
+  u32x4 raw[W];
 #pragma unroll
-  for (int r = 0; r < W; r++) load_tile<Full>(xs.p[r], q0, g.n, raw[r]);
+  for (int r = 0; r < W; r++) raw[r] = reinterpret_cast<const u32x4*>(xs.p[r])[ql];
 #pragma unroll
-  for (int r = 0; r < W; r++) quantize_tile<C, D, Full, kKeep>(raw[r], q0, wires.p[r], g);
+  for (int k = 0; k < W / U; k++) {
+    float v[U][8];
+    uint8_t* wp[U];
+    uint32_t qs[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const u32x4 x = raw[k * U + u];
+      const uint32_t rw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        v[u][2 * i] = ld16<D>(rw[i] & 0xffffu);
+        v[u][2 * i + 1] = ld16<D>(rw[i] >> 16);
+      }
+      wp[u] = wires.p[k * U + u];
+      qs[u] = q;
+    }
+    uint8_t* own = wp[0];
+#pragma unroll
+    for (int u = 1; u < U; u++)
+      if (j % U == u) own = wp[u];
+    quantize_core<C, kKeep, Full, U>(v, wp, qs, own, q, q_end, g);
+  }
+  __syncthreads();
+
+  // stage 1: the lane's quarter of the reduced block
+  {
+    const uint32_t blk = ql >> 2;
+    uint32_t w[W][IO::nw];
+    float sc[W], zc[W];
+#pragma unroll
+    for (int r = 0; r < W; r++) {
+      IO::load(wires.p[r] + (size_t)blk * T::block_bytes, ql & 3, w[r]);
+      sc[r] = h2f(ld_u16(wires.p[r] + g.off_s + (size_t)blk * 2)) * T::unpack_scale;
+      zc[r] = T::asym ? h2f(ld_u16(wires.p[r] + g.off_z + (size_t)blk * 2)) : 0.0f;
+    }
+    // acc = x0 + x1 + ... in rank order, as in stage 1's own kernel
+    float acc[1][8];
+#pragma unroll
+    for (int r = 0; r < W; r++) {
+      float cv[8];
+      code_values<C, 8>(w[r], cv);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        if constexpr (T::asym) {
+          const float x = __builtin_fmaf(cv[i], sc[r], zc[r]);
+          acc[0][i] = r == 0 ? x : acc[0][i] + x;
+        } else {
+          acc[0][i] = r == 0 ? cv[i] * sc[r] : __builtin_fmaf(cv[i], sc[r], acc[0][i]);
+        }
+      }
+    }
+    uint8_t* const rp[1] = {red};
+    const uint32_t rq[1] = {q};
+    quantize_core<C, kKeep, Full, 1>(acc, rp, rq, red, q, q_end, g);
+  }
+  __syncthreads();
+
+  // stage 2: dequantize the reduced quarter once, store it to every output
+  {
+    const uint32_t blk = ql >> 2;
+    uint32_t w[IO::nw];
+    IO::load(red + (size_t)blk * T::block_bytes, ql & 3, w);
+    const float sv = h2f(ld_u16(red + g.off_s + (size_t)blk * 2)) * T::unpack_scale;
+    const float zv = T::asym ? h2f(ld_u16(red + g.off_z + (size_t)blk * 2)) : 0.0f;
+    float cv[8], y[8];
+    code_values<C, 8>(w, cv);
+#pragma unroll
+    for (int i = 0; i < 8; i++) y[i] = T::asym ? __builtin_fmaf(cv[i], sv, zv) : cv[i] * sv;
+    const u32x4 out{st16x2<D>(y[0], y[1]), st16x2<D>(y[2], y[3]), st16x2<D>(y[4], y[5]),
+                    st16x2<D>(y[6], y[7])};
+    if (has) {
+#pragma unroll
+      for (int r = 0; r < W; r++) st_out<kStage2>(reinterpret_cast<u32x4*>(ys.p[r]) + q, out);
+    }
+  }
 }
 
 template <int C, int D, int W>
 __global__ __launch_bounds__(kThreads) void k_fused(InPtrs xs, OutPtrs wires, uint8_t* red,
                                                     OutPtrs ys, Geo g) {
-  const uint32_t T = blockIdx.x;
-  const uint32_t q0 = T * (kThreads * kPerLane) + threadIdx.x;   // this lane's quarters
-  const uint32_t blk = T * kThreads + threadIdx.x;               // this lane's block
-  const bool full = tile_full(T, g.n);                           // uniform
-  InPtrs win;
-#pragma unroll
-  for (int r = 0; r < W; r++) win.p[r] = wires.p[r];
-  // every rank's loads are issued before any is quantized: at the small sizes
-  // this kernel serves, the memory round trips are the time
-  if (full)
-    fused_stage0<C, D, W, true>(xs, wires, q0, g);
+  const uint32_t q = blockIdx.x * kThreads + threadIdx.x;
+  // uniform: every quarter of the workgroup holds 8 elements
+  if (8ull * ((uint64_t)blockIdx.x + 1ull) * kThreads <= (uint64_t)g.n)
+    fused_tile<C, D, W, true>(xs, wires, red, ys, q, g);
   else
-    fused_stage0<C, D, W, false>(xs, wires, q0, g);
-  __syncthreads();
-  if (full) {
-    S1In<C, W> in;
-    s1_load<C, W>(win, blk, g, in);
-    s1_reduce_store<C, W, true>(in, red, blk, g);
-  } else if (blk < g.nb) {
-    S1In<C, W> in;
-    s1_load<C, W>(win, blk, g, in);
-    s1_reduce_store<C, W, false>(in, red, blk, g);
-  }
-  __syncthreads();
-  const uint32_t nq = (g.n + 7) / 8;
-#pragma unroll
-  for (int r = 0; r < W; r++) {
-    if (full)
-      dequant_tile<C, D, true>(red, ys.p[r], q0, nq, g);
-    else
-      dequant_tile<C, D, false>(red, ys.p[r], q0, nq, g);
-  }
+    fused_tile<C, D, W, false>(xs, wires, red, ys, q, g);
 }
 
 // the FP codec in one launch: copy (converting under the cast option), sum,
-// copy back, over the 1024 chunks of 16 bytes of workgroup T
+// copy back; one 16-byte chunk per lane
 template <int D, int W>
 __global__ __launch_bounds__(kThreads) void k_fused_fp(InPtrs xs, OutPtrs wires, uint8_t* red,
                                                        OutPtrs ys, uint32_t nchunks) {
   constexpr int Dw = D == kBF16H ? kF16 : D;      // the wire's element type
   constexpr int Dx = D == kBF16H ? kBF16 : D;     // the buffers' element type
-  const uint32_t c0 = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
+  const uint32_t c = blockIdx.x * kThreads + threadIdx.x;
+  const bool has = c < nchunks;
+  if (has) {
 #pragma unroll
-  for (int r = 0; r < W; r++) {
-#pragma unroll
-    for (int j = 0; j < kPerLane; j++) {
-      const uint32_t c = c0 + j * kThreads;
-      if (c >= nchunks) break;
+    for (int r = 0; r < W; r++) {
       u32x4 q = reinterpret_cast<const u32x4*>(xs.p[r])[c];
       if constexpr (Dx != Dw) {
 #pragma unroll
@@ -602,10 +693,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_fp(InPtrs xs, OutPtrs wires,
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kPerLane; j++) {
-    const uint32_t c = c0 + j * kThreads;
-    if (c >= nchunks) break;
+  if (has) {
     u32x4 q[W];
 #pragma unroll
     for (int r = 0; r < W; r++) q[r] = reinterpret_cast<const u32x4*>(wires.p[r])[c];
@@ -623,20 +711,15 @@ __global__ __launch_bounds__(kThreads) void k_fused_fp(InPtrs xs, OutPtrs wires,
     reinterpret_cast<u32x4*>(red)[c] = u32x4{out[0], out[1], out[2], out[3]};
   }
   __syncthreads();
+  if (has) {
+    u32x4 q = reinterpret_cast<const u32x4*>(red)[c];
+    if constexpr (Dx != Dw) {
 #pragma unroll
-  for (int r = 0; r < W; r++) {
-#pragma unroll
-    for (int j = 0; j < kPerLane; j++) {
-      const uint32_t c = c0 + j * kThreads;
-      if (c >= nchunks) break;
-      u32x4 q = reinterpret_cast<const u32x4*>(red)[c];
-      if constexpr (Dx != Dw) {
-#pragma unroll
-        for (int k = 0; k < 4; k++)
-          q[k] = st16x2<Dx>(ld16<Dw>(q[k] & 0xffffu), ld16<Dw>(q[k] >> 16));
-      }
-      st_out<kStage2>(reinterpret_cast<u32x4*>(ys.p[r]) + c, q);
+      for (int k = 0; k < 4; k++)
+        q[k] = st16x2<Dx>(ld16<Dw>(q[k] & 0xffffu), ld16<Dw>(q[k] >> 16));
     }
+#pragma unroll
+    for (int r = 0; r < W; r++) st_out<kStage2>(reinterpret_cast<u32x4*>(ys.p[r]) + c, q);
   }
 }
 
@@ -724,11 +807,12 @@ void fused_launch(const InPtrs& xs, const OutPtrs& wires, uint8_t* red, const Ou
                   const Layout& L, hipStream_t st) {
   if constexpr (C == kFP) {
     const uint32_t nc = (uint32_t)(L.n / 8);
-    hipLaunchKernelGGL((k_fused_fp<D, W>), dim3(groups(nc, kThreads * kPerLane)),
-                       dim3(kThreads), 0, st, xs, wires, red, ys, nc);
+    hipLaunchKernelGGL((k_fused_fp<D, W>), dim3(groups(nc, kThreads)), dim3(kThreads), 0, st,
+                       xs, wires, red, ys, nc);
   } else {
-    hipLaunchKernelGGL((k_fused<C, D, W>), dim3(groups(L.nb, kThreads)), dim3(kThreads), 0,
-                       st, xs, wires, red, ys, geo(L));
+    // 64 blocks (256 quarters) per workgroup
+    hipLaunchKernelGGL((k_fused<C, D, W>), dim3(groups(L.nb, kThreads / 4)), dim3(kThreads),
+                       0, st, xs, wires, red, ys, geo(L));
   }
 }
 

@@ -174,7 +174,8 @@ FUSED_EDGE = 2 * 1024 * 1024          # elements: 4 MiB per rank, the single-lau
                                                            O.Q6A, O.Q4A)])
 def test_sim_launch_paths(qr, codec, n):
     """qr_allreduce_sim at the size where it switches from one launch to
-    three, W=2 fp16 and W=4 bf16: every element equals the staged calls',
-    sampled blocks equal the oracle's"""
+    three, W=2 fp16, W=4 bf16 and W=8 bf16: every element equals the staged
+    calls', sampled blocks equal the oracle's"""
     _check_full(qr, 2, codec, n=n, windows=6)
     _check_full(qr, 3, codec, n=n, windows=6)
+    _check_full(qr, 4, codec, n=n, windows=6)

@@ -334,6 +334,40 @@ def test_guard_bands(qr):
                 assert np.all(h[:G // 2] == 0x3C3C) and np.all(h[G // 2 + n:] == 0x3C3C)
 
 
+def test_sim_guard_bands(qr):
+    """qr_allreduce_sim (one launch for W <= 4, three for W = 8) writes
+    nothing outside its workspace planes and its outputs"""
+    G = 4096
+    for codec in CODECS:
+        for W in (2, 4, 8):
+            for n in (8, 40, 8192 + 24):
+                say("sim guard", codec, W, n)
+                xs_np = _inputs(5, W, n, O.FP16)
+                xs = [dev16(x) for x in xs_np]
+                need = qr.qr_sim_workspace_bytes(W, codec, n)
+                big_ws = torch.full((need + 2 * G,), 0xA5, dtype=torch.uint8, device="cuda")
+                ws = big_ws[G:G + need]
+                big_y = [torch.full((n + G,), 0x3C3C, dtype=torch.int16, device="cuda")
+                         for _ in range(W)]
+                ys = [b[G // 2:G // 2 + n] for b in big_y]
+                qr.qr_allreduce_sim(codec, xs, ys, ws, dtype=O.FP16)
+                torch.cuda.synchronize()
+                h = hostu8(big_ws)
+                assert np.all(h[:G] == 0xA5) and np.all(h[G + need:] == 0xA5), (codec, W, n)
+                wb = qr.qr_wire_bytes(codec, n)
+                stride = (wb + 255) // 256 * 256
+                inner = h[G:G + need].copy()
+                for r in range(W + 1):
+                    for a, e in plane_slices(codec, n).values():
+                        inner[r * stride + a:r * stride + e] = 0xA5
+                assert np.all(inner == 0xA5), ("workspace padding written", codec, W, n)
+                want = O.allreduce(codec, O.FP16, xs_np)
+                for r, b in enumerate(big_y):
+                    hy = host16(b)
+                    assert np.all(hy[:G // 2] == 0x3C3C) and np.all(hy[G // 2 + n:] == 0x3C3C)
+                    assert_within_ulp(hy[G // 2:G // 2 + n], want[r], O.FP16, "sim guard y")
+
+
 def test_rejected_call_writes_nothing(qr):
     n, W, codec = 4096, 2, O.Q4
     xs = [dev16(x) for x in _inputs(1, W, n, O.FP16)]
