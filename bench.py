@@ -118,15 +118,23 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
+SPIN_CYCLES = 400000      # ~0.2 ms of GPU clock: longer than the host needs to enqueue a call
+
+
 def time_each(fn, iters, stream):
     """Microseconds of each of `iters` calls of fn(), from a pair of HIP
-    events recorded on the launch stream around each call."""
+    events recorded on the launch stream around each call.  Before each call
+    the stream runs a short spin kernel, so that the events and the call's
+    launches are all enqueued while the GPU is busy: the time between the
+    events is then the device's own (launch processing included), not the
+    host's submission of a call that takes only a few microseconds."""
+    import torch
     ev = HipEvents(2 * iters)
     for i in range(iters):
+        torch.cuda._sleep(SPIN_CYCLES)
         ev.record(2 * i, stream)
         fn()
         ev.record(2 * i + 1, stream)
-    import torch
     torch.cuda.synchronize()
     us = [ev.ms(2 * i, 2 * i + 1) * 1e3 for i in range(iters)]
     ev.close()
