@@ -320,6 +320,24 @@ __device__ __forceinline__ void group_max_min(const float* p, bool any, float& m
   mn = any ? mn : __builtin_inff();
 }
 
+// One rank's term of the stage-1 sum, in rank order: acc = x_0 for the first
+// rank, acc = acc + x_r after it.  A symmetric/fp8 term cv*s is exact, so
+// acc + cv*s is one fused multiply-add; an asymmetric term cv*s + z is
+// rounded once (the product is exact) and then added.
+template <int C, int N>
+__device__ __forceinline__ void add_rank(float (&acc)[N], const float (&cv)[N], float s, float z,
+                                         bool first) {
+#pragma unroll
+  for (int i = 0; i < N; i++) {
+    if constexpr (CodecT<C>::asym) {
+      const float x = __builtin_fmaf(cv[i], s, z);
+      acc[i] = first ? x : acc[i] + x;
+    } else {
+      acc[i] = first ? cv[i] * s : __builtin_fmaf(cv[i], s, acc[i]);
+    }
+  }
+}
+
 // max and min of a whole block p[0..32): one chain each, so that every pair
 // of new values takes one v_max3/v_min3
 __device__ __forceinline__ void block_max_min(const float* p, float& mx, float& mn) {

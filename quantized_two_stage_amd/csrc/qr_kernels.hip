@@ -6,7 +6,10 @@
 //   k_sum_fp     stage 1 of the FP codec, and the one-stage allreduce: sum of
 //                the raw buffers, rounded once
 //   k_dequant    stage 2 / dequantize: codes -> binary16/bfloat16, W outputs
-//   k_copy       stages 0 and 2 of the FP codec (the wire is the raw data)
+//   k_copy       stages 0 and 2 of the FP codec (the wire is the raw data;
+//                converted under the bf16 -> fp16 cast option)
+//   k_fused      all three stages in one launch for small buffers, each
+//   k_fused_fp   workgroup taking its tile of blocks through all three
 //
 // The method is the 2-stage allreduce of "Integrate quick allreduce and
 // select the best allreduce implementation" (vLLM PR #18473, PR description
@@ -26,6 +29,9 @@
 //     once, which matters because this kernel is the one closest to the
 //     VALU limit (W=2, 4-bit codes: 1.7 bytes of HBM per element).
 //   - the FP kernels give each lane 16-byte chunks, four per lane.
+//   - k_fused gives each lane one quarter block of every rank (a workgroup
+//     holds 64 blocks) and quantizes four ranks at a time as the four slots
+//     of the quad quantizer.
 #include "qr_device.h"
 #include "qr_internal.h"
 
@@ -312,11 +318,10 @@ __global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires,
   }
 }
 
-// stages 0 and 2 of FP: dst.p[r] <- src.p[r], 16-byte chunks (Stage only
-// names the two uses apart in profiles)
 // stages 0 and 2 of FP: dst.p[r] <- src.p[r], 16-byte chunks, four per
-// lane; Din != Dout converts every element (the cast option: bfloat16 into a
-// binary16 wire at stage 0, binary16 back to bfloat16 at stage 2)
+// lane; Stage selects the store policy (and names the two uses apart in
+// profiles); Din != Dout converts every element (the cast option: bfloat16
+// into a binary16 wire at stage 0, binary16 back to bfloat16 at stage 2)
 template <int Stage, int Din, int Dout>
 __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
                                                    uint32_t nchunks) {
@@ -387,23 +392,13 @@ __device__ __forceinline__ void s1_reduce_store(const S1In<C, W>& in, uint8_t* r
   using T = CodecT<C>;
   const uint32_t e0 = blk * kBlock;
   const int L = Full || g.n - e0 >= (uint32_t)kBlock ? kBlock : (int)(g.n - e0);
-  // acc = x0 + x1 + ... in rank order.  A symmetric/fp8 term cv*s is exact,
-  // so acc + cv*s is one fused multiply-add; an asymmetric term cv*s + z is
-  // rounded once (the product is exact) and then added.
+  // acc = x0 + x1 + ... in rank order
   float acc[kBlock];
 #pragma unroll
   for (int r = 0; r < W; r++) {
     float cv[kBlock];
     code_values<C, kBlock>(in.cw[r], cv);
-#pragma unroll
-    for (int i = 0; i < kBlock; i++) {
-      if constexpr (T::asym) {
-        const float x = __builtin_fmaf(cv[i], in.sc[r], in.zc[r]);
-        acc[i] = r == 0 ? x : acc[i] + x;
-      } else {
-        acc[i] = r == 0 ? cv[i] * in.sc[r] : __builtin_fmaf(cv[i], in.sc[r], acc[i]);
-      }
-    }
+    add_rank<C, kBlock>(acc, cv, in.sc[r], in.zc[r], r == 0);
   }
   float mx, mn;
   if constexpr (Full) {
@@ -624,15 +619,7 @@ __device__ __forceinline__ void fused_tile(const InPtrs& xs, const OutPtrs& wire
     for (int r = 0; r < W; r++) {
       float cv[8];
       code_values<C, 8>(w[r], cv);
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        if constexpr (T::asym) {
-          const float x = __builtin_fmaf(cv[i], sc[r], zc[r]);
-          acc[0][i] = r == 0 ? x : acc[0][i] + x;
-        } else {
-          acc[0][i] = r == 0 ? cv[i] * sc[r] : __builtin_fmaf(cv[i], sc[r], acc[0][i]);
-        }
-      }
+      add_rank<C, 8>(acc[0], cv, sc[r], zc[r], r == 0);
     }
     uint8_t* const rp[1] = {red};
     const uint32_t rq[1] = {q};
