@@ -368,6 +368,45 @@ def test_sim_guard_bands(qr):
                     assert_within_ulp(hy[G // 2:G // 2 + n], want[r], O.FP16, "sim guard y")
 
 
+def test_graph_capture(qr):
+    """qr_allreduce_sim and qr_allreduce_oneshot captured in a graph (they
+    allocate nothing and issue no memset) and replayed three times, each with
+    new inputs copied into the captured buffers and eager work in between:
+    every replay equals the oracle"""
+    for W, n, codec in ((2, 4096, O.Q4), (4, 3 * 8192 + 24, O.Q6A), (8, 8192, O.FP8),
+                        (2, 3 * (1 << 20) + 8, O.Q8)):          # the last one takes three launches
+        say("graph", W, n, codec)
+        xs = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(W)]
+        ys = [torch.empty_like(xs[0]) for _ in range(W)]
+        y1 = [torch.empty_like(xs[0]) for _ in range(W)]
+        ws = qr.alloc_workspace(W, codec, n)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):                # warm-up outside the capture
+            qr.qr_allreduce_sim(codec, xs, ys, ws, dtype=O.FP16)
+            qr.qr_allreduce_oneshot(xs, y1, dtype=O.FP16)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            qr.qr_allreduce_sim(codec, xs, ys, ws, dtype=O.FP16)
+            qr.qr_allreduce_oneshot(xs, y1, dtype=O.FP16)
+        for rep in range(3):
+            xs_np = _inputs(1 + rep, W, n, O.FP16, salt=rep)
+            for x, h in zip(xs, xs_np):
+                x.copy_(dev16(h))
+            junk = torch.randn(1 << 16, device="cuda").sum()     # eager work between replays
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            want = O.allreduce(codec, O.FP16, xs_np)
+            want1 = O.oneshot(O.FP16, xs_np)
+            for r in range(W):
+                assert_within_ulp(host16(ys[r]), want[r], O.FP16, "graph replay %d y[%d]" % (rep, r))
+                assert np.array_equal(host16(y1[r]), want1[r]), ("graph replay oneshot", rep, r)
+            del junk
+
+
 def test_rejected_call_writes_nothing(qr):
     n, W, codec = 4096, 2, O.Q4
     xs = [dev16(x) for x in _inputs(1, W, n, O.FP16)]
