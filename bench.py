@@ -349,7 +349,7 @@ def main():
     value = total_payload / (ms_per_step * 1e-3) / 1e9
     dom = max(kernels, key=lambda k: k["us"])
     traffic = None
-    if os.path.exists(PROFILE_TRAFFIC):
+    if os.path.exists(PROFILE_TRAFFIC) and args.config == 2:    # the profiled workload
         tr = json.load(open(PROFILE_TRAFFIC))
         ent = tr.get("kernels", {}).get(dom["kernel"])
         if ent and tr.get("source_sha") == kernel_source_sha():
