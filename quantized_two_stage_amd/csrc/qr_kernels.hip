@@ -392,13 +392,30 @@ __device__ __forceinline__ void s1_reduce_store(const S1In<C, W>& in, uint8_t* r
   using T = CodecT<C>;
   const uint32_t e0 = blk * kBlock;
   const int L = Full || g.n - e0 >= (uint32_t)kBlock ? kBlock : (int)(g.n - e0);
-  // acc = x0 + x1 + ... in rank order
+  // acc = x0 + x1 + ... in rank order.  For W <= 4, 4- and 8-bit codes a
+  // word-aligned group of 8 at a time, so that each group's code values are
+  // used as soon as they are formed: fewer live registers, higher occupancy.
+  // (6-bit groups of 8 start mid-word, and at W = 8 the compiler does better
+  // with whole blocks.)
   float acc[kBlock];
 #pragma unroll
   for (int r = 0; r < W; r++) {
-    float cv[kBlock];
-    code_values<C, kBlock>(in.cw[r], cv);
-    add_rank<C, kBlock>(acc, cv, in.sc[r], in.zc[r], r == 0);
+    if constexpr (T::bits == 6 || W > 4) {
+      float cv[kBlock];
+      code_values<C, kBlock>(in.cw[r], cv);
+      add_rank<C, kBlock>(acc, cv, in.sc[r], in.zc[r], r == 0);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        float cv[8], a8[8];
+        code_values<C, 8>(in.cw[r] + k * (8 * T::bits / 32), cv);
+#pragma unroll
+        for (int i = 0; i < 8; i++) a8[i] = acc[8 * k + i];
+        add_rank<C, 8>(a8, cv, in.sc[r], in.zc[r], r == 0);
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc[8 * k + i] = a8[i];
+      }
+    }
   }
   float mx, mn;
   if constexpr (Full) {
