@@ -239,12 +239,35 @@ def cpu_baseline(codecs, dtype, xs_np, sample, threads):
             t.join()
     dt = time.perf_counter() - t0
     payload = len(codecs) * nb * 32 * 2
+    # the same scalar code on one thread, on a sixteenth of the sample
+    nb1 = max(1, nb // 16)
+    t1 = time.perf_counter()
+    for codec in codecs:
+        work(0, nb1, codec)
+    dt1 = time.perf_counter() - t1
     return {"value": payload / dt / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": "blocks 0..%d (%d elements = %.1f MB per rank) of each of the %d "
                       "ranks, all %d codecs, full pipeline; %.2f s wall" % (
                           nb, nb * 32, nb * 64 / 2 ** 20, len(xs_np), len(codecs), dt),
-            "seconds": dt}
+            "seconds": dt,
+            "single_thread": {"value": len(codecs) * nb1 * 64 / dt1 / 1e9, "unit": "GB/s",
+                              "sample": "blocks 0..%d, %.2f s" % (nb1, dt1)},
+            "host": host_info()}
+
+
+def host_info():
+    """core count and CPU model of the host the oracle ran on"""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_count": os.cpu_count(), "usable_cores": len(os.sched_getaffinity(0)),
+            "model": model}
 
 
 def main():
