@@ -20,7 +20,9 @@ Prints one JSON line: effective GB/s = per-rank payload bytes (2n per
 allreduce) / time, per step over all codecs; per-codec microseconds and
 GB/s; per-kernel durations; the roofline of the kernel that takes the most
 time; a cold-cache measurement of stage 1; and the CPU oracle timed on a
-bounded sample.
+bounded sample.  Unless --no-extra: the other workloads (W=8, the bf16
+workload with and without the cast option, and size sweeps from 4 KB to
+64 MB per rank buffer).
 """
 import argparse
 import hashlib
@@ -53,7 +55,7 @@ def parse():
                    help="elements per rank of the oracle's sample")
     p.add_argument("--no-cold", action="store_true")
     p.add_argument("--no-extra", action="store_true",
-                   help="skip the other workloads (size sweep, W=8)")
+                   help="skip the other workloads (size sweeps, W=8)")
     return p.parse_args()
 
 
@@ -214,6 +216,47 @@ def measure_workload(qr, I, torch, stream, config, n=None, codecs=None, iters=20
     del xs, ys, flush
     torch.cuda.empty_cache()
     return out
+
+
+SWEEP_SIZES = tuple(2 ** k for k in range(11, 26))      # elements: 4 KB .. 64 MB per rank
+
+
+def measure_sweep(qr, I, torch, stream, Ws=(2, 4, 8), sizes=SWEEP_SIZES):
+    """The simulated allreduce (qr_allreduce_sim) of every codec, and the
+    one-stage allreduce (key "1stage"), at every size from 4 KB to 64 MB per
+    rank buffer and W = 2, 4, 8.  fp16 buffers drawn as in the W=2 64 MB
+    workload; rank r's buffer is the same at every W, and a smaller size is
+    the leading part of the largest.  Per point: median and minimum us per
+    call, timed call by call as in measure_workload."""
+    Wmax, nmax = max(Ws), max(sizes)
+    xs_all = [torch.from_numpy(x.view(np.int16)).to("cuda")
+              for x in I.make(2, W=Wmax, n=nmax)]
+    ys_all = [torch.empty_like(x) for x in xs_all]
+    res = {}
+    for W in Ws:
+        per_size = {}
+        for n in sizes:
+            xs = [x[:n] for x in xs_all[:W]]
+            ys = [y[:n] for y in ys_all[:W]]
+            iters = 100 if 2 * n <= (1 << 20) else 20
+            r = {}
+            for c in I.ALL_CODECS:
+                ws = qr.alloc_workspace(W, c, n)
+                for _ in range(3):
+                    qr.qr_allreduce_sim(c, xs, ys, ws, dtype=I.FP16)
+                us = time_each(lambda: qr.qr_allreduce_sim(c, xs, ys, ws, dtype=I.FP16),
+                               iters, stream)
+                r[I.CODEC_NAMES[c]] = {"us": float(np.median(us)), "us_min": float(min(us))}
+                del ws
+            for _ in range(3):
+                qr.qr_allreduce_oneshot(xs, ys, dtype=I.FP16)
+            us = time_each(lambda: qr.qr_allreduce_oneshot(xs, ys, dtype=I.FP16), iters, stream)
+            r["1stage"] = {"us": float(np.median(us)), "us_min": float(min(us))}
+            per_size["%d" % (2 * n)] = r
+        res["W%d" % W] = per_size
+    del xs_all, ys_all
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(codecs, dtype, xs_np, sample, threads):
@@ -453,6 +496,13 @@ def main():
             sweep["%d" % (2 * size)] = r
         extra["config3_sweep"] = {"workload": c["desc"], "W": c["W"],
                                   "key": "bytes per rank buffer", "per_size": sweep}
+        print("bench: size sweep, W=2/4/8, every codec, fp16", file=sys.stderr, flush=True)
+        extra["sweep_fp16"] = {
+            "workload": "fp16 buffers drawn as the W=2 64 MB workload, 4 KB..64 MB per rank, "
+                        "W=2/4/8, every codec and the one-stage allreduce; us per call "
+                        "(median, min)",
+            "key": "W, then bytes per rank buffer",
+            "results": measure_sweep(qr, I, torch, stream)}
 
     cpu = None
     if not args.no_cpu_baseline:
