@@ -155,3 +155,26 @@ def test_allreduce_oneshot_rejects(kw, code):
     assert _call_oneshot(**kw) == code
     assert qr.LIB.qr_last_error().decode() != ""
     assert qr.LIB.qr_allreduce_oneshot(2, 0, None, _pp([FAKE, FAKE]), 2048, None) == -1
+
+
+def test_last_error_is_per_thread():
+    """each host thread reads back its own last error: two threads fail with
+    different errors, meet at a barrier, then each reads its message"""
+    import threading
+    qr = _lib()
+    bar = threading.Barrier(2)
+    got = {}
+
+    def run(name, kw):
+        code = _call_sim(**kw)
+        bar.wait()                       # both calls have failed before either reads
+        got[name] = (code, qr.LIB.qr_last_error().decode())
+
+    ts = [threading.Thread(target=run, args=("w", dict(W=3))),
+          threading.Thread(target=run, args=("n", dict(n=0)))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert got["w"][0] == -2 and "W = 3" in got["w"][1], got
+    assert got["n"][0] == -3 and "n must be > 0" in got["n"][1], got

@@ -480,3 +480,48 @@ def test_fp8_every_value(qr, dtype):
     codes = set(hostu8(wire)[:32 * nblk].tolist())
     assert len(codes) >= 250, len(codes)
     assert_within_ulp(host16(y), O.dequantize(O.FP8, dtype, rw, x.size), dtype, "fp8 y", ulps=0)
+
+
+def test_concurrent_host_threads(qr):
+    """four host threads, each with its own stream and buffers, issue
+    simulated allreduces at the same time (the library keeps no state
+    between calls): every result equals the oracle"""
+    import threading
+    jobs = [(2, O.Q4, 3 * 8192 + 40), (4, O.Q6A, 8192 + 8), (8, O.FP8, 4096),
+            (4, O.Q8, 3 * (1 << 20) + 8)]                      # the last takes three launches
+    data = []
+    for k, (W, codec, n) in enumerate(jobs):
+        xs_np = _inputs(2, W, n, O.FP16, salt=20 + k)
+        data.append((W, codec, n, xs_np, O.allreduce(codec, O.FP16, xs_np)))
+    say("threads", [(W, codec, n) for W, codec, n, _, _ in data])
+    bufs = []
+    for W, codec, n, xs_np, _ in data:
+        xs = [dev16(x) for x in xs_np]
+        bufs.append((xs, [torch.empty_like(xs[0]) for _ in range(W)],
+                     qr.alloc_workspace(W, codec, n), torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    bar = threading.Barrier(len(jobs))
+    errors = []
+
+    def run(k):
+        try:
+            W, codec = data[k][0], data[k][1]
+            xs, ys, ws, s = bufs[k]
+            bar.wait()
+            for _ in range(5):
+                qr.qr_allreduce_sim(codec, xs, ys, ws, dtype=O.FP16, stream=s)
+            s.synchronize()
+        except Exception as e:          # reported by the main thread
+            errors.append((k, repr(e)))
+
+    ts = [threading.Thread(target=run, args=(k,)) for k in range(len(jobs))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for k, (W, codec, n, _, want) in enumerate(data):
+        for r in range(W):
+            assert_within_ulp(host16(bufs[k][1][r]), want[r], O.FP16,
+                              "thread %d y[%d]" % (k, r))
