@@ -401,17 +401,14 @@ __device__ __forceinline__ void s1_reduce_store(const S1In<C, W>& in, uint8_t* r
 #pragma unroll
   for (int r = 0; r < W; r++) {
     if constexpr (T::bits == 6 || W > 4) {
-      float cv[kBlock];
-      code_values<C, kBlock>(in.cw[r], cv);
-      add_rank<C, kBlock>(acc, cv, in.sc[r], in.zc[r], r == 0);
+      add_codes<C, kBlock>(acc, in.cw[r], in.sc[r], in.zc[r], r == 0);
     } else {
 #pragma unroll
       for (int k = 0; k < 4; k++) {
-        float cv[8], a8[8];
-        code_values<C, 8>(in.cw[r] + k * (8 * T::bits / 32), cv);
+        float a8[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) a8[i] = acc[8 * k + i];
-        add_rank<C, 8>(a8, cv, in.sc[r], in.zc[r], r == 0);
+        add_codes<C, 8>(a8, in.cw[r] + k * (8 * T::bits / 32), in.sc[r], in.zc[r], r == 0);
 #pragma unroll
         for (int i = 0; i < 8; i++) acc[8 * k + i] = a8[i];
       }
@@ -633,11 +630,7 @@ __device__ __forceinline__ void fused_tile(const InPtrs& xs, const OutPtrs& wire
     // acc = x0 + x1 + ... in rank order, as in stage 1's own kernel
     float acc[1][8];
 #pragma unroll
-    for (int r = 0; r < W; r++) {
-      float cv[8];
-      code_values<C, 8>(w[r], cv);
-      add_rank<C, 8>(acc[0], cv, sc[r], zc[r], r == 0);
-    }
+    for (int r = 0; r < W; r++) add_codes<C, 8>(acc[0], w[r], sc[r], zc[r], r == 0);
     uint8_t* const rp[1] = {red};
     const uint32_t rq[1] = {q};
     quantize_core<C, kKeep, Full, 1>(acc, rp, rq, red, q, q_end, g);

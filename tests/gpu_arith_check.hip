@@ -14,6 +14,12 @@
 //   7. f2h (v_cvt_f16_f32) == nearest-even binary16 (subnormals, overflow to
 //      inf) for every non-NaN binary32, against an integer conversion written
 //      from the two formats' definitions
+//   8. fma_mix16<Hi> (v_fma_mix_f32 on a binary16 half) reads every non-NaN
+//      binary16 in either half exactly, whatever the other half holds
+//   9. fma_mix16<Hi>(f, S, z) == fmaf(f * 2^-24, S, z) for every field
+//      f < 1024 (the subnormals the asymmetric codes are read as), every
+//      positive finite binary16 scale s with S = s * 2^24 and S = s * 2^20,
+//      and a binary16 zero point z drawn per case
 // Prints one line per check and exits 0 only if every count is zero.
 // Grid-stride loops with explicit bounds; counters in one small array.
 #include <hip/hip_runtime.h>
@@ -24,7 +30,8 @@
 
 using namespace qr;
 
-enum { kDiv = 0, kRcp = 6, kRint = 7, kEnc = 8, kDec = 9, kBf = 10, kF2h = 11, kSlots = 12 };
+enum { kDiv = 0, kRcp = 6, kRint = 7, kEnc = 8, kDec = 9, kBf = 10, kF2h = 11, kMixCvt = 12,
+       kMixFma = 13, kSlots = 14 };
 
 __device__ void miss(uint32_t* c, int slot) { atomicAdd(&c[slot], 1u); }
 
@@ -103,6 +110,44 @@ __global__ void k_dec(uint32_t* c) {
   if (__builtin_bit_cast(uint32_t, e4m3_dec<3>((w & 0x00ffffffu) | (code << 24))) != want) miss(c, kDec);
 }
 
+__device__ uint32_t hash32(uint32_t x) {
+  x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
+  return x;
+}
+
+__global__ void k_mix_cvt(uint32_t* c) {
+  const uint32_t p = blockIdx.x * blockDim.x + threadIdx.x;     // 0..65535
+  if (p >= 65536u || (p & 0x7fffu) > 0x7c00u) return;             // NaN patterns
+  const uint32_t want = __builtin_bit_cast(uint32_t, h2f(p));
+  const uint32_t junk = hash32(p) & 0xffffu;
+  if (__builtin_bit_cast(uint32_t, fma_mix16<false>((junk << 16) | p, 1.0f, -0.0f)) != want)
+    miss(c, kMixCvt);
+  if (__builtin_bit_cast(uint32_t, fma_mix16<true>((p << 16) | junk, 1.0f, -0.0f)) != want)
+    miss(c, kMixCvt);
+}
+
+__global__ void k_mix_fma(uint32_t* c) {
+  const uint64_t n = 2ull * 0x7bffull * 1024ull;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint32_t f = (uint32_t)(i & 1023u);
+    const uint32_t sb = (uint32_t)((i >> 10) % 0x7bffull) + 1u;     // 0x0001 .. 0x7bff
+    const bool shifted = i >= n / 2;
+    const float S = h2f(sb) * (shifted ? 1048576.0f : 16777216.0f);
+    uint32_t zb = hash32((uint32_t)i) & 0xffffu;
+    if ((zb & 0x7fffu) >= 0x7c00u) zb &= 0x83ffu;                    // keep z finite
+    const float z = h2f(zb);
+    const float want = __builtin_fmaf((float)f * 5.9604644775390625e-8f, S, z);   // f * 2^-24
+    const uint32_t junk = hash32((uint32_t)i ^ 0x9e3779b9u) & 0xffffu;
+    if (__builtin_bit_cast(uint32_t, fma_mix16<false>((junk << 16) | f, S, z)) !=
+        __builtin_bit_cast(uint32_t, want))
+      miss(c, kMixFma);
+    if (__builtin_bit_cast(uint32_t, fma_mix16<true>((f << 16) | junk, S, z)) !=
+        __builtin_bit_cast(uint32_t, want))
+      miss(c, kMixFma);
+  }
+}
+
 __global__ void k_bf(uint32_t* c) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32); i += stride) {
@@ -171,6 +216,8 @@ int main() {
   k_dec<<<1, 256>>>(c);
   k_bf<<<8192, 256>>>(c);
   k_f2h<<<8192, 256>>>(c);
+  k_mix_cvt<<<256, 256>>>(c);
+  k_mix_fma<<<8192, 256>>>(c);
   CK(hipGetLastError());
   CK(hipDeviceSynchronize());
   uint32_t h[kSlots];
@@ -188,7 +235,10 @@ int main() {
   printf("e4m3_dec: %u mismatches over all non-NaN codes, 4 byte positions\n", h[kDec]);
   printf("f2bf: %u mismatches over all non-NaN binary32\n", h[kBf]);
   printf("f2h: %u mismatches over all non-NaN binary32\n", h[kF2h]);
-  total += h[kRcp] + h[kRint] + h[kEnc] + h[kDec] + h[kBf] + h[kF2h];
+  printf("fma_mix16 read: %u mismatches over all non-NaN binary16, both halves\n", h[kMixCvt]);
+  printf("fma_mix16 fma: %u mismatches over all fields < 1024 x positive finite binary16 scales"
+         " x (2^24, 2^20), both halves\n", h[kMixFma]);
+  total += h[kRcp] + h[kRint] + h[kEnc] + h[kDec] + h[kBf] + h[kF2h] + h[kMixCvt] + h[kMixFma];
   printf("%s\n", total == 0 ? "ALL OK" : "MISMATCHES");
   return total == 0 ? 0 : 1;
 }
