@@ -76,14 +76,15 @@ def _is_inf(bits, dtype):
     return (bits & 0x7FFF) == (0x7C00 if dtype == O.FP16 else 0x7F80)
 
 
-def assert_within_ulp(got, want, dtype, what, ulps=0):
+def assert_within_ulp(got, want, dtype, what, ulps=0, signed_zero=True):
     """outputs within `ulps` units in the last place of the buffer type
-    (ordered-integer distance; +0 and -0 equal; inf only equals inf of the
-    same sign); returns how many elements are not bit-identical.  The default
-    is 0: the kernels round exactly as the definition does (binary32, then
-    the buffer type), so any 1-ulp difference is a rounding-order bug (one
-    such, a binary32 result rounded straight to binary16 by a merged
-    instruction, differed by exactly 1 ulp on rare elements)."""
+    (ordered-integer distance; inf only equals inf of the same sign; with
+    signed_zero, a zero must also carry the expected sign); returns how many
+    elements are not bit-identical.  The default is 0 ulps: the kernels
+    round exactly as the definition does (binary32, then the buffer type), so
+    any 1-ulp difference is a rounding-order bug (one such, a binary32 result
+    rounded straight to binary16 by a merged instruction, differed by exactly
+    1 ulp on rare elements, and turned -0 into +0)."""
     got, want = np.asarray(got, np.uint16), np.asarray(want, np.uint16)
     assert got.shape == want.shape
     assert np.array_equal(_is_nan(got, dtype), _is_nan(want, dtype)), what
@@ -94,6 +95,10 @@ def assert_within_ulp(got, want, dtype, what, ulps=0):
     d = ulp_distance(got[fin], want[fin])
     worst = int(d.max()) if d.size else 0
     assert worst <= ulps, "%s: %d ulp (index %d)" % (what, worst, np.nonzero(fin)[0][np.argmax(d)])
+    if signed_zero:
+        zs = np.nonzero((((got | want) & 0x7FFF) == 0) & (got != want))[0]
+        assert zs.size == 0, "%s: %d zeros of the wrong sign (first at %d: got %04x want %04x)" % (
+            what, zs.size, zs[0], got[zs[0]], want[zs[0]])
     return int(np.count_nonzero((got != want) & ~(((got | want) & 0x7FFF) == 0)))
 
 

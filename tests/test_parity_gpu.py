@@ -1,6 +1,6 @@
 """Parity of the HIP path with the oracle, element by element, through the C
-ABI: every wire plane (codes, scales, zeros) and every output bit-exact (+0
-and -0 compare equal in outputs), for every codec x buffer
+ABI: every wire plane (codes, scales, zeros) and every output bit-exact
+(zeros included, with their sign), for every codec x buffer
 type x W in {2,4,8}, at sizes that span several 256-lane workgroups and end in
 a ragged partial block; plus the hand-worked fixtures, owner-restricted
 stage 1, edge cases, guard bands and the no-write-on-error rule."""
