@@ -443,6 +443,14 @@ def main():
         copy_gbps["%dMiB" % (size >> 20)] = 2 * size * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
         del src, dst
 
+    # the floor of a call's time as time_each measures it: one launch of a
+    # kernel that writes a single element
+    tiny = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        tiny.zero_()
+    launch_floor_us = float(np.median(time_each(lambda: tiny.zero_(), 100, stream)))
+    del tiny
+
     cold = None
     if not args.no_cold:
         # stage 1 with L2 and the 256 MB Infinity Cache flushed before each
@@ -531,6 +539,7 @@ def main():
         "stage1_cold": cold,
         "other_workloads": extra,
         "device_copy_gbps": copy_gbps,
+        "launch_floor_us": launch_floor_us,
         "kernel_source_sha": kernel_source_sha(),
     }
     print(json.dumps(out), flush=True)
