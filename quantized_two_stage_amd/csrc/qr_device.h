@@ -144,6 +144,27 @@ __device__ __forceinline__ uint32_t rint_bits(float c) {
   return __builtin_bit_cast(uint32_t, c + kRoundMagic);
 }
 
+// rint_bits(t)'s low byte written into byte Byte of w in the same
+// instruction (an SDWA destination select on the v_add_f32): byte 0 clears
+// the other bytes, bytes 1..3 keep them.  One instruction per 8- or 4-bit
+// code instead of an add and a funnel shift.
+template <int Byte>
+__device__ __forceinline__ void rint_byte(uint32_t& w, float t) {
+  const float m = kRoundMagic;
+  if constexpr (Byte == 0)
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD "
+        "src1_sel:DWORD" : "=v"(w) : "v"(t), "v"(m));
+  else if constexpr (Byte == 1)
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+        "src1_sel:DWORD" : "+v"(w) : "v"(t), "v"(m));
+  else if constexpr (Byte == 2)
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+        "src1_sel:DWORD" : "+v"(w) : "v"(t), "v"(m));
+  else
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+        "src1_sel:DWORD" : "+v"(w) : "v"(t), "v"(m));
+}
+
 // a / D, correctly rounded, for the integer codecs' divisors (D = 127, 31,
 // 7, 255, 63, 15): q0 = a*R with R = RN(1/D), then one residual step
 // q0 + RN(a - q0*D)*R with two fused multiply-adds.  For each of these D this
@@ -234,6 +255,30 @@ __device__ __forceinline__ void encode(float (&t)[N], bool sat,
     for (int k = 0; k < N / 4; k++)
       w[k] = e4m3_pack2(t[4 * k + 2], t[4 * k + 3],
                         e4m3_pack2(t[4 * k], t[4 * k + 1], 0u, false), true);
+  } else if constexpr (T::bits == 8) {
+#pragma unroll
+    for (int k = 0; k < N / 4; k++) {
+      rint_byte<0>(w[k], t[4 * k]);
+      rint_byte<1>(w[k], t[4 * k + 1]);
+      rint_byte<2>(w[k], t[4 * k + 2]);
+      rint_byte<3>(w[k], t[4 * k + 3]);
+    }
+  } else if constexpr (T::bits == 4) {
+    // even codes as the bytes of `ev`, odd codes as the bytes of `od`, then
+    // the low nibbles interleaved: code i at bits [4i, 4i+4)
+#pragma unroll
+    for (int k = 0; k < N / 8; k++) {
+      uint32_t ev, od;
+      rint_byte<0>(ev, t[8 * k]);
+      rint_byte<1>(ev, t[8 * k + 2]);
+      rint_byte<2>(ev, t[8 * k + 4]);
+      rint_byte<3>(ev, t[8 * k + 6]);
+      rint_byte<0>(od, t[8 * k + 1]);
+      rint_byte<1>(od, t[8 * k + 3]);
+      rint_byte<2>(od, t[8 * k + 5]);
+      rint_byte<3>(od, t[8 * k + 7]);
+      w[k] = (ev & 0x0f0f0f0fu) | ((od << 4) & 0xf0f0f0f0u);
+    }
   } else {
     uint32_t c[N];
 #pragma unroll

@@ -20,6 +20,9 @@
 //      f < 1024 (the subnormals the asymmetric codes are read as), every
 //      positive finite binary16 scale s with S = s * 2^24 and S = s * 2^20,
 //      and a binary16 zero point z drawn per case
+//  10. rint_byte<B> (an SDWA byte write of the rounding add) holds
+//      round-half-even(c) in byte B, keeps the other bytes (B > 0) or clears
+//      them (B = 0), for every |c| <= 256
 // Prints one line per check and exits 0 only if every count is zero.
 // Grid-stride loops with explicit bounds; counters in one small array.
 #include <hip/hip_runtime.h>
@@ -31,7 +34,7 @@
 using namespace qr;
 
 enum { kDiv = 0, kRcp = 6, kRint = 7, kEnc = 8, kDec = 9, kBf = 10, kF2h = 11, kMixCvt = 12,
-       kMixFma = 13, kSlots = 14 };
+       kMixFma = 13, kRByte = 14, kSlots = 15 };
 
 __device__ void miss(uint32_t* c, int slot) { atomicAdd(&c[slot], 1u); }
 
@@ -113,6 +116,26 @@ __global__ void k_dec(uint32_t* c) {
 __device__ uint32_t hash32(uint32_t x) {
   x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
   return x;
+}
+
+__global__ void k_rint_byte(uint32_t* c) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2ull * 0x43800001ull;
+       i += stride) {
+    const uint32_t u = (uint32_t)(i % 0x43800001ull) | (i >= 0x43800001ull ? 0x80000000u : 0u);
+    const float x = __builtin_bit_cast(float, u);         // |x| <= 256
+    const uint32_t want = (uint32_t)(int)__builtin_rintf(x) & 0xffu;
+    const uint32_t junk = hash32(u);
+    uint32_t w0 = junk, w1 = junk, w2 = junk, w3 = junk;
+    rint_byte<0>(w0, x);
+    rint_byte<1>(w1, x);
+    rint_byte<2>(w2, x);
+    rint_byte<3>(w3, x);
+    if (w0 != want) miss(c, kRByte);
+    if (w1 != ((junk & 0xffff00ffu) | (want << 8))) miss(c, kRByte);
+    if (w2 != ((junk & 0xff00ffffu) | (want << 16))) miss(c, kRByte);
+    if (w3 != ((junk & 0x00ffffffu) | (want << 24))) miss(c, kRByte);
+  }
 }
 
 __global__ void k_mix_cvt(uint32_t* c) {
@@ -218,6 +241,7 @@ int main() {
   k_f2h<<<8192, 256>>>(c);
   k_mix_cvt<<<256, 256>>>(c);
   k_mix_fma<<<8192, 256>>>(c);
+  k_rint_byte<<<8192, 256>>>(c);
   CK(hipGetLastError());
   CK(hipDeviceSynchronize());
   uint32_t h[kSlots];
@@ -238,7 +262,9 @@ int main() {
   printf("fma_mix16 read: %u mismatches over all non-NaN binary16, both halves\n", h[kMixCvt]);
   printf("fma_mix16 fma: %u mismatches over all fields < 1024 x positive finite binary16 scales"
          " x (2^24, 2^20), both halves\n", h[kMixFma]);
-  total += h[kRcp] + h[kRint] + h[kEnc] + h[kDec] + h[kBf] + h[kF2h] + h[kMixCvt] + h[kMixFma];
+  printf("rint_byte: %u mismatches over all |c| <= 256, 4 byte positions\n", h[kRByte]);
+  total += h[kRcp] + h[kRint] + h[kEnc] + h[kDec] + h[kBf] + h[kF2h] + h[kMixCvt] + h[kMixFma] +
+           h[kRByte];
   printf("%s\n", total == 0 ? "ALL OK" : "MISMATCHES");
   return total == 0 ? 0 : 1;
 }
