@@ -19,10 +19,11 @@
 // Every kernel streams HBM; nothing is a contraction, so no MFMA and no LDS.
 //   - k_quantize and k_dequant give each lane one quarter block (8 elements
 //     = 16 contiguous bytes of 16-bit data, consecutive lanes on consecutive
-//     quarters), four quarters per lane issued before any is used.  The four
-//     lanes of a block share its statistics through DPP quad permutes and
-//     each computes the block's scale itself (a few instructions, instead of
-//     a round trip through LDS).
+//     quarters), four quarters per lane issued before any is used.  A quad
+//     of lanes holds the quarters of four blocks: it reduces each block's
+//     max/min with DPP quad permutes, lane j derives block j's scale, and
+//     1/s reaches the other lanes by a DPP broadcast (a few instructions,
+//     instead of a round trip through LDS).
 //   - k_stage1 gives each lane a whole block: W code blocks of 16/24/32
 //     contiguous bytes and W scales in, one code block and scale out; the
 //     per-block work (max/min, two divisions, rounding of the scale) is done
