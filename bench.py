@@ -60,9 +60,16 @@ def parse():
 
 
 def kernel_source_sha():
+    """hash of the kernel sources with comments and blank lines removed: a
+    change to a comment leaves recorded counters valid, any change to the
+    code does not"""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        h.update(open(f, "rb").read())
+        src = re.sub(r"/\*.*?\*/", "", open(f).read(), flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        lines = [ln.rstrip() for ln in src.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 
