@@ -3,7 +3,10 @@
 Every function has the name of the C entry point it calls and takes torch
 tensors on the GPU; all work happens in libqr.so's HIP kernels, on the current
 torch stream unless `stream` is given.  There is no other implementation: if
-libqr.so is missing this module raises on import.
+libqr.so is missing this module raises on import.  Since the C ABI sees only
+pointers, each function first checks what only the tensors know (enough
+bytes behind every pointer, contiguous, in device memory, as many outputs as
+inputs) and raises ValueError before any call.
 """
 import ctypes
 import os
@@ -93,6 +96,32 @@ def _n16(t):
     return t.numel() * t.element_size() // 2
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _bufs(*groups):
+    """The C ABI sees only pointers: refuse, before any call, a tensor the
+    kernels would run past (too small or not contiguous) or one not in
+    device memory.  groups: (name, tensors, bytes each must hold)."""
+    for what, ts, need in groups:
+        for i, t in enumerate(ts):
+            if not t.is_contiguous():
+                raise ValueError("%s[%d] is not contiguous" % (what, i))
+            if _nbytes(t) < need:
+                raise ValueError("%s[%d] holds %d bytes, %d needed" % (what, i, _nbytes(t),
+                                                                       need))
+    for what, ts, _ in groups:
+        for i, t in enumerate(ts):
+            if not t.is_cuda:
+                raise ValueError("%s[%d] is not in GPU memory" % (what, i))
+
+
+def _same_count(xs, ys, a, b):
+    if len(xs) != len(ys):
+        raise ValueError("%d %s but %d %s" % (len(xs), a, len(ys), b))
+
+
 def qr_last_error():
     return LIB.qr_last_error().decode()
 
@@ -106,30 +135,41 @@ def qr_sim_workspace_bytes(W, codec, n):
 
 
 def qr_quantize(codec, x, wire, dtype=None, stream=None):
+    n = _n16(x)
+    _bufs(("x", [x], 2 * n), ("wire", [wire], qr_wire_bytes(codec, n)))
     _check(LIB.qr_quantize(codec, _dtype_of(x, dtype), _ptr(x), _n16(x), _ptr(wire),
                            _stream(stream)))
     return wire
 
 
 def qr_dequantize(codec, wire, y, dtype=None, stream=None):
+    n = _n16(y)
+    _bufs(("wire", [wire], qr_wire_bytes(codec, n)), ("y", [y], 2 * n))
     _check(LIB.qr_dequantize(codec, _dtype_of(y, dtype), _ptr(wire), _n16(y), _ptr(y),
                              _stream(stream)))
     return y
 
 
 def qr_quantize_ranks(codec, xs, wires, dtype=None, stream=None):
+    _same_count(xs, wires, "inputs", "wire images")
+    n = _n16(xs[0])
+    _bufs(("xs", xs, 2 * n), ("wires", wires, qr_wire_bytes(codec, n)))
     _check(LIB.qr_quantize_ranks(codec, _dtype_of(xs[0], dtype), len(xs), _ptrs(xs),
                                  _n16(xs[0]), _ptrs(wires), _stream(stream)))
     return wires
 
 
 def qr_reduce_stage1(codec, wires, n, reduced, dtype, owner=-1, stream=None):
+    _bufs(("wires", wires, qr_wire_bytes(codec, n)),
+          ("reduced", [reduced], qr_wire_bytes(codec, n)))
     _check(LIB.qr_reduce_stage1(codec, dtype, len(wires), _ptrs(wires), n, owner,
                                 _ptr(reduced), _stream(stream)))
     return reduced
 
 
 def qr_gather_stage2(codec, reduced, ys, dtype=None, stream=None):
+    n = _n16(ys[0])
+    _bufs(("reduced", [reduced], qr_wire_bytes(codec, n)), ("ys", ys, 2 * n))
     _check(LIB.qr_gather_stage2(codec, _dtype_of(ys[0], dtype), len(ys), _ptr(reduced),
                                 _n16(ys[0]), _ptrs(ys), _stream(stream)))
     return ys
@@ -137,8 +177,11 @@ def qr_gather_stage2(codec, reduced, ys, dtype=None, stream=None):
 
 def qr_allreduce_sim(codec, xs, ys, workspace, dtype=None, stream=None):
     """ys[r] = the simulated two-stage allreduce of xs (out-of-place)."""
+    _same_count(xs, ys, "inputs", "outputs")
     n = _n16(xs[0])
-    ws_bytes = workspace.numel() * workspace.element_size()
+    # the workspace's size is passed to the call, which checks it
+    _bufs(("xs", xs, 2 * n), ("ys", ys, 2 * n), ("workspace", [workspace], 0))
+    ws_bytes = _nbytes(workspace)
     _check(LIB.qr_allreduce_sim(len(xs), _dtype_of(xs[0], dtype), codec, _ptrs(xs),
                                 _ptrs(ys), n, _ptr(workspace), ws_bytes, _stream(stream)))
     return ys
@@ -146,6 +189,9 @@ def qr_allreduce_sim(codec, xs, ys, workspace, dtype=None, stream=None):
 
 def qr_allreduce_oneshot(xs, ys, dtype=None, stream=None):
     """ys[r] = the one-stage allreduce of xs: every rank sums all W buffers."""
+    _same_count(xs, ys, "inputs", "outputs")
+    n = _n16(xs[0])
+    _bufs(("xs", xs, 2 * n), ("ys", ys, 2 * n))
     _check(LIB.qr_allreduce_oneshot(len(xs), _dtype_of(xs[0], dtype), _ptrs(xs), _ptrs(ys),
                                     _n16(xs[0]), _stream(stream)))
     return ys

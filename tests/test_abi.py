@@ -178,3 +178,34 @@ def test_last_error_is_per_thread():
         t.join()
     assert got["w"][0] == -2 and "W = 3" in got["w"][1], got
     assert got["n"][0] == -3 and "n must be > 0" in got["n"][1], got
+
+
+def test_binding_refuses_tensors_the_kernels_would_overrun():
+    """the Python binding checks what only the tensors know, before any call:
+    as many outputs as inputs, enough bytes behind every pointer, contiguous
+    memory, device memory (CPU tensors here: each check fires before any
+    library call)"""
+    import torch
+    qr = _lib()
+    n, W, c = 4096, 2, qr.QR_Q4
+    xs = [torch.zeros(n, dtype=torch.float16) for _ in range(W)]
+    ys = [torch.zeros(n, dtype=torch.float16) for _ in range(W)]
+    ws = torch.zeros(qr.qr_sim_workspace_bytes(W, c, n), dtype=torch.uint8)
+    wire = torch.zeros(qr.qr_wire_bytes(c, n), dtype=torch.uint8)
+    cases = [
+        (lambda: qr.qr_allreduce_sim(c, xs, ys[:1], ws), "2 inputs but 1 outputs"),
+        (lambda: qr.qr_allreduce_sim(c, xs, [ys[0], ys[1][:n - 8]], ws), "ys[1] holds"),
+        (lambda: qr.qr_allreduce_sim(c, [xs[0], torch.zeros(2 * n, dtype=torch.float16)[::2]],
+                                     ys, ws), "xs[1] is not contiguous"),
+        (lambda: qr.qr_allreduce_sim(c, xs, ys, ws), "not in GPU memory"),
+        (lambda: qr.qr_allreduce_oneshot(xs, ys[:1]), "2 inputs but 1 outputs"),
+        (lambda: qr.qr_quantize(c, xs[0], wire[:-1]), "wire[0] holds"),
+        (lambda: qr.qr_dequantize(c, wire[:-2], ys[0]), "wire[0] holds"),
+        (lambda: qr.qr_quantize_ranks(c, xs, [wire]), "2 inputs but 1 wire images"),
+        (lambda: qr.qr_reduce_stage1(c, [wire, wire], n, wire[:100], 0), "reduced[0] holds"),
+        (lambda: qr.qr_gather_stage2(c, wire, [ys[0], ys[1][:10]]), "ys[1] holds"),
+    ]
+    for call, msg in cases:
+        with pytest.raises(ValueError) as e:
+            call()
+        assert msg in str(e.value), (msg, str(e.value))
