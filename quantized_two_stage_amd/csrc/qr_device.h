@@ -399,19 +399,78 @@ __device__ __forceinline__ float fma_mix16(uint32_t h2, float S, float z) {
   return r;
 }
 
+// q/16 for the signed 4-bit field in bits [0, 4) of byte Byte of w
+// (v_cvt_off_f32_i4 with an SDWA byte select): exact, and the other 28 bits
+// of w are ignored.  One instruction per symmetric 4-bit code: the even code
+// of a byte is its low nibble, the odd code the low nibble of the same byte
+// of w >> 4.
+template <int Byte>
+__device__ __forceinline__ float off_i4(uint32_t w) {
+  float r;
+  if constexpr (Byte == 0)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0"
+        : "=v"(r) : "v"(w));
+  else if constexpr (Byte == 1)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1"
+        : "=v"(r) : "v"(w));
+  else if constexpr (Byte == 2)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2"
+        : "=v"(r) : "v"(w));
+  else
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3"
+        : "=v"(r) : "v"(w));
+  return r;
+}
+
 // add_rank on the rank's code words directly.  Asymmetric 4-bit codes
 // (unsigned) are masked into the two 16-bit halves of a word, where a field
 // f < 1024 reads as the binary16 subnormal f * 2^-24; with the scale taken
 // as s * 2^24 (s * 2^20 for a code shifted up by 4 bits) one v_fma_mix_f32
 // gives the term u*s + z, exactly as the definition rounds it (the product
 // is exact).  This replaces a conversion and an FMA per code (stage 1 3-6%
-// faster; for 8-bit codes the same scheme measured no gain).  Other codecs
-// go through code_values and add_rank.
+// faster; for 8-bit codes the same scheme measured no gain).
+// Symmetric 4-bit codes (s here is the scale times 1/16, unpack_scale):
+//   - first rank: flipping bit 3 of every nibble gives u = q + 8 in
+//     [0, 16), read as a binary16 subnormal as above; fma(u, s*2^24, -8s) is
+//     u*s - 8s = q*s, exact, so one v_fma_mix_f32 per code forms the term.
+//   - later ranks: off_i4 gives q/16 in one instruction per code, and
+//     fma(q/16, 16s, acc) rounds acc + q*s once (the product is exact).
+// Other codecs go through code_values and add_rank.
 template <int C, int N>
 __device__ __forceinline__ void add_codes(float (&acc)[N], const uint32_t* w, float s, float z,
                                           bool first) {
   using T = CodecT<C>;
-  if constexpr (T::asym && T::bits == 4) {
+  if constexpr (!T::asym && T::bits == 4) {
+    // s = scale / 16 (exact); every constant below is a power-of-two multiple
+    if (first) {
+      const float S0 = s * 268435456.0f, S4 = s * 16777216.0f;     // scale * 2^24, * 2^20
+      const float Z = s * -128.0f;                                   // -8 * scale
+#pragma unroll
+      for (int k = 0; k < N / 8; k++) {
+        const uint32_t x = w[k] ^ 0x88888888u;
+        const uint32_t a = x & 0x000f000fu, b = x & 0x00f000f0u;
+        const uint32_t c = (x >> 8) & 0x000f000fu, d = (x >> 8) & 0x00f000f0u;
+        acc[8 * k + 0] = fma_mix16<false>(a, S0, Z);
+        acc[8 * k + 4] = fma_mix16<true>(a, S0, Z);
+        acc[8 * k + 1] = fma_mix16<false>(b, S4, Z);
+        acc[8 * k + 5] = fma_mix16<true>(b, S4, Z);
+        acc[8 * k + 2] = fma_mix16<false>(c, S0, Z);
+        acc[8 * k + 6] = fma_mix16<true>(c, S0, Z);
+        acc[8 * k + 3] = fma_mix16<false>(d, S4, Z);
+        acc[8 * k + 7] = fma_mix16<true>(d, S4, Z);
+      }
+    } else {
+      const float S = s * 256.0f;                                    // 16 * scale
+#pragma unroll
+      for (int k = 0; k < N / 8; k++) {
+        const uint32_t h = w[k] >> 4;
+        const float cv[8] = {off_i4<0>(w[k]), off_i4<0>(h), off_i4<1>(w[k]), off_i4<1>(h),
+                             off_i4<2>(w[k]), off_i4<2>(h), off_i4<3>(w[k]), off_i4<3>(h)};
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc[8 * k + i] = __builtin_fmaf(cv[i], S, acc[8 * k + i]);
+      }
+    }
+  } else if constexpr (T::asym && T::bits == 4) {
     const float S0 = s * 16777216.0f, S4 = s * 1048576.0f;        // s * 2^24, s * 2^20
 #pragma unroll
     for (int k = 0; k < N / 8; k++) {

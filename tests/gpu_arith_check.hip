@@ -23,6 +23,12 @@
 //  10. rint_byte<B> (an SDWA byte write of the rounding add) holds
 //      round-half-even(c) in byte B, keeps the other bytes (B > 0) or clears
 //      them (B = 0), for every |c| <= 256
+//  11. off_i4<B>(w) (v_cvt_off_f32_i4, SDWA byte B) == q/16 for the signed
+//      4-bit field in bits [8B, 8B+4) of w, for every 32-bit w and B = 0..3
+//  12. the symmetric 4-bit first-rank term: fma_mix16 on the offset field
+//      (bit 3 flipped) at bit 0 or bit 4 of either half, with the scale
+//      constants add_codes uses, == q * s exactly, for every code q and every
+//      positive finite binary16 scale s
 // Prints one line per check and exits 0 only if every count is zero.
 // Grid-stride loops with explicit bounds; counters in one small array.
 #include <hip/hip_runtime.h>
@@ -34,7 +40,7 @@
 using namespace qr;
 
 enum { kDiv = 0, kRcp = 6, kRint = 7, kEnc = 8, kDec = 9, kBf = 10, kF2h = 11, kMixCvt = 12,
-       kMixFma = 13, kRByte = 14, kSlots = 15 };
+       kMixFma = 13, kRByte = 14, kOffI4 = 15, kSymMix = 16, kSlots = 17 };
 
 __device__ void miss(uint32_t* c, int slot) { atomicAdd(&c[slot], 1u); }
 
@@ -171,6 +177,37 @@ __global__ void k_mix_fma(uint32_t* c) {
   }
 }
 
+__global__ void k_off_i4(uint32_t* c) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32); i += stride) {
+    const uint32_t w = (uint32_t)i;
+    const float got[4] = {off_i4<0>(w), off_i4<1>(w), off_i4<2>(w), off_i4<3>(w)};
+    for (int b = 0; b < 4; b++) {
+      const int q = (int)((w >> (8 * b)) & 0xfu) - (int)((w >> (8 * b)) & 0x8u) * 2;
+      if (__builtin_bit_cast(uint32_t, got[b]) != __builtin_bit_cast(uint32_t, (float)q / 16.0f))
+        miss(c, kOffI4);
+    }
+  }
+}
+
+__global__ void k_sym_mix(uint32_t* c) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t nib = i & 15u, sb = (i >> 4) + 1u;               // code bits, scale 0x0001..
+  if (sb >= 0x7c00u) return;
+  const int q = (int)nib - (int)(nib & 8u) * 2;
+  const float want = (float)q * h2f(sb);                          // exact
+  const float s = h2f(sb) * 0.0625f;                              // as add_codes receives it
+  const float S0 = s * 268435456.0f, S4 = s * 16777216.0f, Z = s * -128.0f;
+  const uint32_t f = nib ^ 8u, junk = hash32(i) & 0xffffu;
+  const float got[4] = {fma_mix16<false>((junk << 16) | f, S0, Z),
+                        fma_mix16<true>((f << 16) | junk, S0, Z),
+                        fma_mix16<false>(((junk & 0xff0fu) << 16) | (f << 4), S4, Z),
+                        fma_mix16<true>((f << 20) | (junk & 0xff0fu), S4, Z)};
+  for (int k = 0; k < 4; k++)
+    if (__builtin_bit_cast(uint32_t, got[k]) != __builtin_bit_cast(uint32_t, want))
+      miss(c, kSymMix);
+}
+
 __global__ void k_bf(uint32_t* c) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32); i += stride) {
@@ -242,6 +279,8 @@ int main() {
   k_mix_cvt<<<256, 256>>>(c);
   k_mix_fma<<<8192, 256>>>(c);
   k_rint_byte<<<8192, 256>>>(c);
+  k_off_i4<<<8192, 256>>>(c);
+  k_sym_mix<<<(16 * 0x7bff + 255) / 256, 256>>>(c);
   CK(hipGetLastError());
   CK(hipDeviceSynchronize());
   uint32_t h[kSlots];
@@ -263,8 +302,11 @@ int main() {
   printf("fma_mix16 fma: %u mismatches over all fields < 1024 x positive finite binary16 scales"
          " x (2^24, 2^20), both halves\n", h[kMixFma]);
   printf("rint_byte: %u mismatches over all |c| <= 256, 4 byte positions\n", h[kRByte]);
+  printf("off_i4: %u mismatches over all 32-bit words, 4 byte positions\n", h[kOffI4]);
+  printf("symmetric 4-bit fma_mix term: %u mismatches over all codes x positive finite binary16"
+         " scales, both halves, both nibble positions\n", h[kSymMix]);
   total += h[kRcp] + h[kRint] + h[kEnc] + h[kDec] + h[kBf] + h[kF2h] + h[kMixCvt] + h[kMixFma] +
-           h[kRByte];
+           h[kRByte] + h[kOffI4] + h[kSymMix];
   printf("%s\n", total == 0 ? "ALL OK" : "MISMATCHES");
   return total == 0 ? 0 : 1;
 }
