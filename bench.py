@@ -19,8 +19,10 @@ Two passes of the same K steps:
 Prints one JSON line: effective GB/s = per-rank payload bytes (2n per
 allreduce) / time, per step over all codecs; per-codec microseconds and
 GB/s; per-kernel durations; the roofline of the kernel that takes the most
-time; a cold-cache measurement of stage 1; and the CPU oracle timed on a
-bounded sample.  Unless --no-extra: the other workloads (W=8, the bf16
+time; a cold-cache measurement of stage 1; beside every kernel figure, a
+plain device copy that moves the same number of bytes (`copy_us`, and
+`vs_copy` = copy time / kernel time), the achievable reference at that size;
+and the CPU oracle timed on a bounded sample.  Unless --no-extra: the other workloads (W=8, the bf16
 workload with and without the cast option, and size sweeps from 4 KB to
 64 MB per rank buffer).
 """
@@ -127,6 +129,38 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
+_COPY_US = {}
+
+
+def copy_same_bytes_us(torch, stream, nbytes, flush=None):
+    """Median microseconds of a plain device-to-device copy (torch's copy_)
+    that moves `nbytes` in all: nbytes/2 read and nbytes/2 written.  The
+    achievable reference for a kernel whose algorithmic bytes are nbytes.
+    With `flush` (a 1 GiB tensor), L2 and the Infinity Cache are flushed
+    before each copy, as before a cold kernel."""
+    key = (nbytes, flush is not None)
+    if key not in _COPY_US:
+        half = (nbytes // 2 + 15) // 16 * 16
+        src = torch.ones(half, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        ev = HipEvents(2)
+        ts = []
+        for _ in range(7):
+            if flush is not None:
+                flush.sum()
+            ev.record(0, stream)
+            dst.copy_(src)
+            ev.record(1, stream)
+            torch.cuda.synchronize()
+            ts.append(ev.ms(0, 1) * 1e3)
+        ev.close()
+        del src, dst
+        _COPY_US[key] = float(np.median(ts))
+    return _COPY_US[key]
+
+
 SPIN_CYCLES = 400000      # ~0.2 ms of GPU clock: longer than the host needs to enqueue a call
 
 
@@ -191,8 +225,10 @@ def measure_workload(qr, I, torch, stream, config, n=None, codecs=None, iters=20
             for st, f in launches.items():
                 t = float(np.median(time_each(f, iters, stream)))
                 ab = algorithmic_bytes(st, W, n, wb)
+                cu = copy_same_bytes_us(torch, stream, ab)
                 r["kernels"][st] = {"us": t, "gbps": ab / (t * 1e-6) / 1e9,
-                                    "frac": ab / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+                                    "frac": ab / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                                    "copy_us": cu, "vs_copy": cu / t}
         if cold:
             ts = []
             launches["quantize"]()
@@ -201,8 +237,10 @@ def measure_workload(qr, I, torch, stream, config, n=None, codecs=None, iters=20
                 ts += time_each(launches["stage1"], 1, stream)
             t = float(np.median(ts))
             ab = algorithmic_bytes("stage1", W, n, wb)
+            cu = copy_same_bytes_us(torch, stream, ab, flush)
             r["stage1_cold"] = {"us": t, "gbps": ab / (t * 1e-6) / 1e9,
-                                "frac": ab / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+                                "frac": ab / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                                "copy_us": cu, "vs_copy": cu / t}
         if kernels or cold:
             del wires, red
         del ws
@@ -413,10 +451,12 @@ def main():
             "effective_gbps": 2 * n / (us * 1e-6) / 1e9}
         for k, st in enumerate(stages):
             ab = algorithmic_bytes(st, W, n, wb)
+            cu = copy_same_bytes_us(torch, stream, ab)
             kernels.append({"kernel": "%s/%s" % (st, I.CODEC_NAMES[c]),
                             "us": float(avg[k] * 1e3),
                             "algorithmic_bytes": ab,
-                            "gbps": ab / (avg[k] * 1e-3) / 1e9})
+                            "gbps": ab / (avg[k] * 1e-3) / 1e9,
+                            "copy_us": cu, "vs_copy": cu / float(avg[k] * 1e3)})
     evs.close()
     total_payload = len(codecs) * 2 * n
     value = total_payload / (ms_per_step * 1e-3) / 1e9
@@ -430,7 +470,8 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["gbps"],
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dom["gbps"] / HBM_PEAK_GBPS,
                 "traffic": traffic, "algorithmic_bytes_per_launch": dom["algorithmic_bytes"],
-                "avg_launch_us": dom["us"]}
+                "avg_launch_us": dom["us"], "copy_same_bytes_us": dom["copy_us"],
+                "vs_copy": dom["vs_copy"]}
 
     # plain device copies: 64 MB (fits the 256 MB Infinity Cache, like the
     # workload's own buffers) and 1 GiB (streams from HBM)
@@ -480,8 +521,10 @@ def main():
             ce.close()
             us = float(np.median(ts) * 1e3)
             ab = algorithmic_bytes("stage1", W, n, wb)
+            cu = copy_same_bytes_us(torch, stream, ab, flush)
             cold["stage1/" + I.CODEC_NAMES[c]] = {"us": us, "gbps": ab / (us * 1e-6) / 1e9,
-                                                  "frac": ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+                                                  "frac": ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                                                  "copy_us": cu, "vs_copy": cu / us}
         del flush
 
     extra = None
