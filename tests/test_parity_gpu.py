@@ -255,6 +255,85 @@ def test_owner_chunks(qr, W):
         assert_bytes_equal(hostu8(acc), hostu8(full), "union of owners")
 
 
+def _random_wire(codec, n, g):
+    """A wire image no quantizer wrote: uniformly random code bytes (every
+    code, -2^(b-1) included, and junk in the unused slots of a partial last
+    block), and binary16 scales and zeros drawn over every finite class:
+    +-0, subnormals, normals up to 65504, both signs.  fp8 NaN codes
+    (0x7f, 0xff) are moved to 0x7e/0xfe: non-finite values are outside the
+    contract.  The FP wire holds random finite binary16 values."""
+    wb = O.wire_bytes(codec, n)
+    w = g.integers(0, 256, wb, dtype=np.uint8)
+
+    def f16s(k):
+        mag = np.where(g.random(k) < 0.3, g.integers(0, 0x400, k),       # 0 and subnormals
+                       g.integers(0x400, 0x7C00, k))                       # normals
+        mag[g.random(k) < 0.1] = 0
+        return (mag | np.where(g.random(k) < 0.3, 0x8000, 0)).astype(np.uint16)
+
+    if codec == O.FP:
+        return f16s(n).view(np.uint8).copy()
+    if codec == O.FP8:
+        cb = O.block_code_bytes(codec) * ((n + 31) // 32)
+        c = w[:cb]
+        c[(c & 0x7F) == 0x7F] -= 1
+    nb = (n + 31) // 32
+    so = O.scale_offset(codec, n)
+    w[so:so + 2 * nb] = f16s(nb).view(np.uint8)
+    if codec & 8:
+        zo = O.zero_offset(codec, n)
+        w[zo:zo + 2 * nb] = f16s(nb).view(np.uint8)
+    return w
+
+
+def _dev_wire(codec, n, img, qr):
+    t = qr.alloc_wire(codec, n)
+    t.copy_(torch.from_numpy(img))
+    return t
+
+
+@pytest.mark.parametrize("W", (2, 4, 8))
+def test_stage1_any_wire(qr, W):
+    """stage 1 on wire images no quantizer wrote (every code value, scales of
+    every finite class and sign, junk in unused code slots): the reduced
+    image bit-exact against the oracle's stage 1 on the same bytes, for
+    every codec.  This reaches the decode of codes stage 0 never writes and
+    the saturated requantization of sums beyond the binary16 scale range."""
+    n = 3 * 8192 + 24
+    for codec in CODECS:
+        g = np.random.default_rng(7000 + 10 * W + codec)
+        imgs = [_random_wire(codec, n, g) for _ in range(W)]
+        say("stage1 any wire", I.CODEC_NAMES[codec], W, n)
+        wires = [_dev_wire(codec, n, im, qr) for im in imgs]
+        red = qr.alloc_wire(codec, n)
+        qr.qr_reduce_stage1(codec, wires, n, red, O.FP16)
+        torch.cuda.synchronize()
+        want = O.stage1(codec, O.FP16, imgs, n)
+        got = hostu8(red)
+        for name, (a, e) in plane_slices(codec, n).items():
+            assert_bytes_equal(got[a:e], want[a:e], "stage1 any wire %s W%d %s" % (
+                I.CODEC_NAMES[codec], W, name))
+
+
+@pytest.mark.parametrize("dtype", (O.FP16, O.BF16), ids=("fp16", "bf16"))
+def test_stage2_any_wire(qr, dtype):
+    """stage 2 (and qr_dequantize) on a wire image no quantizer wrote: every
+    output bit-exact against the oracle, for every codec."""
+    n = 3 * 8192 + 24
+    for codec in CODECS:
+        g = np.random.default_rng(8000 + codec + 100 * dtype)
+        img = _random_wire(codec, n, g)
+        say("stage2 any wire", I.CODEC_NAMES[codec], dtype, n)
+        red = _dev_wire(codec, n, img, qr)
+        ys = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(2)]
+        qr.qr_gather_stage2(codec, red, ys, dtype=dtype)
+        torch.cuda.synchronize()
+        want = O.stage2(codec, dtype, 2, img, n)
+        for r in range(2):
+            assert_within_ulp(host16(ys[r]), want[r], dtype, "stage2 any wire %s y[%d]" % (
+                I.CODEC_NAMES[codec], r))
+
+
 @pytest.mark.parametrize("dtype", (O.FP16, O.BF16), ids=("fp16", "bf16"))
 def test_edge_values(qr, dtype):
     """all-zero, constant, +-0 mixes, sums that overflow to inf, huge and
