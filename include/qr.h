@@ -104,7 +104,8 @@ typedef enum {
 enum {
   QR_OK = 0,
   QR_ERR_ARG = -1,         /* null pointer, overlapping buffers, bad owner  */
-  QR_ERR_UNSUPPORTED = -2, /* W not in {2,4,8}, unknown dtype or codec      */
+  QR_ERR_UNSUPPORTED = -2, /* W outside what the call takes, unknown dtype  */
+                           /* or codec                                      */
   QR_ERR_SIZE = -3,        /* n == 0, n % 8 != 0, or 2n > QR_MAX_BYTES      */
   QR_ERR_ALIGN = -4,       /* a device pointer not 16-byte aligned          */
   QR_ERR_WORKSPACE = -5,   /* workspace smaller than qr_sim_workspace_bytes */
@@ -130,7 +131,8 @@ int qr_quantize(qr_codec codec, qr_dtype dtype, const void* x, size_t n,
 int qr_dequantize(qr_codec codec, qr_dtype dtype, const void* wire, size_t n,
                   void* y, void* stream);
 
-/* Stage 0 for W ranks in one launch: wires[r] = quantize(xs[r]). */
+/* Stage 0 for W ranks in one launch: wires[r] = quantize(xs[r]); any W in
+ * 1..8 (each rank is quantized on its own). */
 int qr_quantize_ranks(qr_codec codec, qr_dtype dtype, int W,
                       const void* const* xs, size_t n, void* const* wires,
                       void* stream);
@@ -140,12 +142,13 @@ int qr_quantize_ranks(qr_codec codec, qr_dtype dtype, int W,
  * when owner == -1, dequantize the W wire images' blocks, sum in binary32 in
  * rank order and requantize into reduced_wire (a full-size wire image; only
  * the owned blocks' codes, scales and zeros are written).  For QR_FP the
- * wires are raw buffers and reduced_wire receives the rounded sums. */
+ * wires are raw buffers and reduced_wire receives the rounded sums.
+ * W in {2,4,8}. */
 int qr_reduce_stage1(qr_codec codec, qr_dtype dtype, int W,
                      const void* const* wires, size_t n, int owner,
                      void* reduced_wire, void* stream);
 
-/* Stage 2: every rank r dequantizes reduced_wire into ys[r]. */
+/* Stage 2: every rank r dequantizes reduced_wire into ys[r]; any W in 1..8. */
 int qr_gather_stage2(qr_codec codec, qr_dtype dtype, int W,
                      const void* reduced_wire, size_t n, void* const* ys,
                      void* stream);
@@ -158,7 +161,7 @@ int qr_gather_stage2(qr_codec codec, qr_dtype dtype, int W,
  * workgroup takes its tile of blocks through all three stages, reading the
  * wire and reduced images back from the workspace); above, three, the
  * kernels of qr_quantize_ranks, qr_reduce_stage1 and qr_gather_stage2.  Both
- * give the same outputs and workspace contents. */
+ * give the same outputs and workspace contents.  W in {2,4,8}. */
 int qr_allreduce_sim(int W, qr_dtype dtype, qr_codec codec,
                      const void* const* xs, void* const* ys, size_t n,
                      void* workspace, size_t ws_bytes, void* stream);
