@@ -263,6 +263,53 @@ def measure_workload(qr, I, torch, stream, config, n=None, codecs=None, iters=20
     return out
 
 
+def measure_stage1_sizes(qr, I, torch, stream, sizes=(1 << 25, 1 << 27, 1 << 29), reps=5):
+    """Stage 1 alone, cold, at W=2 and fp16 for growing rank buffers (64 MB,
+    256 MB and 1 GiB per rank), every codec of the W=2 workload: the kernel's
+    fraction of HBM peak once the transfer is large enough that launch ramp
+    and drain no longer dominate.  Rank buffers larger than the workload's
+    64 MB repeat its seeded buffers; stage 1's time does not depend on the
+    values.  Beside each figure, a cold device copy of the same bytes."""
+    cfg = I.CONFIGS[2]
+    W, codecs = cfg["W"], cfg["codecs"]
+    base = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in I.make(2)]
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    out = {}
+    for n in sizes:
+        xs = [b.repeat((n + b.numel() - 1) // b.numel())[:n].contiguous() for b in base]
+        per = {}
+        for c in codecs:
+            wb = qr.qr_wire_bytes(c, n)
+            wires = [qr.alloc_wire(c, n) for _ in range(W)]
+            red = qr.alloc_wire(c, n)
+            qr.qr_quantize_ranks(c, xs, wires, dtype=I.FP16)
+            qr.qr_reduce_stage1(c, wires, n, red, I.FP16)
+            ev = HipEvents(2)
+            ts = []
+            for _ in range(reps):
+                flush.sum()
+                ev.record(0, stream)
+                qr.qr_reduce_stage1(c, wires, n, red, I.FP16)
+                ev.record(1, stream)
+                torch.cuda.synchronize()
+                ts.append(ev.ms(0, 1) * 1e3)
+            ev.close()
+            t = float(np.median(ts))
+            ab = algorithmic_bytes("stage1", W, n, wb)
+            cu = copy_same_bytes_us(torch, stream, ab, flush)
+            per[I.CODEC_NAMES[c]] = {"us": t, "algorithmic_bytes": ab,
+                                     "gbps": ab / (t * 1e-6) / 1e9,
+                                     "frac": ab / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                                     "copy_us": cu, "vs_copy": cu / t}
+            del wires, red
+            torch.cuda.empty_cache()
+        out["%d" % (2 * n)] = per
+        del xs
+    del base, flush
+    torch.cuda.empty_cache()
+    return out
+
+
 SWEEP_SIZES = tuple(2 ** k for k in range(11, 26))      # elements: 4 KB .. 64 MB per rank
 
 
@@ -544,6 +591,13 @@ def main():
             "W": c["W"], "elements_per_rank": c["n"],
             "per_codec": measure_workload(qr, I, torch, stream, 4, cold=False,
                                           dtype=qr.QR_BF16_VIA_FP16)}
+        print("bench: stage 1 alone, cold, W=2, 64 MB .. 1 GiB per rank", file=sys.stderr,
+              flush=True)
+        extra["stage1_sizes"] = {
+            "workload": "stage 1 alone, cold caches, W=2 fp16, codecs of the W=2 64 MB workload; "
+                        "rank buffers beyond 64 MB repeat its seeded buffers",
+            "key": "bytes per rank buffer",
+            "results": measure_stage1_sizes(qr, I, torch, stream)}
         c = I.CONFIGS[3]
         print("bench: config 3 size sweep (%s)" % c["desc"], file=sys.stderr, flush=True)
         sweep = {}
