@@ -292,6 +292,95 @@ def check_block_codes(L, count=300):
             assert not codes[v.size:].any()
 
 
+def _finite_f16_bits():
+    """every finite binary16 bit pattern, +-0 and subnormals included"""
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    return b[(b & 0x7C00) != 0x7C00]
+
+
+def _unpack_codes(codes_plane, nb, b):
+    """code i of each block from bits [b*i, b*i+b) of the block's
+    little-endian bitstring, by numpy's unpackbits (independent of the
+    oracle's packing code)"""
+    blk = codes_plane[:nb * 4 * b].reshape(nb, 4 * b)
+    bits = np.unpackbits(blk, axis=1, bitorder="little").reshape(nb, 32, b)
+    return (bits.astype(np.int64) << np.arange(b)).sum(axis=2)
+
+
+def check_one_element_sweep(L):
+    """Exhaustive in one element: two fixed blocks of binary16 values, one
+    element of which takes every finite binary16 value (63488 blocks each),
+    quantized by the oracle in one call per codec.  Every block's scale (and
+    zero) must be the binary16 grid neighbour of the binary32 quotient found
+    by nextafter; every code the nearest (ties to even) to t = v * (1/s),
+    by numpy's rint (binary32) or torch's float8_e4m3fn cast, clamped; the
+    varying element's code also by brute force over every code."""
+    g = np.random.default_rng(31)
+    sweep = _finite_f16_bits()
+    f = np.float32
+    bases = [(g.standard_normal(32).astype(np.float16).view(np.uint16), 0),
+             ((g.standard_normal(32) * 1e-3).astype(np.float16).view(np.uint16), 17)]
+    table = e4m3_table()
+    for codec in QUANT:
+        b, qm = BITS[codec], QMAX[codec]
+        for base, j in bases:
+            x = np.tile(base, (sweep.size, 1))
+            x[:, j] = sweep
+            nb = sweep.size
+            wire = O.quantize(codec, O.FP16, x.ravel(), L=L)
+            # plane offsets from the layout's definition: each plane starts at
+            # the next 256-byte boundary after the previous one
+            so = (nb * 4 * b + 255) // 256 * 256
+            s = wire[so:so + 2 * nb].view(np.uint16)
+            codes = _unpack_codes(wire, nb, b)
+            v = x.view(np.float16).astype(np.float32)
+            mx, mn = v.max(axis=1), v.min(axis=1)
+            if codec in ASYM:
+                zo = (so + 2 * nb + 255) // 256 * 256
+                z = wire[zo:zo + 2 * nb].view(np.uint16)
+                mn0 = np.where(mn == 0, f(0.0), mn)
+                assert np.array_equal(z, grid_down16(mn0)), codec
+                zf = z.view(np.float16).astype(np.float32)
+                d = mx - zf
+                with np.errstate(divide="ignore", over="ignore"):
+                    want_s = np.where(d > 0, grid_up16(d / f(qm)), 0).astype(np.uint16)
+                assert np.array_equal(s, want_s), codec
+                inv = np.where(s > 0, f(1.0) / np.maximum(s.view(np.float16).astype(f), f(6e-8)),
+                               f(0.0)).astype(f)
+                t = (v - zf[:, None]) * inv[:, None]
+                want = np.clip(np.rint(t), 0, qm).astype(np.int64)
+                got = codes
+            else:
+                a = np.maximum(np.abs(mx), np.abs(mn))
+                arg = np.where(mx == mn, a, a / f(qm)).astype(f)
+                want_s = np.where(a > 0, grid_up16(arg), 0).astype(np.uint16)
+                assert np.array_equal(s, want_s), codec
+                inv = np.where(s > 0, f(1.0) / np.maximum(s.view(np.float16).astype(f), f(6e-8)),
+                               f(0.0)).astype(f)
+                t = v * inv[:, None]
+                if codec == O.FP8:
+                    import torch
+                    tc = torch.from_numpy(np.clip(t, -448, 448))
+                    want = tc.to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+                    want[s == 0] = 0
+                    got = codes
+                else:
+                    want = np.clip(np.rint(t), -qm, qm).astype(np.int64)
+                    got = np.where(codes >= 1 << (b - 1), codes - (1 << b), codes)
+            bad = np.nonzero(got != want)
+            assert bad[0].size == 0, (codec, j, bad[0][:3], bad[1][:3])
+            # the varying element by brute force over every code
+            tj = t[:, j].astype(np.float64)
+            if codec == O.FP8:
+                wj = e4m3_nearest(tj, table)
+                wj[s == 0] = 0
+            else:
+                lo = 0 if codec in ASYM else -qm
+                wj = np.concatenate([nearest_int_even(tj[k:k + 4096], lo, qm)
+                                     for k in range(0, tj.size, 4096)])
+            assert np.array_equal(got[:, j], wj), codec
+
+
 def check_error_bound(L, count=400):
     """|v - dequant| within half a step (plus binary32 slop) per element."""
     for codec in QUANT:
@@ -629,4 +718,4 @@ QUICK_CHECKS = [check_golden, check_layout, check_chunks, check_zero_blocks,
                 check_block_codes, check_error_bound, check_idempotent,
                 check_fp_closed_form, check_oneshot_closed_form, check_cast_option,
                 check_end_to_end_bound,
-                check_owner_split]
+                check_owner_split, check_one_element_sweep]
