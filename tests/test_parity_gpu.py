@@ -231,9 +231,10 @@ def test_golden_fixtures_gpu(qr):
 @pytest.mark.parametrize("W", (2, 4, 8))
 def test_owner_chunks(qr, W):
     """stage 1 for each owner writes exactly its chunk; together they give
-    the full reduced image."""
-    for codec in (O.FP, O.Q4, O.Q6A, O.FP8):
-        n = 32 * 37 + 16
+    the full reduced image.  847 blocks: at W=2 owner 1 starts at block 424,
+    off a 256-block workgroup tile, and spans full and partial tiles."""
+    for codec, n in [(c, m) for m in (32 * 37 + 16, 32 * 846 + 16)
+                     for c in (O.FP, O.Q4, O.Q6A, O.FP8, O.Q8)]:
         xs_np = _inputs(5, W, n, O.FP16, salt=1)
         say("owners", codec, W, n)
         xs = [dev16(x) for x in xs_np]
