@@ -36,7 +36,6 @@ enum Codec { kFP = 0, kQ8 = 1, kQ6 = 2, kQ4 = 3, kFP8 = 5,
 enum DType { kF16 = 0, kBF16 = 1, kBF16H = 2 };
 
 constexpr int kBlock = 32;   // elements per block
-constexpr int kQuarter = 8;  // elements per lane in the four-lane layout
 
 template <int C>
 struct CodecT {
