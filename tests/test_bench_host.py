@@ -1,0 +1,41 @@
+"""Host-side logic of bench.py, on the CPU: the one-GPU rule, the algorithmic
+byte counts the roofline divides by, and the kernel-source hash that decides
+whether the recorded HBM traffic counters still apply."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=60)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_algorithmic_bytes_of_the_64MB_workload():
+    # W=2, n = 32 Mi elements; a Q4 symmetric wire image is 16 B of codes and
+    # 2 B of scale per 32-element block: 1 Mi blocks -> 18,874,368 bytes
+    n, wb = 1 << 25, 18874368
+    assert bench.algorithmic_bytes("quantize", 2, n, wb) == 2 * (2 * n) + 2 * wb
+    assert bench.algorithmic_bytes("stage1", 2, n, wb) == 56623104      # 2 read + 1 written
+    assert bench.algorithmic_bytes("stage2", 2, n, wb) == 2 * wb + 2 * (2 * n)
+    # FP: the wire is the buffer itself
+    assert bench.algorithmic_bytes("stage1", 8, n, 2 * n) == 9 * 2 * n
+
+
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    body = "int f(int x) {\n  return x + 1;  // one\n}\n/* block\n comment */\n"
+    src.write_text(body)
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(src)])
+    h0 = bench.kernel_source_sha()
+    src.write_text(body.replace("// one", "// a different comment").replace(
+        "/* block\n comment */", "/* other */") + "\n\n")
+    assert bench.kernel_source_sha() == h0
+    src.write_text(body.replace("x + 1", "x + 2"))
+    assert bench.kernel_source_sha() != h0
