@@ -313,16 +313,43 @@ def measure_stage1_sizes(qr, I, torch, stream, sizes=(1 << 25, 1 << 27, 1 << 29)
 SWEEP_SIZES = tuple(2 ** k for k in range(11, 26))      # elements: 4 KB .. 64 MB per rank
 
 
-def measure_sweep(qr, I, torch, stream, Ws=(2, 4, 8), sizes=SWEEP_SIZES):
+def min_sizes(sweep):
+    """From a sweep (measure_sweep's result): for every W and codec, the
+    smallest rank buffer (bytes) from which the two-stage allreduce with that
+    codec is faster than the one-stage allreduce at that size and at every
+    larger size of the sweep; None where it is not faster at the largest size.
+    The analogue of the minimum sizes below which the pages' wrapper keeps the
+    one-stage kernel, for this single-GPU simulation (no link time)."""
+    out = {}
+    for Wk, per_size in sweep.items():
+        sizes = sorted(per_size, key=int)
+        row = {}
+        for c in per_size[sizes[0]]:
+            if c == "1stage":
+                continue
+            best = None
+            for sz in reversed(sizes):
+                if per_size[sz][c]["us"] < per_size[sz]["1stage"]["us"]:
+                    best = int(sz)
+                else:
+                    break
+            row[c] = best
+        out[Wk] = row
+    return out
+
+
+def measure_sweep(qr, I, torch, stream, Ws=(2, 4, 8), sizes=SWEEP_SIZES, dtype=0):
     """The simulated allreduce (qr_allreduce_sim) of every codec, and the
     one-stage allreduce (key "1stage"), at every size from 4 KB to 64 MB per
-    rank buffer and W = 2, 4, 8.  fp16 buffers drawn as in the W=2 64 MB
-    workload; rank r's buffer is the same at every W, and a smaller size is
-    the leading part of the largest.  Per point: median and minimum us per
-    call, timed call by call as in measure_workload."""
+    rank buffer and W = 2, 4, 8.  Buffers drawn as in the W=2 64 MB workload
+    and rounded to the buffer type (`dtype`: 0 fp16, 1 bf16, 2 bf16 buffers
+    through binary16, the cast option); rank r's buffer is the same at every
+    W, and a smaller size is the leading part of the largest.  Per point:
+    median and minimum us per call, timed call by call as in
+    measure_workload."""
     Wmax, nmax = max(Ws), max(sizes)
     xs_all = [torch.from_numpy(x.view(np.int16)).to("cuda")
-              for x in I.make(2, W=Wmax, n=nmax)]
+              for x in I.make(2, W=Wmax, n=nmax, dtype=I.BF16 if dtype else I.FP16)]
     ys_all = [torch.empty_like(x) for x in xs_all]
     res = {}
     for W in Ws:
@@ -335,14 +362,14 @@ def measure_sweep(qr, I, torch, stream, Ws=(2, 4, 8), sizes=SWEEP_SIZES):
             for c in I.ALL_CODECS:
                 ws = qr.alloc_workspace(W, c, n)
                 for _ in range(3):
-                    qr.qr_allreduce_sim(c, xs, ys, ws, dtype=I.FP16)
-                us = time_each(lambda: qr.qr_allreduce_sim(c, xs, ys, ws, dtype=I.FP16),
+                    qr.qr_allreduce_sim(c, xs, ys, ws, dtype=dtype)
+                us = time_each(lambda: qr.qr_allreduce_sim(c, xs, ys, ws, dtype=dtype),
                                iters, stream)
                 r[I.CODEC_NAMES[c]] = {"us": float(np.median(us)), "us_min": float(min(us))}
                 del ws
             for _ in range(3):
-                qr.qr_allreduce_oneshot(xs, ys, dtype=I.FP16)
-            us = time_each(lambda: qr.qr_allreduce_oneshot(xs, ys, dtype=I.FP16), iters, stream)
+                qr.qr_allreduce_oneshot(xs, ys, dtype=dtype)
+            us = time_each(lambda: qr.qr_allreduce_oneshot(xs, ys, dtype=dtype), iters, stream)
             r["1stage"] = {"us": float(np.median(us)), "us_min": float(min(us))}
             per_size["%d" % (2 * n)] = r
         res["W%d" % W] = per_size
@@ -615,6 +642,23 @@ def main():
                         "(median, min)",
             "key": "W, then bytes per rank buffer",
             "results": measure_sweep(qr, I, torch, stream)}
+        print("bench: size sweep, bf16 and bf16 through fp16", file=sys.stderr, flush=True)
+        for key, dt, what in (("sweep_bf16", I.BF16, "bf16 buffers"),
+                              ("sweep_bf16_via_fp16", 2, "bf16 buffers through binary16 "
+                                                         "(the cast option)")):
+            extra[key] = {
+                "workload": "%s drawn as the W=2 64 MB workload, 4 KB..64 MB per rank, "
+                            "W=2/4/8, every codec and the one-stage allreduce; us per call "
+                            "(median, min)" % what,
+                "key": "W, then bytes per rank buffer",
+                "results": measure_sweep(qr, I, torch, stream, dtype=dt)}
+        extra["min_sizes"] = {
+            "what": "per buffer type, W and codec: the smallest rank buffer (bytes) from which "
+                    "the two-stage allreduce is faster than the one-stage allreduce at every "
+                    "larger size of the sweep (null: not faster at 64 MB)",
+            "fp16": min_sizes(extra["sweep_fp16"]["results"]),
+            "bf16": min_sizes(extra["sweep_bf16"]["results"]),
+            "bf16_via_fp16": min_sizes(extra["sweep_bf16_via_fp16"]["results"])}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -39,3 +39,17 @@ def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
     assert bench.kernel_source_sha() == h0
     src.write_text(body.replace("x + 1", "x + 2"))
     assert bench.kernel_source_sha() != h0
+
+
+def test_min_sizes_takes_the_size_from_which_the_lead_holds():
+    def pt(one, q4, q8):
+        return {"1stage": {"us": one}, "q4": {"us": q4}, "q8": {"us": q8}}
+    sweep = {"W2": {"4096": pt(5.0, 5.1, 5.2),
+                    "8388608": pt(12.0, 11.0, 13.0),     # q4 ahead, q8 behind
+                    "16777216": pt(20.0, 21.0, 19.0),    # q4 behind again, q8 ahead
+                    "33554432": pt(40.0, 30.0, 35.0),
+                    "67108864": pt(80.0, 60.0, 70.0)}}
+    got = bench.min_sizes(sweep)["W2"]
+    assert got == {"q4": 33554432, "q8": 16777216}
+    sweep["W2"]["67108864"]["q8"]["us"] = 90.0          # behind at the largest size
+    assert bench.min_sizes(sweep)["W2"]["q8"] is None
