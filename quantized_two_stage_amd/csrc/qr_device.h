@@ -421,6 +421,15 @@ __device__ __forceinline__ float off_i4(uint32_t w) {
   return r;
 }
 
+// bit 5 (the sign bit) of every 6-bit field of a block's 192-bit string, as
+// it falls in word k
+constexpr uint32_t six_sign_mask(int k) {
+  uint32_t m = 0;
+  for (int b = 5; b < 192; b += 6)
+    if (b >= 32 * k && b < 32 * k + 32) m |= 1u << (b - 32 * k);
+  return m;
+}
+
 // add_rank on the rank's code words directly.  Asymmetric 4-bit codes
 // (unsigned) are masked into the two 16-bit halves of a word, where a field
 // f < 1024 reads as the binary16 subnormal f * 2^-24; with the scale taken
@@ -434,7 +443,13 @@ __device__ __forceinline__ float off_i4(uint32_t w) {
 //     u*s - 8s = q*s, exact, so one v_fma_mix_f32 per code forms the term.
 //   - later ranks: off_i4 gives q/16 in one instruction per code, and
 //     fma(q/16, 16s, acc) rounds acc + q*s once (the product is exact).
-// Other codecs go through code_values and add_rank.
+// 6-bit codes, read the same way: a field extracted zero-extended is the
+// binary16 subnormal f * 2^-24, and one v_fma_mix_f32 with s * 2^24 forms the
+// term.  Asymmetric: u*s + z for every rank (instead of a convert and an
+// FMA).  Symmetric, first rank: with bit 5 of every field flipped (one XOR
+// per word) the field is q + 32, and fma(q + 32, s, -32s) = q*s exactly.
+// Other codecs, and later ranks of symmetric 6-bit codes, go through
+// code_values and add_rank.
 template <int C, int N>
 __device__ __forceinline__ void add_codes(float (&acc)[N], const uint32_t* w, float s, float z,
                                           bool first) {
@@ -468,6 +483,29 @@ __device__ __forceinline__ void add_codes(float (&acc)[N], const uint32_t* w, fl
 #pragma unroll
         for (int i = 0; i < 8; i++) acc[8 * k + i] = __builtin_fmaf(cv[i], S, acc[8 * k + i]);
       }
+    }
+  } else if constexpr (T::bits == 6) {
+    if (T::asym || first) {
+      constexpr int nw = (N * 6 + 31) / 32;
+      uint32_t x[nw];
+#pragma unroll
+      for (int k = 0; k < nw; k++) x[k] = T::asym ? w[k] : w[k] ^ six_sign_mask(k);
+      const float S = s * 16777216.0f;                               // s * 2^24
+      const float Z = T::asym ? z : s * -32.0f;
+#pragma unroll
+      for (int i = 0; i < N; i++) {
+        const int off = 6 * i, k = off >> 5, sh = off & 31;
+        const uint32_t f = sh + 6 <= 32
+                               ? __builtin_amdgcn_ubfe(x[k], sh, 6)
+                               : __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(x[k + 1], x[k], sh),
+                                                       0, 6);
+        const float t = fma_mix16<false>(f, S, Z);
+        acc[i] = first ? t : acc[i] + t;
+      }
+    } else {
+      float cv[N];
+      code_values<C, N>(w, cv);
+      add_rank<C, N>(acc, cv, s, z, false);
     }
   } else if constexpr (T::asym && T::bits == 4) {
     const float S0 = s * 16777216.0f, S4 = s * 1048576.0f;        // s * 2^24, s * 2^20

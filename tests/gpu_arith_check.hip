@@ -29,6 +29,10 @@
 //      (bit 3 flipped) at bit 0 or bit 4 of either half, with the scale
 //      constants add_codes uses, == q * s exactly, for every code q and every
 //      positive finite binary16 scale s
+//  13. the same for the symmetric 6-bit first-rank term: the field with bit 5
+//      flipped, read as a binary16 subnormal, fma'd with s * 2^24 and -32s,
+//      == q * s exactly for every 6-bit code q and every positive finite
+//      binary16 scale s
 // Prints one line per check and exits 0 only if every count is zero.
 // Grid-stride loops with explicit bounds; counters in one small array.
 #include <hip/hip_runtime.h>
@@ -40,7 +44,7 @@
 using namespace qr;
 
 enum { kDiv = 0, kRcp = 6, kRint = 7, kEnc = 8, kDec = 9, kBf = 10, kF2h = 11, kMixCvt = 12,
-       kMixFma = 13, kRByte = 14, kOffI4 = 15, kSymMix = 16, kSlots = 17 };
+       kMixFma = 13, kRByte = 14, kOffI4 = 15, kSymMix = 16, kSym6Mix = 17, kSlots = 18 };
 
 __device__ void miss(uint32_t* c, int slot) { atomicAdd(&c[slot], 1u); }
 
@@ -208,6 +212,21 @@ __global__ void k_sym_mix(uint32_t* c) {
       miss(c, kSymMix);
 }
 
+__global__ void k_sym6_mix(uint32_t* c) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t field = i & 63u, sb = (i >> 6) + 1u;             // code bits, scale 0x0001..
+  if (sb >= 0x7c00u) return;
+  const int q = (int)field - (int)(field & 32u) * 2;
+  const float want = (float)q * h2f(sb);                          // exact
+  const float s = h2f(sb);
+  const uint32_t f = field ^ 32u, junk = hash32(i) & 0xffffu;
+  const float got[2] = {fma_mix16<false>((junk << 16) | f, s * 16777216.0f, s * -32.0f),
+                        fma_mix16<true>((f << 16) | junk, s * 16777216.0f, s * -32.0f)};
+  for (int k = 0; k < 2; k++)
+    if (__builtin_bit_cast(uint32_t, got[k]) != __builtin_bit_cast(uint32_t, want))
+      miss(c, kSym6Mix);
+}
+
 __global__ void k_bf(uint32_t* c) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32); i += stride) {
@@ -281,6 +300,7 @@ int main() {
   k_rint_byte<<<8192, 256>>>(c);
   k_off_i4<<<8192, 256>>>(c);
   k_sym_mix<<<(16 * 0x7bff + 255) / 256, 256>>>(c);
+  k_sym6_mix<<<(64 * 0x7bff + 255) / 256, 256>>>(c);
   CK(hipGetLastError());
   CK(hipDeviceSynchronize());
   uint32_t h[kSlots];
@@ -305,8 +325,10 @@ int main() {
   printf("off_i4: %u mismatches over all 32-bit words, 4 byte positions\n", h[kOffI4]);
   printf("symmetric 4-bit fma_mix term: %u mismatches over all codes x positive finite binary16"
          " scales, both halves, both nibble positions\n", h[kSymMix]);
+  printf("symmetric 6-bit fma_mix term: %u mismatches over all codes x positive finite binary16"
+         " scales, both halves\n", h[kSym6Mix]);
   total += h[kRcp] + h[kRint] + h[kEnc] + h[kDec] + h[kBf] + h[kF2h] + h[kMixCvt] + h[kMixFma] +
-           h[kRByte] + h[kOffI4] + h[kSymMix];
+           h[kRByte] + h[kOffI4] + h[kSymMix] + h[kSym6Mix];
   printf("%s\n", total == 0 ? "ALL OK" : "MISMATCHES");
   return total == 0 ? 0 : 1;
 }
