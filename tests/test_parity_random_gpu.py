@@ -91,3 +91,11 @@ def test_random_cases(qr, block):
         for r in range(W):
             assert_within_ulp(host16(ys2[r]), want_ys[r], O.BF16 if dtype else O.FP16,
                               "%s sim y[%d]" % (label, r))
+
+        # the one-stage allreduce on the same buffers
+        qr.qr_allreduce_oneshot(xs, ys2, dtype=dtype)
+        torch.cuda.synchronize()
+        want_one = O.oneshot(dtype, xs_np)
+        for r in range(W):
+            assert_within_ulp(host16(ys2[r]), want_one[r], O.BF16 if dtype else O.FP16,
+                              "%s one-stage y[%d]" % (label, r))
