@@ -168,8 +168,9 @@ int qr_allreduce_sim(int W, qr_dtype dtype, qr_codec codec,
 
 /* The one-stage (one-shot) allreduce without a wire format ("1stage", f16,
  * in PR #18473's description item 2 and its tp2 timing table; the review
- * thread of that PR proposes it for small buffers, the two-stage one for
- * large): every rank r reads all W buffers and writes
+ * thread of "Add quickreduce as alternative to custom allreduce", vLLM PR
+ * #16804, proposes one shot for small buffers and two shot for large ones):
+ * every rank r reads all W buffers and writes
  *     ys[r][i] = round_to_dtype(((x_0[i] + x_1[i]) + ...) + x_{W-1}[i]),
  * the sum taken in binary32 in rank order and rounded once (round to nearest
  * even; overflow -> inf) -- the same values as qr_allreduce_sim with QR_FP.

@@ -15,9 +15,10 @@
  *     QuickReduceRegime (FP=0, INT8=1, INT6=2, INT4=3, NONE=4) and
  *     QuickAllReduce.quick_all_reduce (out-of-place; input never modified).
  *   - PR #18473's description item 2 and its tp2 timing table name a second,
- *     one-stage ("1stage", f16 only) allreduce; the review thread of the same
- *     PR describes it as the one-shot kind (every rank reads every rank's
- *     buffer and reduces locally), to be used for small buffers.
+ *     one-stage ("1stage", f16 only) allreduce.  The review thread of "Add
+ *     quickreduce as alternative to custom allreduce" (vLLM PR #16804)
+ *     proposes the one-shot kind (every rank reads every rank's buffer and
+ *     reduces locally) for small buffers and two shots for larger ones.
  *
  * The pages name the formats only.  The readings taken where they are silent
  * (all stated again next to the code that implements them):

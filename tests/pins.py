@@ -602,6 +602,98 @@ def check_end_to_end_bound(L):
             assert np.all(np.abs(y - exact) <= bound), (W, codec)
 
 
+def _decode_wire_numpy(codec, n, wire):
+    """Every element of a quantized wire image as binary32, decoded with
+    numpy alone: code fields by np.unpackbits, the scale (and zero) planes at
+    their 256-byte boundaries, symmetric codes sign-extended, fp8 codes
+    through torch's float8_e4m3fn table.  The product code * scale is exact in
+    binary32 (at most 8 + 11 significant bits); an asymmetric value adds the
+    zero with one binary32 rounding (numpy float32 addition)."""
+    nb = (n + 31) // 32
+    b = BITS[codec]
+    f = np.uint16
+    codes = _unpack_codes(wire, nb, b)
+    so = (nb * 4 * b + 255) // 256 * 256
+    s = wire[so:so + 2 * nb].view(f).view(np.float16).astype(np.float64)[:, None]
+    if codec == O.FP8:
+        vals = (e4m3_table()[codes] * s).astype(np.float32)
+    elif codec in SYM:
+        q = np.where(codes >= 1 << (b - 1), codes - (1 << b), codes)
+        vals = (q * s).astype(np.float32)
+    else:
+        zo = (so + 2 * nb + 255) // 256 * 256
+        z = wire[zo:zo + 2 * nb].view(f).view(np.float16).astype(np.float32)[:, None]
+        vals = (codes * s).astype(np.float32) + z
+    return vals.reshape(-1)[:n]
+
+
+def _stage1_cases(seed):
+    """Rank buffers for the stage-1 composition pin: W in (2, 3, 4, 8), both
+    buffer types, a ragged tail.  Block kinds, drawn per block:
+      - cancellation: one rank holds small values (2^-9 scale), two others
+        hold +B and -B with B near 2^14, the rest zero; in binary32 the small
+        terms are absorbed or not depending on the order of the additions;
+      - mixed magnitudes: every rank N(0,1) times its own 2^U(-6, 6), so the
+        binary32 sums carry more significant bits than the buffer type;
+      - plain N(0,1)."""
+    g = np.random.default_rng(seed)
+    for W in (2, 3, 4, 8):
+        for dtype in (O.FP16, O.BF16):
+            nb = 48
+            n = 32 * nb - 8 * int(g.integers(0, 4))
+            xs64 = [np.zeros(n) for _ in range(W)]
+            for k in range(nb):
+                lo, hi = 32 * k, min(n, 32 * k + 32)
+                L = hi - lo
+                kind = k % 3
+                if kind == 0 and W >= 3:
+                    a, b, c = g.choice(W, 3, replace=False)
+                    big = g.uniform(0.5, 1.0, L) * 2.0 ** 14
+                    xs64[a][lo:hi] = g.standard_normal(L) * 2.0 ** -9
+                    xs64[b][lo:hi] = big
+                    xs64[c][lo:hi] = -big
+                elif kind == 1:
+                    for r in range(W):
+                        xs64[r][lo:hi] = g.standard_normal(L) * 2.0 ** g.uniform(-6, 6)
+                else:
+                    for r in range(W):
+                        xs64[r][lo:hi] = g.standard_normal(L)
+            if dtype == O.FP16:
+                xs = [x.astype(np.float16).view(np.uint16) for x in xs64]
+            else:
+                xs = [torch_f32_to_bf16(x.astype(np.float32)) for x in xs64]
+            yield W, dtype, n, xs
+
+
+def check_stage1_composition(L):
+    """Stage 1 of every quantized codec is the composition of three pinned
+    parts: the W wire images (the oracle's quantizer, pinned by the checks
+    above) are decoded with numpy, summed in numpy binary32 in rank order
+    0..W-1, and every block of the reduced image must equal the oracle's block
+    quantizer applied to those binary32 sums (codes, scale and zero).  The
+    cancellation blocks make the order and the precision of the sum visible,
+    the mixed-magnitude blocks the requantization of sums that the buffer type
+    cannot hold."""
+    for W, dtype, n, xs in _stage1_cases(12):
+        for codec in QUANT:
+            wires = [O.quantize(codec, dtype, x, L=L) for x in xs]
+            vals = [_decode_wire_numpy(codec, n, w) for w in wires]
+            acc = vals[0].copy()
+            for v in vals[1:]:
+                acc = (acc + v).astype(np.float32)
+            red = O.stage1(codec, dtype, wires, n, L=L)
+            nb = (n + 31) // 32
+            b = BITS[codec]
+            got_codes = _unpack_codes(red, nb, b)
+            _, got_s, got_z = _planes(codec, n, red, L)
+            for k in range(nb):
+                codes, s, z = O.quantize_block(codec, acc[32 * k:min(n, 32 * k + 32)], L)
+                assert np.array_equal(got_codes[k], codes.astype(np.int64)), (W, dtype, codec, k)
+                assert got_s[k] == s, (W, dtype, codec, k, got_s[k], s)
+                if codec in ASYM:
+                    assert got_z[k] == z, (W, dtype, codec, k)
+
+
 def check_chunks(L):
     for W in (1, 2, 3, 4, 8):
         for n in (8, 16, 40, 256, 2048, 2056, 32 * 7 + 8, 32 * 1000):
@@ -717,5 +809,5 @@ QUICK_CHECKS = [check_golden, check_layout, check_chunks, check_zero_blocks,
                 check_f2h, check_ru_rd, check_e4m3, check_bf16,
                 check_block_codes, check_error_bound, check_idempotent,
                 check_fp_closed_form, check_oneshot_closed_form, check_cast_option,
-                check_end_to_end_bound,
+                check_end_to_end_bound, check_stage1_composition,
                 check_owner_split, check_one_element_sweep]

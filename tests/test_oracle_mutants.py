@@ -83,6 +83,26 @@ MUTANTS = {
     "cast_fp_wire_kept_bf16": [
         ("static int wire_type(int dtype) { return dtype == T_BF16_VIA_FP16 ? T_FP16 : dtype; }",
          "static int wire_type(int dtype) { return dtype == T_BF16_VIA_FP16 ? T_BF16 : dtype; }")],
+    # stage 1 of the quantized codecs alone (the FP codec's sum kept as it is)
+    "quantized_sum_in_reverse_rank_order": [
+        ("for (int r = 0; r < W; r++) {\n      if (c == C_FP) {",
+         "for (int rr = 0; rr < W; rr++) {\n      int r = (c == C_FP) ? rr : W - 1 - rr;\n"
+         "      if (c == C_FP) {"),
+        ("acc[i] = (r == 0) ? v[i] : acc[i] + v[i];",
+         "acc[i] = (rr == 0) ? v[i] : acc[i] + v[i];")],
+    "quantized_sum_in_binary64": [
+        ("for (int i = 0; i < L; i++) acc[i] = (r == 0) ? v[i] : acc[i] + v[i];\n    }",
+         "for (int i = 0; i < L; i++) {\n"
+         "        if (c != C_FP) acc64[i] = (r == 0) ? (double)v[i] : acc64[i] + (double)v[i];\n"
+         "        acc[i] = (r == 0) ? v[i] : acc[i] + v[i];\n"
+         "      }\n    }\n"
+         "    if (c != C_FP) for (int i = 0; i < L; i++) acc[i] = (float)acc64[i];"),
+        ("float acc[BLK], v[BLK];\n    for (int r = 0; r < W; r++) {",
+         "float acc[BLK], v[BLK];\n    double acc64[BLK];\n    for (int r = 0; r < W; r++) {")],
+    "requantize_from_sums_rounded_to_buffer_type": [
+        ("      wire_put_block(c, reduced, n, k, acc, L);",
+         "      for (int i = 0; i < L; i++) acc[i] = ld(dtype, st(dtype, acc[i]));\n"
+         "      wire_put_block(c, reduced, n, k, acc, L);")],
     "zero_plane_overlaps_scales": [
         ("return align256(ref_scale_offset(c, n) + 2 * nblocks(n));",
          "return align256(ref_scale_offset(c, n));")],
