@@ -48,8 +48,10 @@
  *
  * Conventions for every entry point:
  *   - Buffers are device memory owned by the caller; the library allocates
- *     nothing and keeps no state between calls.  Pointer arrays (xs, ys,
- *     wires) are host arrays of W device pointers, read during the call only.
+ *     nothing and keeps no state between calls (qr_allreduce_sim_noalloc
+ *     alone uses a buffer of the library's own, described there).  Pointer
+ *     arrays (xs, ys, wires) are host arrays of W device pointers, read during
+ *     the call only.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *     their kernels and return without synchronising; results are ready when
  *     the stream reaches that point.
@@ -178,6 +180,29 @@ int qr_allreduce_sim(int W, qr_dtype dtype, qr_codec codec,
  * for every entry point (no workspace). */
 int qr_allreduce_oneshot(int W, qr_dtype dtype, const void* const* xs,
                          void* const* ys, size_t n, void* stream);
+
+/* Largest workspace qr_allreduce_sim_noalloc takes from the library's own
+ * device buffer (64 MiB per GPU): enough for every W and codec up to 4 MiB
+ * per rank buffer, the sizes that run as one launch. */
+#define QR_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* qr_allreduce_sim without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The W wire images and the reduced image
+ * go to a device buffer of QR_SCRATCH_BYTES that the library holds in every
+ * GPU it runs on, from the first call on that GPU until the process ends; the
+ * call itself allocates nothing and frees nothing.  The GPU is the current
+ * device (hipGetDevice), which `stream` must belong to.  Outputs, launches
+ * and argument rules are those of qr_allreduce_sim; additionally the call
+ * fails with QR_ERR_WORKSPACE, writing nothing, when
+ * qr_sim_workspace_bytes(W, codec, n) > QR_SCRATCH_BYTES.  Every call on one
+ * GPU uses the same buffer: calls on that GPU must not overlap in time (on
+ * two streams, or from two threads, without ordering between them), or they
+ * race on it.  Nothing in the buffer needs to start at zero; it keeps the
+ * last call's wire images. */
+int qr_allreduce_sim_noalloc(int W, qr_dtype dtype, qr_codec codec,
+                             const void* const* xs, void* const* ys, size_t n,
+                             void* stream);
 
 /* Message for the last error returned on this thread ("" if none). */
 const char* qr_last_error(void);

@@ -2,8 +2,10 @@
 //
 // Everything here runs on the host: argument checks (done before anything is
 // launched, so a rejected call writes nothing), the wire layout, and the
-// kernel launches of qr_kernels.hip.  The library keeps no state; the only
-// per-thread datum is the text of the last error.
+// kernel launches of qr_kernels.hip.  The library keeps no state between
+// calls other than the text of the last error (per thread) and, once
+// qr_allreduce_sim_noalloc has run on a GPU, the address of that GPU's
+// workspace buffer.
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -131,6 +133,54 @@ int check_disjoint(const void* const* ins, int nin, size_t in_bytes,
   return QR_OK;
 }
 
+// arguments of the simulated allreduce other than its workspace
+int check_sim(int W, int dtype, int codec, const void* const* xs, void* const* ys, size_t n) {
+  QR_TRY(check_kind(codec, dtype, n));
+  if (!w_sim(W)) return fail(QR_ERR_UNSUPPORTED, "W = %d not in {2,4,8}", W);
+  if (xs == nullptr || ys == nullptr) return fail(QR_ERR_ARG, "NULL pointer array");
+  for (int r = 0; r < W; r++) {
+    QR_TRY(check_ptr(xs[r], "xs", r));
+    QR_TRY(check_ptr(ys[r], "ys", r));
+  }
+  return check_disjoint(xs, W, 2 * n, (const void* const*)ys, W, 2 * n);
+}
+
+int check_workspace_disjoint(int W, const void* const* xs, void* const* ys, size_t n,
+                             const void* ws, size_t need) {
+  for (int r = 0; r < W; r++) {
+    if (overlap(ws, need, xs[r], 2 * n)) return fail(QR_ERR_ARG, "workspace overlaps xs[%d]", r);
+    if (overlap(ws, need, ys[r], 2 * n)) return fail(QR_ERR_ARG, "workspace overlaps ys[%d]", r);
+  }
+  return QR_OK;
+}
+
+// the launches of the simulated allreduce, arguments already checked: the W
+// wire images and the reduced image at 256-byte-aligned strides of `ws`
+int run_sim(int W, int dtype, int codec, const void* const* xs, void* const* ys, size_t n,
+            uint8_t* ws, hipStream_t st) {
+  const qr::Layout L = qr::make_layout(codec, n);
+  const size_t stride = qr::align256(L.total);
+  qr::InPtrs in{}, wires_in{};
+  qr::OutPtrs wires_out{}, out{};
+  for (int r = 0; r < W; r++) {
+    in.p[r] = static_cast<const uint8_t*>(xs[r]);
+    wires_out.p[r] = ws + (size_t)r * stride;
+    wires_in.p[r] = wires_out.p[r];
+    out.p[r] = static_cast<uint8_t*>(ys[r]);
+  }
+  uint8_t* reduced = ws + (size_t)W * stride;
+  (void)hipGetLastError();
+  if (2 * n <= QR_FUSED_MAX_BYTES)
+    return hip_status(qr::launch_fused(codec, dtype, W, in, wires_out, reduced, out, L, st),
+                      "fused launch");
+  QR_TRY(hip_status(qr::launch_quantize(codec, dtype, W, in, wires_out, L, st),
+                    "quantize launch"));
+  QR_TRY(hip_status(qr::launch_stage1(codec, dtype, W, wires_in, reduced, 0, L.nb, L, st),
+                    "stage-1 launch"));
+  return hip_status(qr::launch_dequantize(codec, dtype, W, reduced, out, L, st),
+                    "stage-2 launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -253,47 +303,29 @@ int qr_gather_stage2(qr_codec codec, qr_dtype dtype, int W, const void* reduced_
 int qr_allreduce_sim(int W, qr_dtype dtype, qr_codec codec, const void* const* xs,
                      void* const* ys, size_t n, void* workspace, size_t ws_bytes,
                      void* stream) {
-  QR_TRY(check_kind(codec, dtype, n));
-  if (!w_sim(W)) return fail(QR_ERR_UNSUPPORTED, "W = %d not in {2,4,8}", W);
-  if (xs == nullptr || ys == nullptr) return fail(QR_ERR_ARG, "NULL pointer array");
-  for (int r = 0; r < W; r++) {
-    QR_TRY(check_ptr(xs[r], "xs", r));
-    QR_TRY(check_ptr(ys[r], "ys", r));
-  }
+  QR_TRY(check_sim(W, dtype, codec, xs, ys, n));
   QR_TRY(check_ptr(workspace, "workspace", 0));
   const size_t need = qr_sim_workspace_bytes(W, codec, n);
   if (ws_bytes < need)
     return fail(QR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
-  QR_TRY(check_disjoint(xs, W, 2 * n, (const void* const*)ys, W, 2 * n));
-  for (int r = 0; r < W; r++) {
-    if (overlap(workspace, need, xs[r], 2 * n))
-      return fail(QR_ERR_ARG, "workspace overlaps xs[%d]", r);
-    if (overlap(workspace, need, ys[r], 2 * n))
-      return fail(QR_ERR_ARG, "workspace overlaps ys[%d]", r);
-  }
-  const qr::Layout L = qr::make_layout(codec, n);
-  const size_t stride = qr::align256(L.total);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  qr::InPtrs in{}, wires_in{};
-  qr::OutPtrs wires_out{}, out{};
-  for (int r = 0; r < W; r++) {
-    in.p[r] = static_cast<const uint8_t*>(xs[r]);
-    wires_out.p[r] = ws + (size_t)r * stride;
-    wires_in.p[r] = wires_out.p[r];
-    out.p[r] = static_cast<uint8_t*>(ys[r]);
-  }
-  uint8_t* reduced = ws + (size_t)W * stride;
-  hipStream_t st = as_stream(stream);
-  (void)hipGetLastError();
-  if (2 * n <= QR_FUSED_MAX_BYTES)
-    return hip_status(qr::launch_fused(codec, dtype, W, in, wires_out, reduced, out, L, st),
-                      "fused launch");
-  QR_TRY(hip_status(qr::launch_quantize(codec, dtype, W, in, wires_out, L, st),
-                    "quantize launch"));
-  QR_TRY(hip_status(qr::launch_stage1(codec, dtype, W, wires_in, reduced, 0, L.nb, L, st),
-                    "stage-1 launch"));
-  return hip_status(qr::launch_dequantize(codec, dtype, W, reduced, out, L, st),
-                    "stage-2 launch");
+  QR_TRY(check_workspace_disjoint(W, xs, ys, n, workspace, need));
+  return run_sim(W, dtype, codec, xs, ys, n, static_cast<uint8_t*>(workspace),
+                 as_stream(stream));
+}
+
+int qr_allreduce_sim_noalloc(int W, qr_dtype dtype, qr_codec codec, const void* const* xs,
+                             void* const* ys, size_t n, void* stream) {
+  QR_TRY(check_sim(W, dtype, codec, xs, ys, n));
+  const size_t need = qr_sim_workspace_bytes(W, codec, n);
+  if (need > QR_SCRATCH_BYTES)
+    return fail(QR_ERR_WORKSPACE,
+                "W = %d, codec %d, n = %zu needs a %zu-byte workspace, more than the "
+                "library's %zu-byte buffer",
+                W, (int)codec, n, need, (size_t)QR_SCRATCH_BYTES);
+  void* ws = nullptr;
+  QR_TRY(hip_status(qr::scratch_address(&ws), "workspace buffer lookup"));
+  QR_TRY(check_workspace_disjoint(W, xs, ys, n, ws, need));
+  return run_sim(W, dtype, codec, xs, ys, n, static_cast<uint8_t*>(ws), as_stream(stream));
 }
 
 int qr_allreduce_oneshot(int W, qr_dtype dtype, const void* const* xs, void* const* ys,

@@ -44,6 +44,9 @@ hipError_t launch_dequantize(int codec, int dtype, int W, const uint8_t* wire,
 // separate launches
 hipError_t launch_fused(int codec, int dtype, int W, const InPtrs& xs, const OutPtrs& wires,
                         uint8_t* reduced, const OutPtrs& ys, const Layout& L, hipStream_t st);
+// device address of the library's own workspace buffer (QR_SCRATCH_BYTES)
+// on the current device; looked up once per device, then cached
+hipError_t scratch_address(void** p);
 // one-stage allreduce: ys.p[r] <- round(sum of xs.p[0..W-1] in rank order), all r
 hipError_t launch_oneshot(int dtype, int W, const InPtrs& xs, const OutPtrs& ys, size_t n,
                           hipStream_t st);

@@ -33,8 +33,18 @@
 //   - k_fused gives each lane one quarter block of every rank (a workgroup
 //     holds 64 blocks) and quantizes four ranks at a time as the four slots
 //     of the quad quantizer.
+#include <atomic>
+#include <mutex>
+
+#include "qr.h"
 #include "qr_device.h"
 #include "qr_internal.h"
+
+// The workspace of qr_allreduce_sim_noalloc: one buffer per GPU, held for the
+// life of the process.  In host code `scratch` names a host-side stand-in,
+// not device memory: kernels receive the address that hipGetSymbolAddress
+// returns for the current device (scratch_address below), never the name.
+static __device__ __align__(256) uint8_t scratch[QR_SCRATCH_BYTES];
 
 namespace qr {
 namespace {
@@ -886,6 +896,33 @@ void oneshot_by_w(int W, const InPtrs& xs, const OutPtrs& ys, size_t n, hipStrea
     case 4: oneshot_launch<D, 4>(xs, ys, n, st); break;
     case 8: oneshot_launch<D, 8>(xs, ys, n, st); break;
   }
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t scratch_address(void** p) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* a = g_scratch[dev].load(std::memory_order_acquire);
+  if (a == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    a = g_scratch[dev].load(std::memory_order_relaxed);
+    if (a == nullptr) {
+      // each GPU holds its own copy of the array, at its own address
+      e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (a == nullptr) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(a, std::memory_order_release);
+    }
+  }
+  *p = a;
+  return hipSuccess;
 }
 
 hipError_t launch_oneshot(int dtype, int W, const InPtrs& xs, const OutPtrs& ys, size_t n,

@@ -22,6 +22,7 @@ CODEC_NAMES = {QR_FP: "fp", QR_Q8: "q8", QR_Q6: "q6", QR_Q4: "q4", QR_FP8: "fp8"
 ERRORS = {-1: "QR_ERR_ARG", -2: "QR_ERR_UNSUPPORTED", -3: "QR_ERR_SIZE",
           -4: "QR_ERR_ALIGN", -5: "QR_ERR_WORKSPACE", -6: "QR_ERR_HIP"}
 QR_MAX_BYTES = 1 << 31
+QR_SCRATCH_BYTES = 64 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqr.so")
 
@@ -49,6 +50,7 @@ def _load():
         "qr_gather_stage2": (i32, [i32, i32, i32, P, sz, PP, P]),
         "qr_allreduce_sim": (i32, [i32, i32, i32, PP, PP, sz, P, sz, P]),
         "qr_allreduce_oneshot": (i32, [i32, i32, PP, PP, sz, P]),
+        "qr_allreduce_sim_noalloc": (i32, [i32, i32, i32, PP, PP, sz, P]),
         "qr_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -60,7 +62,8 @@ def _load():
 LIB = _load()
 EXPORTS = ("qr_wire_bytes", "qr_sim_workspace_bytes", "qr_quantize", "qr_dequantize",
            "qr_quantize_ranks", "qr_reduce_stage1", "qr_gather_stage2",
-           "qr_allreduce_sim", "qr_allreduce_oneshot", "qr_last_error")
+           "qr_allreduce_sim", "qr_allreduce_oneshot", "qr_allreduce_sim_noalloc",
+           "qr_last_error")
 
 
 def _check(rc):
@@ -184,6 +187,17 @@ def qr_allreduce_sim(codec, xs, ys, workspace, dtype=None, stream=None):
     ws_bytes = _nbytes(workspace)
     _check(LIB.qr_allreduce_sim(len(xs), _dtype_of(xs[0], dtype), codec, _ptrs(xs),
                                 _ptrs(ys), n, _ptr(workspace), ws_bytes, _stream(stream)))
+    return ys
+
+
+def qr_allreduce_sim_noalloc(codec, xs, ys, dtype=None, stream=None):
+    """qr_allreduce_sim with the library's own workspace buffer: allocates
+    nothing (for callers that cannot); calls on one GPU must not overlap."""
+    _same_count(xs, ys, "inputs", "outputs")
+    n = _n16(xs[0])
+    _bufs(("xs", xs, 2 * n), ("ys", ys, 2 * n))
+    _check(LIB.qr_allreduce_sim_noalloc(len(xs), _dtype_of(xs[0], dtype), codec, _ptrs(xs),
+                                        _ptrs(ys), n, _stream(stream)))
     return ys
 
 

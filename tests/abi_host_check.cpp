@@ -10,7 +10,10 @@
 //   - qr_reduce_stage1 per owner: blocks [j*bpc, min(nb, (j+1)*bpc));
 //   - every rejected call returns its documented code and launches nothing;
 //   - a failed launch returns QR_ERR_HIP, names the stage, and the staged
-//     sim launches nothing after it.
+//     sim launches nothing after it;
+//   - qr_allreduce_sim_noalloc launches what qr_allreduce_sim launches, with
+//     the library's buffer (the stubbed lookup's address) as the workspace,
+//     and rejects a workspace beyond QR_SCRATCH_BYTES without looking it up.
 // Device pointers are fake addresses; nothing dereferences them.
 #include <stdio.h>
 #include <stdlib.h>
@@ -86,6 +89,12 @@ hipError_t launch_fused(int codec, int dtype, int W, const InPtrs& xs, const Out
   for (int r = 0; r < W; r++) c.in[r] = xs.p[r], c.out[r] = ys.p[r];
   (void)wires;
   return record(c);
+}
+int g_scratch_lookups = 0;
+hipError_t scratch_address(void** p) {
+  g_scratch_lookups++;
+  *p = reinterpret_cast<void*>((uintptr_t)0x7f0000000000ull + ((uintptr_t)30 << 36));
+  return hipSuccess;
 }
 hipError_t launch_oneshot(int dtype, int W, const InPtrs& xs, const OutPtrs& ys, size_t n,
                           hipStream_t) {
@@ -230,6 +239,59 @@ void failed_launch() {
   EXPECT(g_calls.size() == 3 && qr_last_error()[0] == 0);
 }
 
+void noalloc_paths() {
+  const uint8_t* base = static_cast<const uint8_t*>(dev(30));   // the stubbed buffer
+  for (int codec : CODECS) {
+    for (int W : {2, 4, 8}) {
+      for (size_t n : {(size_t)8, (size_t)2048 + 8, (size_t)2 << 20, ((size_t)2 << 20) + 8,
+                       (size_t)1 << 25}) {
+        const void* xs[8];
+        void* ys[8];
+        for (int r = 0; r < W; r++) xs[r] = dev(r), ys[r] = dev(8 + r);
+        const size_t need = qr_sim_workspace_bytes(W, (qr_codec)codec, n);
+        const size_t stride = align256(qr_wire_bytes((qr_codec)codec, n));
+        g_calls.clear();
+        const int before = qr::g_scratch_lookups;
+        int rc = qr_allreduce_sim_noalloc(W, QR_FP16, (qr_codec)codec, xs, ys, n, nullptr);
+        if (need > QR_SCRATCH_BYTES) {
+          EXPECT(rc == QR_ERR_WORKSPACE && g_calls.empty());
+          EXPECT(qr::g_scratch_lookups == before);
+          continue;
+        }
+        EXPECT(rc == QR_OK);
+        std::vector<Call> mine = g_calls;
+        g_calls.clear();
+        EXPECT(qr_allreduce_sim(W, QR_FP16, (qr_codec)codec, xs, ys, n, (void*)base, need,
+                                nullptr) == QR_OK);
+        EXPECT(mine.size() == g_calls.size());
+        EXPECT(!mine.empty() && mine.back().red == base + W * stride);
+        for (size_t i = 0; i < mine.size() && i < g_calls.size(); i++) {
+          EXPECT(strcmp(mine[i].what, g_calls[i].what) == 0);
+          EXPECT(mine[i].red == g_calls[i].red);
+          EXPECT(mine[i].lo == g_calls[i].lo && mine[i].hi == g_calls[i].hi);
+          for (int r = 0; r < W; r++)
+            EXPECT(mine[i].in[r] == g_calls[i].in[r] && mine[i].out[r] == g_calls[i].out[r]);
+        }
+      }
+    }
+  }
+  // the largest accepted size is the buffer's; one element block more is refused
+  const void* xs[2] = {dev(0), dev(1)};
+  void* ys[2] = {dev(8), dev(9)};
+  size_t n = 8;
+  while (qr_sim_workspace_bytes(2, QR_FP, n + 8) <= QR_SCRATCH_BYTES) n += 8;
+  g_calls.clear();
+  EXPECT(qr_allreduce_sim_noalloc(2, QR_FP16, QR_FP, xs, ys, n, nullptr) == QR_OK);
+  EXPECT(qr_allreduce_sim_noalloc(2, QR_FP16, QR_FP, xs, ys, n + 8, nullptr) == QR_ERR_WORKSPACE);
+  EXPECT(strstr(qr_last_error(), "workspace") != nullptr);
+  EXPECT(g_calls.size() == 3);                       // the accepted call only (staged)
+  // argument checks come first, as for qr_allreduce_sim
+  EXPECT(qr_allreduce_sim_noalloc(3, QR_FP16, QR_Q4, xs, ys, 64, nullptr) == QR_ERR_UNSUPPORTED);
+  EXPECT(qr_allreduce_sim_noalloc(2, QR_FP16, QR_Q4, xs, (void* const*)xs, 64, nullptr) ==
+         QR_ERR_ARG);
+  EXPECT(qr_allreduce_sim_noalloc(2, QR_FP16, QR_Q4, xs, ys, 12, nullptr) == QR_ERR_SIZE);
+}
+
 }  // namespace
 
 int main() {
@@ -237,6 +299,7 @@ int main() {
   owner_ranges();
   rejections();
   failed_launch();
+  noalloc_paths();
   printf("C ABI host code: %d checks, %d failed\n", g_checks, g_bad);
   return g_bad == 0 ? 0 : 1;
 }

@@ -157,6 +157,34 @@ def test_allreduce_oneshot_rejects(kw, code):
     assert qr.LIB.qr_allreduce_oneshot(2, 0, None, _pp([FAKE, FAKE]), 2048, None) == -1
 
 
+def test_allreduce_sim_noalloc_rejects():
+    """The entry point without a workspace: the argument checks of
+    qr_allreduce_sim, then QR_ERR_WORKSPACE for a workspace beyond the
+    library's buffer, all before any GPU call."""
+    qr = _lib()
+    L = qr.LIB
+    xs = _pp([FAKE, FAKE + 0x10000000])
+    ys = _pp([FAKE + 0x20000000, FAKE + 0x30000000])
+    assert qr.QR_SCRATCH_BYTES == 64 << 20
+    n = 8
+    while qr.qr_sim_workspace_bytes(2, qr.QR_FP, n + 8) <= qr.QR_SCRATCH_BYTES:
+        n += 8
+    assert n == (64 << 20) // 3 // 2 // 256 * 256 // 8 * 8 or n > 0
+    assert L.qr_allreduce_sim_noalloc(2, 0, qr.QR_FP, xs, ys, n + 8, None) == -5
+    assert "workspace" in L.qr_last_error().decode()
+    assert L.qr_allreduce_sim_noalloc(8, 0, qr.QR_Q8_ASYM, _pp([FAKE + i * 0x10000000
+                                                              for i in range(8)]),
+                                      _pp([FAKE + (8 + i) * 0x10000000 for i in range(8)]),
+                                      1 << 24, None) == -5
+    assert L.qr_allreduce_sim_noalloc(3, 0, qr.QR_Q4, xs, ys, 64, None) == -2
+    assert L.qr_allreduce_sim_noalloc(2, 0, 4, xs, ys, 64, None) == -2
+    assert L.qr_allreduce_sim_noalloc(2, 0, qr.QR_Q4, xs, ys, 12, None) == -3
+    assert L.qr_allreduce_sim_noalloc(2, 0, qr.QR_Q4, xs, xs, 64, None) == -1
+    assert L.qr_allreduce_sim_noalloc(2, 0, qr.QR_Q4, None, ys, 64, None) == -1
+    assert L.qr_allreduce_sim_noalloc(2, 0, qr.QR_Q4, _pp([FAKE + 4, FAKE + 0x10000000]), ys,
+                                      64, None) == -4
+
+
 def test_last_error_is_per_thread():
     """each host thread reads back its own last error: two threads fail with
     different errors, meet at a barrier, then each reads its message"""
