@@ -120,8 +120,24 @@ enum {
 /* Bytes of one rank's wire image for n elements (0 for an unknown codec). */
 size_t qr_wire_bytes(qr_codec codec, size_t n);
 
-/* Workspace qr_allreduce_sim needs: W wire images and one reduced image,
- * each starting on a 256-byte boundary (0 for an unsupported W or codec). */
+/* The receive buffer: the W ranks' wire data as an owner receives them,
+ * the stage-0 output and stage-1 input of qr_allreduce_sim.  It holds the
+ * bytes of the W wire images in tiles of 256 blocks: tile t of rank r
+ * (blocks [256t, 256t+256) of that rank) starts at byte (t*W + r) * T and
+ * holds the 256 blocks' codes (256 * 32*b/8 bytes), then their binary16
+ * scales (512 bytes), then (asymmetric codecs) their binary16 zeros (512
+ * bytes), so T = 256 * (32*b/8 + 2 [+ 2]); FP: the 256 blocks' raw 16-bit
+ * data, T = 16384.  Slots of blocks past the last one are padding, never
+ * read or written.  The W tiles of one range of blocks are thus adjacent:
+ * stage 1 reads them as one stream instead of W (on a real node the senders
+ * would write their tiles into the owner's buffer at these offsets).
+ * Bytes of the buffer: ceil(ceil(n/32)/256) * W * T (0 for an unknown codec
+ * or W outside 1..8). */
+size_t qr_recv_bytes(int W, qr_codec codec, size_t n);
+
+/* Workspace qr_allreduce_sim needs: the receive buffer (qr_recv_bytes),
+ * then the reduced image at the next 256-byte boundary (0 for an
+ * unsupported W or codec). */
 size_t qr_sim_workspace_bytes(int W, qr_codec codec, size_t n);
 
 /* Stage 0 for one rank: quantize x (n elements of `dtype`) into `wire`
@@ -150,6 +166,18 @@ int qr_reduce_stage1(qr_codec codec, qr_dtype dtype, int W,
                      const void* const* wires, size_t n, int owner,
                      void* reduced_wire, void* stream);
 
+/* Stage 0 for W ranks into a receive buffer (qr_recv_bytes(W, codec, n)
+ * bytes): the same codes, scales and zeros as qr_quantize_ranks writes, at
+ * the receive buffer's offsets.  W in {2,4,8}. */
+int qr_quantize_recv(qr_codec codec, qr_dtype dtype, int W,
+                     const void* const* xs, size_t n, void* recv, void* stream);
+
+/* Stage 1 from a receive buffer: as qr_reduce_stage1 (the same owner
+ * ranges, the same reduced image), reading the W ranks' blocks from `recv`.
+ * W in {2,4,8}. */
+int qr_reduce_recv(qr_codec codec, qr_dtype dtype, int W, const void* recv,
+                   size_t n, int owner, void* reduced_wire, void* stream);
+
 /* Stage 2: every rank r dequantizes reduced_wire into ys[r]; any W in 1..8. */
 int qr_gather_stage2(qr_codec codec, qr_dtype dtype, int W,
                      const void* reduced_wire, size_t n, void* const* ys,
@@ -158,12 +186,13 @@ int qr_gather_stage2(qr_codec codec, qr_dtype dtype, int W,
 /* The whole simulated allreduce: ys[r] = stage2(stage1(quantize(xs[0..W-1])))
  * for every r.  `workspace` is caller-owned device memory of at least
  * qr_sim_workspace_bytes(W, codec, n) bytes that must not overlap any x or y;
- * it receives the W wire images and the reduced image, as the staged calls
- * would write them.  Launches on `stream`: for 2n <= 4 MiB, one (each
- * workgroup takes its tile of blocks through all three stages, reading the
- * wire and reduced images back from the workspace); above, three, the
- * kernels of qr_quantize_ranks, qr_reduce_stage1 and qr_gather_stage2.  Both
- * give the same outputs and workspace contents.  W in {2,4,8}. */
+ * it receives the receive buffer and the reduced image, as qr_quantize_recv
+ * and qr_reduce_recv would write them.  Launches on `stream`: for
+ * 2n <= 4 MiB, one (each workgroup takes its tile of blocks through all
+ * three stages, reading the receive buffer and the reduced image back from
+ * the workspace); above, three, the kernels of qr_quantize_recv,
+ * qr_reduce_recv and qr_gather_stage2.  Both give the same outputs and
+ * workspace contents.  W in {2,4,8}. */
 int qr_allreduce_sim(int W, qr_dtype dtype, qr_codec codec,
                      const void* const* xs, void* const* ys, size_t n,
                      void* workspace, size_t ws_bytes, void* stream);

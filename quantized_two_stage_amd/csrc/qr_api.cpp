@@ -35,18 +35,22 @@ Layout make_layout(int codec, size_t n) {
   L.n = n;
   L.nb = (n + 31) / 32;
   L.nslices = 2 * L.nb;
+  L.ntiles = (L.nb + kTileBlocks - 1) / kTileBlocks;
   if (codec == QR_FP) {
     L.code_bytes = 2 * n;
     L.total = 2 * n;
+    L.tile_bytes = (size_t)kTileBlocks * 64;
     return L;
   }
-  L.code_bytes = L.nb * (size_t)(32 * code_bits(codec) / 8);
+  const size_t cb = (size_t)(32 * code_bits(codec) / 8);
+  L.code_bytes = L.nb * cb;
   L.off_s = align256(L.code_bytes);
   L.total = L.off_s + 2 * L.nb;
   if (codec & 8) {
     L.off_z = align256(L.total);
     L.total = L.off_z + 2 * L.nb;
   }
+  L.tile_bytes = (size_t)kTileBlocks * (cb + 2 + ((codec & 8) ? 2 : 0));
   return L;
 }
 
@@ -154,31 +158,50 @@ int check_workspace_disjoint(int W, const void* const* xs, void* const* ys, size
   return QR_OK;
 }
 
-// the launches of the simulated allreduce, arguments already checked: the W
-// wire images and the reduced image at 256-byte-aligned strides of `ws`
+// rank r's base pointer in a receive buffer: the start of its first tile
+void recv_ptrs(uint8_t* recv, int W, const qr::Layout& L, qr::OutPtrs& out, qr::InPtrs& in) {
+  for (int r = 0; r < W; r++) {
+    out.p[r] = recv + (size_t)r * L.tile_bytes;
+    in.p[r] = out.p[r];
+  }
+}
+
+// the launches of the simulated allreduce, arguments already checked: the
+// receive buffer at the start of `ws`, the reduced image at the next
+// 256-byte boundary after it
 int run_sim(int W, int dtype, int codec, const void* const* xs, void* const* ys, size_t n,
             uint8_t* ws, hipStream_t st) {
   const qr::Layout L = qr::make_layout(codec, n);
-  const size_t stride = qr::align256(L.total);
   qr::InPtrs in{}, wires_in{};
   qr::OutPtrs wires_out{}, out{};
+  recv_ptrs(ws, W, L, wires_out, wires_in);
   for (int r = 0; r < W; r++) {
     in.p[r] = static_cast<const uint8_t*>(xs[r]);
-    wires_out.p[r] = ws + (size_t)r * stride;
-    wires_in.p[r] = wires_out.p[r];
     out.p[r] = static_cast<uint8_t*>(ys[r]);
   }
-  uint8_t* reduced = ws + (size_t)W * stride;
+  uint8_t* reduced = ws + qr::align256(L.recv_bytes(W));
   (void)hipGetLastError();
   if (2 * n <= QR_FUSED_MAX_BYTES)
     return hip_status(qr::launch_fused(codec, dtype, W, in, wires_out, reduced, out, L, st),
                       "fused launch");
-  QR_TRY(hip_status(qr::launch_quantize(codec, dtype, W, in, wires_out, L, st),
+  QR_TRY(hip_status(qr::launch_quantize(codec, dtype, W, in, wires_out, true, L, st),
                     "quantize launch"));
-  QR_TRY(hip_status(qr::launch_stage1(codec, dtype, W, wires_in, reduced, 0, L.nb, L, st),
+  QR_TRY(hip_status(qr::launch_stage1(codec, dtype, W, wires_in, true, reduced, 0, L.nb, L,
+                                      st),
                     "stage-1 launch"));
   return hip_status(qr::launch_dequantize(codec, dtype, W, reduced, out, L, st),
                     "stage-2 launch");
+}
+
+// owner j's blocks [j*bpc, min(nb, (j+1)*bpc)), bpc = ceil(nb/W); all blocks for -1
+void owner_range(int W, int owner, const qr::Layout& L, size_t& lo, size_t& hi) {
+  lo = 0;
+  hi = L.nb;
+  if (owner >= 0) {
+    const size_t bpc = (L.nb + W - 1) / W;
+    lo = (size_t)owner * bpc < L.nb ? (size_t)owner * bpc : L.nb;
+    hi = lo + bpc < L.nb ? lo + bpc : L.nb;
+  }
 }
 
 }  // namespace
@@ -190,9 +213,15 @@ size_t qr_wire_bytes(qr_codec codec, size_t n) {
   return qr::make_layout(codec, n).total;
 }
 
+size_t qr_recv_bytes(int W, qr_codec codec, size_t n) {
+  if (W < 1 || W > qr::kMaxRanks || !qr::codec_valid(codec)) return 0;
+  return qr::make_layout(codec, n).recv_bytes(W);
+}
+
 size_t qr_sim_workspace_bytes(int W, qr_codec codec, size_t n) {
   if (!w_sim(W) || !qr::codec_valid(codec)) return 0;
-  return (size_t)(W + 1) * qr::align256(qr::make_layout(codec, n).total);
+  const qr::Layout L = qr::make_layout(codec, n);
+  return qr::align256(L.recv_bytes(W)) + qr::align256(L.total);
 }
 
 const char* qr_last_error(void) { return g_err; }
@@ -210,7 +239,7 @@ int qr_quantize(qr_codec codec, qr_dtype dtype, const void* x, size_t n,
   in.p[0] = static_cast<const uint8_t*>(x);
   out.p[0] = static_cast<uint8_t*>(wire);
   (void)hipGetLastError();
-  return hip_status(qr::launch_quantize(codec, dtype, 1, in, out, L, as_stream(stream)),
+  return hip_status(qr::launch_quantize(codec, dtype, 1, in, out, false, L, as_stream(stream)),
                     "quantize launch");
 }
 
@@ -250,7 +279,7 @@ int qr_quantize_ranks(qr_codec codec, qr_dtype dtype, int W, const void* const* 
     out.p[r] = static_cast<uint8_t*>(wires[r]);
   }
   (void)hipGetLastError();
-  return hip_status(qr::launch_quantize(codec, dtype, W, in, out, L, as_stream(stream)),
+  return hip_status(qr::launch_quantize(codec, dtype, W, in, out, false, L, as_stream(stream)),
                     "quantize launch");
 }
 
@@ -266,16 +295,54 @@ int qr_reduce_stage1(qr_codec codec, qr_dtype dtype, int W, const void* const* w
   const qr::Layout L = qr::make_layout(codec, n);
   const void* outs[1] = {reduced_wire};
   QR_TRY(check_disjoint(wires, W, L.total, outs, 1, L.total));
-  size_t lo = 0, hi = L.nb;
-  if (owner >= 0) {
-    const size_t bpc = (L.nb + W - 1) / W;
-    lo = (size_t)owner * bpc < L.nb ? (size_t)owner * bpc : L.nb;
-    hi = lo + bpc < L.nb ? lo + bpc : L.nb;
-  }
+  size_t lo, hi;
+  owner_range(W, owner, L, lo, hi);
   qr::InPtrs in{};
   for (int r = 0; r < W; r++) in.p[r] = static_cast<const uint8_t*>(wires[r]);
   (void)hipGetLastError();
-  return hip_status(qr::launch_stage1(codec, dtype, W, in,
+  return hip_status(qr::launch_stage1(codec, dtype, W, in, false,
+                                      static_cast<uint8_t*>(reduced_wire), lo, hi, L,
+                                      as_stream(stream)),
+                    "stage-1 launch");
+}
+
+int qr_quantize_recv(qr_codec codec, qr_dtype dtype, int W, const void* const* xs, size_t n,
+                     void* recv, void* stream) {
+  QR_TRY(check_kind(codec, dtype, n));
+  if (!w_sim(W)) return fail(QR_ERR_UNSUPPORTED, "W = %d not in {2,4,8}", W);
+  if (xs == nullptr) return fail(QR_ERR_ARG, "NULL pointer array");
+  for (int r = 0; r < W; r++) QR_TRY(check_ptr(xs[r], "xs", r));
+  QR_TRY(check_ptr(recv, "recv", 0));
+  const qr::Layout L = qr::make_layout(codec, n);
+  const void* outs[1] = {recv};
+  QR_TRY(check_disjoint(xs, W, 2 * n, outs, 1, L.recv_bytes(W)));
+  qr::InPtrs in{}, unused{};
+  qr::OutPtrs out{};
+  recv_ptrs(static_cast<uint8_t*>(recv), W, L, out, unused);
+  for (int r = 0; r < W; r++) in.p[r] = static_cast<const uint8_t*>(xs[r]);
+  (void)hipGetLastError();
+  return hip_status(qr::launch_quantize(codec, dtype, W, in, out, true, L, as_stream(stream)),
+                    "quantize launch");
+}
+
+int qr_reduce_recv(qr_codec codec, qr_dtype dtype, int W, const void* recv, size_t n,
+                   int owner, void* reduced_wire, void* stream) {
+  QR_TRY(check_kind(codec, dtype, n));
+  if (!w_sim(W)) return fail(QR_ERR_UNSUPPORTED, "W = %d not in {2,4,8}", W);
+  if (owner < -1 || owner >= W)
+    return fail(QR_ERR_ARG, "owner = %d outside -1..W-1", owner);
+  QR_TRY(check_ptr(recv, "recv", 0));
+  QR_TRY(check_ptr(reduced_wire, "reduced_wire", 0));
+  const qr::Layout L = qr::make_layout(codec, n);
+  const void* outs[1] = {reduced_wire};
+  QR_TRY(check_disjoint(&recv, 1, L.recv_bytes(W), outs, 1, L.total));
+  size_t lo, hi;
+  owner_range(W, owner, L, lo, hi);
+  qr::InPtrs in{};
+  qr::OutPtrs unused{};
+  recv_ptrs(const_cast<uint8_t*>(static_cast<const uint8_t*>(recv)), W, L, unused, in);
+  (void)hipGetLastError();
+  return hip_status(qr::launch_stage1(codec, dtype, W, in, true,
                                       static_cast<uint8_t*>(reduced_wire), lo, hi, L,
                                       as_stream(stream)),
                     "stage-1 launch");

@@ -92,7 +92,36 @@ struct Geo {
   uint32_t nb;       // blocks per rank
   uint32_t off_s;    // scale plane offset
   uint32_t off_z;    // zero plane offset
+  uint64_t tstride;  // receive buffer: bytes from one tile of a rank to its next (W tiles)
 };
+
+// Byte offsets of block blk's codes, scale and zero from a rank's base
+// pointer.  Recv == false: the planar wire image (codes at blk * CB, scales
+// and zeros in their planes).  Recv == true: the rank's tiles in the receive
+// buffer, the base being its first tile; tile t = blk / kTileBlocks starts
+// t * tstride further and holds kTileBlocks blocks' codes, then their scales,
+// then their zeros.  FP (raw data) uses code() alone, with CB = 64.
+template <int CB, bool Recv>
+struct WireAt {
+  static constexpr uint32_t kTB = kTileBlocks;
+  __device__ static __forceinline__ uint64_t tile(const Geo& g, uint32_t blk) {
+    return (uint64_t)(blk / kTB) * g.tstride;
+  }
+  __device__ static __forceinline__ uint64_t code(const Geo& g, uint32_t blk) {
+    if constexpr (Recv) return tile(g, blk) + (blk % kTB) * (uint32_t)CB;
+    return (uint64_t)blk * CB;
+  }
+  __device__ static __forceinline__ uint64_t scale(const Geo& g, uint32_t blk) {
+    if constexpr (Recv) return tile(g, blk) + kTB * CB + (blk % kTB) * 2u;
+    return g.off_s + (uint64_t)blk * 2;
+  }
+  __device__ static __forceinline__ uint64_t zero(const Geo& g, uint32_t blk) {
+    if constexpr (Recv) return tile(g, blk) + kTB * (CB + 2) + (blk % kTB) * 2u;
+    return g.off_z + (uint64_t)blk * 2;
+  }
+};
+template <int C, bool Recv>
+using At = WireAt<CodecT<C>::block_bytes, Recv>;
 
 __device__ __forceinline__ uint32_t ld_u16(const uint8_t* p) {
   return *reinterpret_cast<const uint16_t*>(p);
@@ -185,8 +214,9 @@ __device__ __forceinline__ uint32_t from_lane_u(uint32_t v) { return quad_perm_u
 // (8q >= n) are left out of the statistics and get code 0.  q_end is a
 // multiple of 4, so a quad is wholly in or out.  Full: the caller guarantees
 // that every quarter holds 8 elements and lies below q_end (no range checks
-// are made).
-template <int C, int Stage, bool Full, int U>
+// are made).  Recv: the wire data go to a rank's tiles of the receive buffer
+// (wire[u] the rank's base there) instead of a planar wire image.
+template <int C, int Stage, bool Full, int U, bool Recv>
 __device__ __forceinline__ void quantize_core(float (&v)[U][8], uint8_t* const (&wire)[U],
                                               const uint32_t (&q)[U], uint8_t* own_wire,
                                               uint32_t own_q, uint32_t q_end, const Geo& g) {
@@ -215,8 +245,8 @@ __device__ __forceinline__ void quantize_core(float (&v)[U][8], uint8_t* const (
   const BlockParams<C> p = block_params<C>(bx, bn);
   if (j < U && (Full || own_q < q_end)) {
     const uint32_t own_blk = own_q >> 2;
-    st_u16(own_wire + g.off_s + (size_t)own_blk * 2, p.s);
-    if constexpr (T::asym) st_u16(own_wire + g.off_z + (size_t)own_blk * 2, p.z);
+    st_u16(own_wire + At<C, Recv>::scale(g, own_blk), p.s);
+    if constexpr (T::asym) st_u16(own_wire + At<C, Recv>::zero(g, own_blk), p.z);
   }
   const uint32_t flags = (p.sat ? 1u : 0u) | (p.s != 0u ? 2u : 0u);
   float inv[U], tz[U];
@@ -249,7 +279,7 @@ __device__ __forceinline__ void quantize_core(float (&v)[U][8], uint8_t* const (
     const bool keep = (Full || 8 * q[u] < g.n) && (!T::fp8 || (fl[u] & 2u) != 0u);
 #pragma unroll
     for (int k = 0; k < nw; k++) w[k] = keep ? w[k] : 0u;
-    uint8_t* cb = wire[u] + (size_t)(q[u] >> 2) * T::block_bytes;
+    uint8_t* cb = wire[u] + At<C, Recv>::code(g, q[u] >> 2);
     if constexpr (T::bits == 6) {
       // lanes 0 and 2 of the quad each write 96 bits (their own 48 and their
       // odd neighbour's 48)
@@ -272,16 +302,17 @@ __device__ __forceinline__ void quantize_core(float (&v)[U][8], uint8_t* const (
 
 // four quarters q0 + 256u (u = 0..3) of one wire image: a quad holds the
 // quarters of four blocks, one per slot
-template <int C, int Stage, bool Full>
+template <int C, int Stage, bool Full, bool Recv>
 __device__ __forceinline__ void quantize_quarters(float (&v)[4][8], uint32_t q0,
                                                   uint32_t q_end, uint8_t* wire,
                                                   const Geo& g) {
   uint8_t* const wp[4] = {wire, wire, wire, wire};
   const uint32_t qs[4] = {q0, q0 + kThreads, q0 + 2 * kThreads, q0 + 3 * kThreads};
-  quantize_core<C, Stage, Full, 4>(v, wp, qs, wire, q0 + (threadIdx.x & 3) * kThreads, q_end, g);
+  quantize_core<C, Stage, Full, 4, Recv>(v, wp, qs, wire, q0 + (threadIdx.x & 3) * kThreads,
+                                         q_end, g);
 }
 
-template <int C, int D, bool Full, int Stage = kStage0>
+template <int C, int D, bool Full, bool Recv, int Stage = kStage0>
 __device__ __forceinline__ void quantize_tile(const u32x4 (&raw)[4], uint32_t q0,
                                               uint8_t* wire, const Geo& g) {
   float v[4][8];
@@ -294,7 +325,7 @@ __device__ __forceinline__ void quantize_tile(const u32x4 (&raw)[4], uint32_t q0
       v[u][2 * k + 1] = ld16<D>(rw[k] >> 16);
     }
   }
-  quantize_quarters<C, Stage, Full>(v, q0, 4 * g.nb, wire, g);
+  quantize_quarters<C, Stage, Full, Recv>(v, q0, 4 * g.nb, wire, g);
 }
 
 template <bool Full>
@@ -314,32 +345,48 @@ __device__ __forceinline__ bool tile_full(uint32_t wg, uint32_t n) {
   return 8ull * ((uint64_t)wg + 1ull) * (kThreads * kPerLane) <= (uint64_t)n;
 }
 
-template <int C, int D>
+// a workgroup quantizes 256 blocks of rank blockIdx.y: one tile of the
+// receive buffer
+template <int C, int D, bool Recv>
 __global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires, Geo g) {
   static_assert(kPerLane == 4, "one block per lane of the quad");
+  static_assert(kThreads * kPerLane / 4 == kTileBlocks, "a workgroup's blocks are one tile");
   const int r = blockIdx.y;
   const uint32_t q0 = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
   u32x4 raw[4];
   if (tile_full(blockIdx.x, g.n)) {
     load_tile<true>(xs.p[r], q0, g.n, raw);
-    quantize_tile<C, D, true>(raw, q0, wires.p[r], g);
+    quantize_tile<C, D, true, Recv>(raw, q0, wires.p[r], g);
   } else {
     load_tile<false>(xs.p[r], q0, g.n, raw);
-    quantize_tile<C, D, false>(raw, q0, wires.p[r], g);
+    quantize_tile<C, D, false, Recv>(raw, q0, wires.p[r], g);
   }
 }
 
+// Byte offset of 16-byte chunk c of a rank's raw data (the FP codec's wire):
+// planar, or in the rank's tiles of the receive buffer (a tile holds the
+// kTileBlocks * 4 chunks of its blocks).
+template <bool Recv>
+__device__ __forceinline__ uint64_t fp_chunk(uint64_t tstride, uint32_t c) {
+  constexpr uint32_t kTC = kTileBlocks * 4;
+  if constexpr (Recv) return (uint64_t)(c / kTC) * tstride + (c % kTC) * 16u;
+  return (uint64_t)c * 16;
+}
+
 // stages 0 and 2 of FP: dst.p[r] <- src.p[r], 16-byte chunks, four per
-// lane; Stage selects the store policy (and names the two uses apart in
-// profiles); Din != Dout converts every element (the cast option: bfloat16
-// into a binary16 wire at stage 0, binary16 back to bfloat16 at stage 2)
-template <int Stage, int Din, int Dout>
+// lane (a workgroup's 1024 chunks are one tile); Stage selects the store
+// policy (and names the two uses apart in profiles); Din != Dout converts
+// every element (the cast option: bfloat16 into a binary16 wire at stage 0,
+// binary16 back to bfloat16 at stage 2); Recv: the destination is a rank's
+// tiles of the receive buffer
+template <int Stage, int Din, int Dout, bool Recv>
 __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
-                                                   uint32_t nchunks) {
+                                                   uint32_t nchunks, uint64_t tstride) {
+  static_assert(kThreads * kPerLane == kTileBlocks * 4, "a workgroup's chunks are one tile");
   constexpr int kS = Stage == 0 ? kStage0 : kStage2;
   const int r = blockIdx.y;
   const u32x4* s = reinterpret_cast<const u32x4*>(src.p[r]);
-  u32x4* d = reinterpret_cast<u32x4*>(dst.p[r]);
+  uint8_t* d = dst.p[r];
   const uint32_t base = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
   u32x4 q[kPerLane];
 #pragma unroll
@@ -355,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
       for (int k = 0; k < 4; k++)
         q[j][k] = st16x2<Dout>(ld16<Din>(q[j][k] & 0xffffu), ld16<Din>(q[j][k] >> 16));
     }
-    if (c < nchunks) st_out<kS>(d + c, q[j]);
+    if (c < nchunks) st_out<kS>(reinterpret_cast<u32x4*>(d + fp_chunk<Recv>(tstride, c)), q[j]);
   }
 }
 
@@ -366,16 +413,21 @@ __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
 template <int C, int W>
 struct S1In {
   uint32_t cw[W][CodecT<C>::words];
-  float sc[W], zc[W];
+  uint32_t sh[W], zh[W];     // binary16 scale and zero bits
 };
 
-template <int C, int W>
+// the W ranks' code blocks and scales (and zeros) of block blk; Recv: from
+// the ranks' tiles of the receive buffer (the W tiles of one workgroup's
+// blocks are consecutive there, so the workgroup reads one contiguous range)
+template <int C, int W, bool Recv>
 __device__ __forceinline__ void s1_load(const InPtrs& wires, uint32_t blk, const Geo& g,
                                         S1In<C, W>& in) {
   using T = CodecT<C>;
+  const uint64_t co = At<C, Recv>::code(g, blk);
+  const uint64_t so = At<C, Recv>::scale(g, blk), zo = At<C, Recv>::zero(g, blk);
 #pragma unroll
   for (int r = 0; r < W; r++) {
-    const uint8_t* cb = wires.p[r] + (size_t)blk * T::block_bytes;
+    const uint8_t* cb = wires.p[r] + co;
     if constexpr (T::words == 6) {
 #pragma unroll
       for (int k = 0; k < 3; k++) {
@@ -391,8 +443,8 @@ __device__ __forceinline__ void s1_load(const InPtrs& wires, uint32_t blk, const
         in.cw[r][4 * k + 2] = q.z; in.cw[r][4 * k + 3] = q.w;
       }
     }
-    in.sc[r] = h2f(ld_u16(wires.p[r] + g.off_s + (size_t)blk * 2)) * T::unpack_scale;
-    in.zc[r] = T::asym ? h2f(ld_u16(wires.p[r] + g.off_z + (size_t)blk * 2)) : 0.0f;
+    in.sh[r] = ld_u16(wires.p[r] + so);
+    in.zh[r] = T::asym ? ld_u16(wires.p[r] + zo) : 0u;
   }
 }
 
@@ -411,15 +463,17 @@ __device__ __forceinline__ void s1_reduce_store(const S1In<C, W>& in, uint8_t* r
   float acc[kBlock];
 #pragma unroll
   for (int r = 0; r < W; r++) {
+    const float sc = h2f(in.sh[r]) * T::unpack_scale;
+    const float zc = T::asym ? h2f(in.zh[r]) : 0.0f;
     if constexpr (T::bits == 6 || W > 4) {
-      add_codes<C, kBlock>(acc, in.cw[r], in.sc[r], in.zc[r], r == 0);
+      add_codes<C, kBlock>(acc, in.cw[r], sc, zc, r == 0);
     } else {
 #pragma unroll
       for (int k = 0; k < 4; k++) {
         float a8[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) a8[i] = acc[8 * k + i];
-        add_codes<C, 8>(a8, in.cw[r] + k * (8 * T::bits / 32), in.sc[r], in.zc[r], r == 0);
+        add_codes<C, 8>(a8, in.cw[r] + k * (8 * T::bits / 32), sc, zc, r == 0);
 #pragma unroll
         for (int i = 0; i < 8; i++) acc[8 * k + i] = a8[i];
       }
@@ -448,7 +502,9 @@ __device__ __forceinline__ void s1_reduce_store(const S1In<C, W>& in, uint8_t* r
       w[k] = first <= 0 ? 0u : first >= 32 ? w[k] : w[k] & ((1u << first) - 1u);
     }
   }
-  uint8_t* cb = red + (size_t)blk * T::block_bytes;
+  // the reduced image is a planar wire image
+  uint8_t* cb = red + At<C, false>::code(g, blk);
+  const uint64_t so = At<C, false>::scale(g, blk), zo = At<C, false>::zero(g, blk);
   if constexpr (T::words == 6) {
 #pragma unroll
     for (int k = 0; k < 3; k++)
@@ -459,12 +515,12 @@ __device__ __forceinline__ void s1_reduce_store(const S1In<C, W>& in, uint8_t* r
       st_out<kStage1>(reinterpret_cast<u32x4*>(cb) + k,
                       u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]});
   }
-  st_u16(red + g.off_s + (size_t)blk * 2, p.s);
-  if constexpr (T::asym) st_u16(red + g.off_z + (size_t)blk * 2, p.z);
+  st_u16(red + so, p.s);
+  if constexpr (T::asym) st_u16(red + zo, p.z);
 }
 
 // one lane per block
-template <int C, int D, int W>
+template <int C, int D, int W, bool Recv>
 __global__ __launch_bounds__(kThreads) void k_stage1(InPtrs wires, uint8_t* red,
                                                      uint32_t blk_lo, uint32_t blk_hi,
                                                      Geo g) {
@@ -473,32 +529,35 @@ __global__ __launch_bounds__(kThreads) void k_stage1(InPtrs wires, uint8_t* red,
   const uint32_t wg_end = blk_lo + (blockIdx.x + 1) * kThreads;
   if (wg_end <= blk_hi && (uint64_t)wg_end * kBlock <= (uint64_t)g.n) {
     S1In<C, W> in;
-    s1_load<C, W>(wires, blk, g, in);
+    s1_load<C, W, Recv>(wires, blk, g, in);
     s1_reduce_store<C, W, true>(in, red, blk, g);
     return;
   }
   if (blk >= blk_hi) return;
   S1In<C, W> in;
-  s1_load<C, W>(wires, blk, g, in);
+  s1_load<C, W, Recv>(wires, blk, g, in);
   s1_reduce_store<C, W, false>(in, red, blk, g);
 }
 
 // Sum of W raw buffers over 16-byte chunks [c_lo, c_hi): the binary32 sum
 // in rank order 0..W-1, rounded once to D, into outs.p[blockIdx.y].  Stage 1
-// of the FP codec (one output: the reduced image) and the one-stage
-// allreduce (gridDim.y = W: every rank reads all W buffers and writes its
-// own output).  Stage selects the store policy of the outputs.
-template <int D, int W, int Stage>
+// of the FP codec (one output: the reduced image; Recv: the inputs are the
+// ranks' tiles of the receive buffer) and the one-stage allreduce
+// (gridDim.y = W: every rank reads all W buffers and writes its own output).
+// Stage selects the store policy of the outputs.
+template <int D, int W, int Stage, bool Recv>
 __global__ __launch_bounds__(kThreads) void k_sum_fp(InPtrs xs, OutPtrs outs,
-                                                     uint32_t c_lo, uint32_t c_hi) {
+                                                     uint32_t c_lo, uint32_t c_hi,
+                                                     uint64_t tstride) {
   const uint32_t base = c_lo + blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
   u32x4 q[kPerLane][W];
 #pragma unroll
   for (int j = 0; j < kPerLane; j++) {
     const uint32_t c = base + j * kThreads;
+    const uint64_t off = fp_chunk<Recv>(tstride, c < c_hi ? c : c_lo);
 #pragma unroll
     for (int r = 0; r < W; r++)
-      q[j][r] = ld_in<kStage1>(reinterpret_cast<const u32x4*>(xs.p[r]) + (c < c_hi ? c : c_lo));
+      q[j][r] = ld_in<kStage1>(reinterpret_cast<const u32x4*>(xs.p[r] + off));
   }
   u32x4* out_p = reinterpret_cast<u32x4*>(outs.p[blockIdx.y]);
 #pragma unroll
@@ -576,8 +635,9 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* wire, OutPt
 // block):
 //   stage 0  the lane's quarter of every rank, four ranks at a time as the
 //            four slots of quantize_core (lane j of the quad derives the
-//            scale of rank j's block), written to the rank's wire image;
-//   stage 1  the W wire quarters read back, dequantized and summed in rank
+//            scale of rank j's block), written to the rank's tile of the
+//            receive buffer;
+//   stage 1  the W quarters read back, dequantized and summed in rank
 //            order, quantized as one slot into the reduced image;
 //   stage 2  the reduced quarter read back, dequantized once and stored to
 //            every rank's output (each rank's output is the same function of
@@ -623,7 +683,7 @@ __device__ __forceinline__ void fused_tile(const InPtrs& xs, const OutPtrs& wire
 #pragma unroll
     for (int u = 1; u < U; u++)
       if (j % U == u) own = wp[u];
-    quantize_core<C, kKeep, Full, U>(v, wp, qs, own, q, q_end, g);
+    quantize_core<C, kKeep, Full, U, true>(v, wp, qs, own, q, q_end, g);
   }
   __syncthreads();
 
@@ -632,11 +692,13 @@ __device__ __forceinline__ void fused_tile(const InPtrs& xs, const OutPtrs& wire
     const uint32_t blk = ql >> 2;
     uint32_t w[W][IO::nw];
     float sc[W], zc[W];
+    const uint64_t co = At<C, true>::code(g, blk);
+    const uint64_t so = At<C, true>::scale(g, blk), zo = At<C, true>::zero(g, blk);
 #pragma unroll
     for (int r = 0; r < W; r++) {
-      IO::load(wires.p[r] + (size_t)blk * T::block_bytes, ql & 3, w[r]);
-      sc[r] = h2f(ld_u16(wires.p[r] + g.off_s + (size_t)blk * 2)) * T::unpack_scale;
-      zc[r] = T::asym ? h2f(ld_u16(wires.p[r] + g.off_z + (size_t)blk * 2)) : 0.0f;
+      IO::load(wires.p[r] + co, ql & 3, w[r]);
+      sc[r] = h2f(ld_u16(wires.p[r] + so)) * T::unpack_scale;
+      zc[r] = T::asym ? h2f(ld_u16(wires.p[r] + zo)) : 0.0f;
     }
     // acc = x0 + x1 + ... in rank order, as in stage 1's own kernel
     float acc[1][8];
@@ -644,7 +706,7 @@ __device__ __forceinline__ void fused_tile(const InPtrs& xs, const OutPtrs& wire
     for (int r = 0; r < W; r++) add_codes<C, 8>(acc[0], w[r], sc[r], zc[r], r == 0);
     uint8_t* const rp[1] = {red};
     const uint32_t rq[1] = {q};
-    quantize_core<C, kKeep, Full, 1>(acc, rp, rq, red, q, q_end, g);
+    quantize_core<C, kKeep, Full, 1, false>(acc, rp, rq, red, q, q_end, g);
   }
   __syncthreads();
 
@@ -679,15 +741,17 @@ __global__ __launch_bounds__(kThreads) void k_fused(InPtrs xs, OutPtrs wires, ui
     fused_tile<C, D, W, false>(xs, wires, red, ys, q, g);
 }
 
-// the FP codec in one launch: copy (converting under the cast option), sum,
-// copy back; one 16-byte chunk per lane
+// the FP codec in one launch: copy (converting under the cast option) into
+// the receive buffer, sum, copy back; one 16-byte chunk per lane
 template <int D, int W>
 __global__ __launch_bounds__(kThreads) void k_fused_fp(InPtrs xs, OutPtrs wires, uint8_t* red,
-                                                       OutPtrs ys, uint32_t nchunks) {
+                                                       OutPtrs ys, uint32_t nchunks,
+                                                       uint64_t tstride) {
   constexpr int Dw = D == kBF16H ? kF16 : D;      // the wire's element type
   constexpr int Dx = D == kBF16H ? kBF16 : D;     // the buffers' element type
   const uint32_t c = blockIdx.x * kThreads + threadIdx.x;
   const bool has = c < nchunks;
+  const uint64_t wo = fp_chunk<true>(tstride, c);
   if (has) {
 #pragma unroll
     for (int r = 0; r < W; r++) {
@@ -697,14 +761,14 @@ __global__ __launch_bounds__(kThreads) void k_fused_fp(InPtrs xs, OutPtrs wires,
         for (int k = 0; k < 4; k++)
           q[k] = st16x2<Dw>(ld16<Dx>(q[k] & 0xffffu), ld16<Dx>(q[k] >> 16));
       }
-      reinterpret_cast<u32x4*>(wires.p[r])[c] = q;
+      *reinterpret_cast<u32x4*>(wires.p[r] + wo) = q;
     }
   }
   __syncthreads();
   if (has) {
     u32x4 q[W];
 #pragma unroll
-    for (int r = 0; r < W; r++) q[r] = reinterpret_cast<const u32x4*>(wires.p[r])[c];
+    for (int r = 0; r < W; r++) q[r] = *reinterpret_cast<const u32x4*>(wires.p[r] + wo);
     uint32_t out[4];
 #pragma unroll
     for (int k = 0; k < 4; k++) {
@@ -734,15 +798,17 @@ __global__ __launch_bounds__(kThreads) void k_fused_fp(InPtrs xs, OutPtrs wires,
 // ---------------------------------------------------------------------------
 // dispatch
 
-Geo geo(const Layout& L) {
-  return Geo{(uint32_t)L.n, (uint32_t)L.nb, (uint32_t)L.off_s, (uint32_t)L.off_z};
+// tstride: in the receive buffer, W tiles separate a rank's consecutive tiles
+Geo geo(const Layout& L, int W = 0, bool recv = false) {
+  return Geo{(uint32_t)L.n, (uint32_t)L.nb, (uint32_t)L.off_s, (uint32_t)L.off_z,
+             recv ? (uint64_t)W * L.tile_bytes : 0ull};
 }
 
 unsigned groups(size_t items, size_t per_group) {
   return (unsigned)((items + per_group - 1) / per_group);
 }
 
-template <int C, int D, int W>
+template <int C, int D, int W, bool Recv>
 void s1_launch(const InPtrs& wires, uint8_t* red, size_t blk_lo, size_t blk_hi,
                const Layout& L, hipStream_t st) {
   if constexpr (C == kFP) {
@@ -752,46 +818,59 @@ void s1_launch(const InPtrs& wires, uint8_t* red, size_t blk_lo, size_t blk_hi,
     const uint32_t c_hi = (uint32_t)(blk_hi * 4 < L.n / 8 ? blk_hi * 4 : L.n / 8);
     OutPtrs out{};
     out.p[0] = red;
-    hipLaunchKernelGGL((k_sum_fp<D, W, kStage1>), dim3(groups(c_hi - c_lo, kThreads * kPerLane)),
-                       dim3(kThreads), 0, st, wires, out, c_lo, c_hi);
+    hipLaunchKernelGGL((k_sum_fp<D, W, kStage1, Recv>),
+                       dim3(groups(c_hi - c_lo, kThreads * kPerLane)), dim3(kThreads), 0, st,
+                       wires, out, c_lo, c_hi, geo(L, W, Recv).tstride);
   } else {
-    hipLaunchKernelGGL((k_stage1<C, D, W>), dim3(groups(blk_hi - blk_lo, kThreads)),
+    hipLaunchKernelGGL((k_stage1<C, D, W, Recv>), dim3(groups(blk_hi - blk_lo, kThreads)),
                        dim3(kThreads), 0, st, wires, red, (uint32_t)blk_lo,
-                       (uint32_t)blk_hi, geo(L));
+                       (uint32_t)blk_hi, geo(L, W, Recv));
   }
 }
 
 // stage 1 depends on the buffer type only through the FP wire's element
 // type (binary16 under the cast option); the other codecs' wires hold codes
 template <int C, int D>
-void s1_by_w(int W, const InPtrs& wires, uint8_t* red, size_t lo, size_t hi,
+void s1_by_w(int W, const InPtrs& wires, bool recv, uint8_t* red, size_t lo, size_t hi,
              const Layout& L, hipStream_t st) {
   if constexpr (D == kBF16H || (C != kFP && D != kF16)) {
-    s1_by_w<C, kF16>(W, wires, red, lo, hi, L, st);
+    s1_by_w<C, kF16>(W, wires, recv, red, lo, hi, L, st);
   } else {
-    switch (W) {
-      case 2: s1_launch<C, D, 2>(wires, red, lo, hi, L, st); break;
-      case 4: s1_launch<C, D, 4>(wires, red, lo, hi, L, st); break;
-      case 8: s1_launch<C, D, 8>(wires, red, lo, hi, L, st); break;
+    switch (W * 2 + (recv ? 1 : 0)) {
+      case 4: s1_launch<C, D, 2, false>(wires, red, lo, hi, L, st); break;
+      case 5: s1_launch<C, D, 2, true>(wires, red, lo, hi, L, st); break;
+      case 8: s1_launch<C, D, 4, false>(wires, red, lo, hi, L, st); break;
+      case 9: s1_launch<C, D, 4, true>(wires, red, lo, hi, L, st); break;
+      case 16: s1_launch<C, D, 8, false>(wires, red, lo, hi, L, st); break;
+      case 17: s1_launch<C, D, 8, true>(wires, red, lo, hi, L, st); break;
       default: break;
     }
   }
 }
 
-template <int C, int D>
-void q_dispatch(int W, const InPtrs& xs, const OutPtrs& wires, const Layout& L,
-                hipStream_t st) {
+template <int C, int D, bool Recv>
+void q_launch(int W, const InPtrs& xs, const OutPtrs& wires, const Layout& L, hipStream_t st) {
   if constexpr (C == kFP) {
     // the FP wire holds the buffer's raw elements (binary16 under the cast)
     constexpr int Dw = D == kBF16H ? kF16 : D;
     constexpr int Din = D == kBF16H ? kBF16 : D;
-    hipLaunchKernelGGL((k_copy<0, Din, Dw>), dim3(groups(L.n / 8, kThreads * kPerLane), W),
-                       dim3(kThreads), 0, st, xs, wires, (uint32_t)(L.n / 8));
+    hipLaunchKernelGGL((k_copy<0, Din, Dw, Recv>), dim3(groups(L.n / 8, kThreads * kPerLane), W),
+                       dim3(kThreads), 0, st, xs, wires, (uint32_t)(L.n / 8),
+                       geo(L, W, Recv).tstride);
   } else {
-    hipLaunchKernelGGL((k_quantize<C, D>),
+    hipLaunchKernelGGL((k_quantize<C, D, Recv>),
                        dim3(groups(4 * L.nb, kThreads * kPerLane), W),
-                       dim3(kThreads), 0, st, xs, wires, geo(L));
+                       dim3(kThreads), 0, st, xs, wires, geo(L, W, Recv));
   }
+}
+
+template <int C, int D>
+void q_dispatch(int W, const InPtrs& xs, const OutPtrs& wires, bool recv, const Layout& L,
+                hipStream_t st) {
+  if (recv)
+    q_launch<C, D, true>(W, xs, wires, L, st);
+  else
+    q_launch<C, D, false>(W, xs, wires, L, st);
 }
 
 template <int C, int D>
@@ -802,8 +881,9 @@ void dq_dispatch(int W, const uint8_t* wire, const OutPtrs& ys, const Layout& L,
     for (int r = 0; r < kMaxRanks; r++) src.p[r] = wire;
     constexpr int Dw = D == kBF16H ? kF16 : D;
     constexpr int Dout = D == kBF16H ? kBF16 : D;
-    hipLaunchKernelGGL((k_copy<2, Dw, Dout>), dim3(groups(L.n / 8, kThreads * kPerLane), W),
-                       dim3(kThreads), 0, st, src, ys, (uint32_t)(L.n / 8));
+    hipLaunchKernelGGL((k_copy<2, Dw, Dout, false>),
+                       dim3(groups(L.n / 8, kThreads * kPerLane), W), dim3(kThreads), 0, st,
+                       src, ys, (uint32_t)(L.n / 8), 0ull);
   } else {
     hipLaunchKernelGGL((k_dequant<C, D>), dim3(groups(L.n / 8, kThreads * kPerLane), W),
                        dim3(kThreads), 0, st, wire, ys, geo(L));
@@ -816,11 +896,11 @@ void fused_launch(const InPtrs& xs, const OutPtrs& wires, uint8_t* red, const Ou
   if constexpr (C == kFP) {
     const uint32_t nc = (uint32_t)(L.n / 8);
     hipLaunchKernelGGL((k_fused_fp<D, W>), dim3(groups(nc, kThreads)), dim3(kThreads), 0, st,
-                       xs, wires, red, ys, nc);
+                       xs, wires, red, ys, nc, geo(L, W, true).tstride);
   } else {
     // 64 blocks (256 quarters) per workgroup
     hipLaunchKernelGGL((k_fused<C, D, W>), dim3(groups(L.nb, kThreads / 4)), dim3(kThreads),
-                       0, st, xs, wires, red, ys, geo(L));
+                       0, st, xs, wires, red, ys, geo(L, W, true));
   }
 }
 
@@ -863,16 +943,17 @@ hipError_t launch_fused(int codec, int dtype, int W, const InPtrs& xs, const Out
 }
 
 hipError_t launch_quantize(int codec, int dtype, int W, const InPtrs& xs,
-                           const OutPtrs& wires, const Layout& L, hipStream_t st) {
-  QR_DISPATCH(codec, dtype, q_dispatch, W, xs, wires, L, st);
+                           const OutPtrs& wires, bool recv, const Layout& L,
+                           hipStream_t st) {
+  QR_DISPATCH(codec, dtype, q_dispatch, W, xs, wires, recv, L, st);
   return hipGetLastError();
 }
 
-hipError_t launch_stage1(int codec, int dtype, int W, const InPtrs& wires,
+hipError_t launch_stage1(int codec, int dtype, int W, const InPtrs& wires, bool recv,
                          uint8_t* reduced, size_t blk_lo, size_t blk_hi,
                          const Layout& L, hipStream_t st) {
   if (blk_hi <= blk_lo) return hipSuccess;
-  QR_DISPATCH(codec, dtype, s1_by_w, W, wires, reduced, blk_lo, blk_hi, L, st);
+  QR_DISPATCH(codec, dtype, s1_by_w, W, wires, recv, reduced, blk_lo, blk_hi, L, st);
   return hipGetLastError();
 }
 
@@ -885,8 +966,8 @@ hipError_t launch_dequantize(int codec, int dtype, int W, const uint8_t* wire,
 template <int D, int W>
 void oneshot_launch(const InPtrs& xs, const OutPtrs& ys, size_t n, hipStream_t st) {
   const uint32_t nc = (uint32_t)(n / 8);
-  hipLaunchKernelGGL((k_sum_fp<D, W, kStage2>), dim3(groups(nc, kThreads * kPerLane), W),
-                     dim3(kThreads), 0, st, xs, ys, 0u, nc);
+  hipLaunchKernelGGL((k_sum_fp<D, W, kStage2, false>), dim3(groups(nc, kThreads * kPerLane), W),
+                     dim3(kThreads), 0, st, xs, ys, 0u, nc, 0ull);
 }
 
 template <int D>

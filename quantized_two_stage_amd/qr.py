@@ -43,6 +43,9 @@ def _load():
     sig = {
         "qr_wire_bytes": (sz, [i32, sz]),
         "qr_sim_workspace_bytes": (sz, [i32, i32, sz]),
+        "qr_recv_bytes": (sz, [i32, i32, sz]),
+        "qr_quantize_recv": (i32, [i32, i32, i32, PP, sz, P, P]),
+        "qr_reduce_recv": (i32, [i32, i32, i32, P, sz, i32, P, P]),
         "qr_quantize": (i32, [i32, i32, P, sz, P, P]),
         "qr_dequantize": (i32, [i32, i32, P, sz, P, P]),
         "qr_quantize_ranks": (i32, [i32, i32, i32, PP, sz, PP, P]),
@@ -60,8 +63,9 @@ def _load():
 
 
 LIB = _load()
-EXPORTS = ("qr_wire_bytes", "qr_sim_workspace_bytes", "qr_quantize", "qr_dequantize",
-           "qr_quantize_ranks", "qr_reduce_stage1", "qr_gather_stage2",
+EXPORTS = ("qr_wire_bytes", "qr_sim_workspace_bytes", "qr_recv_bytes", "qr_quantize",
+           "qr_dequantize", "qr_quantize_ranks", "qr_quantize_recv", "qr_reduce_stage1",
+           "qr_reduce_recv", "qr_gather_stage2",
            "qr_allreduce_sim", "qr_allreduce_oneshot", "qr_allreduce_sim_noalloc",
            "qr_last_error")
 
@@ -137,6 +141,10 @@ def qr_sim_workspace_bytes(W, codec, n):
     return LIB.qr_sim_workspace_bytes(W, codec, n)
 
 
+def qr_recv_bytes(W, codec, n):
+    return LIB.qr_recv_bytes(W, codec, n)
+
+
 def qr_quantize(codec, x, wire, dtype=None, stream=None):
     n = _n16(x)
     _bufs(("x", [x], 2 * n), ("wire", [wire], qr_wire_bytes(codec, n)))
@@ -160,6 +168,24 @@ def qr_quantize_ranks(codec, xs, wires, dtype=None, stream=None):
     _check(LIB.qr_quantize_ranks(codec, _dtype_of(xs[0], dtype), len(xs), _ptrs(xs),
                                  _n16(xs[0]), _ptrs(wires), _stream(stream)))
     return wires
+
+
+def qr_quantize_recv(codec, xs, recv, dtype=None, stream=None):
+    """stage 0 of W ranks into one receive buffer (qr_recv_bytes bytes)"""
+    n = _n16(xs[0])
+    _bufs(("xs", xs, 2 * n), ("recv", [recv], qr_recv_bytes(len(xs), codec, n)))
+    _check(LIB.qr_quantize_recv(codec, _dtype_of(xs[0], dtype), len(xs), _ptrs(xs), n,
+                                _ptr(recv), _stream(stream)))
+    return recv
+
+
+def qr_reduce_recv(codec, W, recv, n, reduced, dtype, owner=-1, stream=None):
+    """stage 1 of W ranks from a receive buffer"""
+    _bufs(("recv", [recv], qr_recv_bytes(W, codec, n)),
+          ("reduced", [reduced], qr_wire_bytes(codec, n)))
+    _check(LIB.qr_reduce_recv(codec, dtype, W, _ptr(recv), n, owner, _ptr(reduced),
+                              _stream(stream)))
+    return reduced
 
 
 def qr_reduce_stage1(codec, wires, n, reduced, dtype, owner=-1, stream=None):
@@ -214,6 +240,11 @@ def qr_allreduce_oneshot(xs, ys, dtype=None, stream=None):
 def alloc_wire(codec, n, device="cuda"):
     """A device buffer for one wire image (padding bytes start at zero)."""
     return torch.zeros(qr_wire_bytes(codec, n), dtype=torch.uint8, device=device)
+
+
+def alloc_recv(W, codec, n, device="cuda"):
+    """A device buffer for a receive buffer (padding bytes start at zero)."""
+    return torch.zeros(qr_recv_bytes(W, codec, n), dtype=torch.uint8, device=device)
 
 
 def alloc_workspace(W, codec, n, device="cuda"):

@@ -29,6 +29,7 @@ namespace {
 struct Call {
   const char* what;
   int codec, dtype, W;
+  bool recv;
   const void* in[qr::kMaxRanks];
   const void* out[qr::kMaxRanks];
   const void* red;
@@ -65,29 +66,30 @@ extern "C" const char* hipGetErrorString(hipError_t e) {
 namespace qr {
 
 hipError_t launch_quantize(int codec, int dtype, int W, const InPtrs& xs, const OutPtrs& wires,
-                           const Layout& L, hipStream_t) {
-  Call c{"quantize", codec, dtype, W, {}, {}, nullptr, 0, 0, L.n, L.total};
+                           bool recv, const Layout& L, hipStream_t) {
+  Call c{"quantize", codec, dtype, W, recv, {}, {}, nullptr, 0, 0, L.n, L.total};
   for (int r = 0; r < W; r++) c.in[r] = xs.p[r], c.out[r] = wires.p[r];
   return record(c);
 }
-hipError_t launch_stage1(int codec, int dtype, int W, const InPtrs& wires, uint8_t* reduced,
-                         size_t blk_lo, size_t blk_hi, const Layout& L, hipStream_t) {
-  Call c{"stage1", codec, dtype, W, {}, {}, reduced, blk_lo, blk_hi, L.n, L.total};
+hipError_t launch_stage1(int codec, int dtype, int W, const InPtrs& wires, bool recv,
+                         uint8_t* reduced, size_t blk_lo, size_t blk_hi, const Layout& L,
+                         hipStream_t) {
+  Call c{"stage1", codec, dtype, W, recv, {}, {}, reduced, blk_lo, blk_hi, L.n, L.total};
   for (int r = 0; r < W; r++) c.in[r] = wires.p[r];
   if (blk_hi <= blk_lo) return hipSuccess;   // the real launcher launches nothing then
   return record(c);
 }
 hipError_t launch_dequantize(int codec, int dtype, int W, const uint8_t* wire, const OutPtrs& ys,
                              const Layout& L, hipStream_t) {
-  Call c{"stage2", codec, dtype, W, {}, {}, wire, 0, 0, L.n, L.total};
+  Call c{"stage2", codec, dtype, W, false, {}, {}, wire, 0, 0, L.n, L.total};
   for (int r = 0; r < W; r++) c.out[r] = ys.p[r];
   return record(c);
 }
 hipError_t launch_fused(int codec, int dtype, int W, const InPtrs& xs, const OutPtrs& wires,
                         uint8_t* reduced, const OutPtrs& ys, const Layout& L, hipStream_t) {
-  Call c{"fused", codec, dtype, W, {}, {}, reduced, 0, 0, L.n, L.total};
-  for (int r = 0; r < W; r++) c.in[r] = xs.p[r], c.out[r] = ys.p[r];
-  (void)wires;
+  Call c{"fused", codec, dtype, W, true, {}, {}, reduced, 0, 0, L.n, L.total};
+  for (int r = 0; r < W; r++) c.in[r] = wires.p[r], c.out[r] = ys.p[r];
+  (void)xs;
   return record(c);
 }
 int g_scratch_lookups = 0;
@@ -98,7 +100,7 @@ hipError_t scratch_address(void** p) {
 }
 hipError_t launch_oneshot(int dtype, int W, const InPtrs& xs, const OutPtrs& ys, size_t n,
                           hipStream_t) {
-  Call c{"oneshot", 0, dtype, W, {}, {}, nullptr, 0, 0, n, 0};
+  Call c{"oneshot", 0, dtype, W, false, {}, {}, nullptr, 0, 0, n, 0};
   for (int r = 0; r < W; r++) c.in[r] = xs.p[r], c.out[r] = ys.p[r];
   return record(c);
 }
@@ -112,6 +114,13 @@ void* dev(int i) { return reinterpret_cast<void*>((uintptr_t)0x7f0000000000ull +
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// one rank's tile of 256 blocks in the receive buffer, from its definition
+size_t tile_bytes(int codec) {
+  if (codec == QR_FP) return 256 * 64;
+  const size_t cb = (codec & 7) == QR_Q6 ? 24 : (codec & 7) == QR_Q4 ? 16 : 32;
+  return 256 * (cb + 2 + ((codec & 8) ? 2 : 0));
+}
+
 const int CODECS[] = {QR_FP, QR_Q8, QR_Q6, QR_Q4, QR_FP8, QR_Q8_ASYM, QR_Q6_ASYM, QR_Q4_ASYM};
 
 void sim_paths() {
@@ -124,30 +133,49 @@ void sim_paths() {
         for (int r = 0; r < W; r++) xs[r] = dev(r), ys[r] = dev(8 + r);
         void* ws = dev(20);
         const size_t need = qr_sim_workspace_bytes(W, (qr_codec)codec, n);
-        const size_t stride = align256(qr_wire_bytes((qr_codec)codec, n));
-        EXPECT(need == (size_t)(W + 1) * stride);
+        const size_t tile = tile_bytes(codec), nt = ((n + 31) / 32 + 255) / 256;
+        const size_t recv = qr_recv_bytes(W, (qr_codec)codec, n);
+        EXPECT(recv == nt * W * tile);
+        const size_t red_at = align256(recv);
+        EXPECT(need == red_at + align256(qr_wire_bytes((qr_codec)codec, n)));
         g_calls.clear();
         int rc = qr_allreduce_sim(W, QR_FP16, (qr_codec)codec, xs, ys, n, ws, need, nullptr);
         EXPECT(rc == QR_OK);
         const uint8_t* base = static_cast<const uint8_t*>(ws);
         if (2 * n <= ((size_t)4 << 20)) {
           EXPECT(g_calls.size() == 1 && strcmp(g_calls[0].what, "fused") == 0);
-          if (!g_calls.empty()) EXPECT(g_calls[0].red == base + W * stride);
+          if (!g_calls.empty()) {
+            EXPECT(g_calls[0].red == base + red_at && g_calls[0].recv);
+            for (int r = 0; r < W; r++) EXPECT(g_calls[0].in[r] == base + r * tile);
+          }
         } else {
           EXPECT(g_calls.size() == 3);
           if (g_calls.size() == 3) {
             EXPECT(strcmp(g_calls[0].what, "quantize") == 0);
             EXPECT(strcmp(g_calls[1].what, "stage1") == 0);
             EXPECT(strcmp(g_calls[2].what, "stage2") == 0);
+            EXPECT(g_calls[0].recv && g_calls[1].recv);
             for (int r = 0; r < W; r++) {
               EXPECT(g_calls[0].in[r] == xs[r]);
-              EXPECT(g_calls[0].out[r] == base + r * stride);
-              EXPECT(g_calls[1].in[r] == base + r * stride);
+              EXPECT(g_calls[0].out[r] == base + r * tile);
+              EXPECT(g_calls[1].in[r] == base + r * tile);
               EXPECT(g_calls[2].out[r] == ys[r]);
             }
-            EXPECT(g_calls[1].red == base + W * stride && g_calls[2].red == base + W * stride);
+            EXPECT(g_calls[1].red == base + red_at && g_calls[2].red == base + red_at);
             EXPECT(g_calls[1].lo == 0 && g_calls[1].hi == (n + 31) / 32);
           }
+        }
+        // the staged calls through a receive buffer launch the same kernels
+        g_calls.clear();
+        EXPECT(qr_quantize_recv((qr_codec)codec, QR_FP16, W, xs, n, (void*)base, nullptr) == QR_OK);
+        EXPECT(qr_reduce_recv((qr_codec)codec, QR_FP16, W, base, n, -1, (void*)(base + red_at),
+                              nullptr) == QR_OK);
+        EXPECT(g_calls.size() == 2);
+        if (g_calls.size() == 2) {
+          EXPECT(g_calls[0].recv && g_calls[1].recv);
+          for (int r = 0; r < W; r++)
+            EXPECT(g_calls[0].out[r] == base + r * tile && g_calls[1].in[r] == base + r * tile);
+          EXPECT(g_calls[1].lo == 0 && g_calls[1].hi == (n + 31) / 32);
         }
         for (const Call& c : g_calls) EXPECT(c.n == n && c.W == W && c.codec == codec);
       }
@@ -166,12 +194,13 @@ void owner_ranges() {
       for (int j = 0; j < W; j++) {
         g_calls.clear();
         EXPECT(qr_reduce_stage1(QR_Q4, QR_FP16, W, wires, n, j, dev(9), nullptr) == QR_OK);
+        EXPECT(qr_reduce_recv(QR_Q4, QR_FP16, W, dev(0), n, j, dev(9), nullptr) == QR_OK);
         size_t lo = j * bpc < nb ? j * bpc : nb, hi = lo + bpc < nb ? lo + bpc : nb;
         if (lo == hi) {
           EXPECT(g_calls.empty());
         } else {
-          EXPECT(g_calls.size() == 1);
-          if (g_calls.size() == 1) EXPECT(g_calls[0].lo == lo && g_calls[0].hi == hi);
+          EXPECT(g_calls.size() == 2);
+          for (const Call& c : g_calls) EXPECT(c.lo == lo && c.hi == hi);
           covered += hi - lo;
         }
       }
@@ -208,6 +237,16 @@ void rejections() {
       {qr_gather_stage2(QR_Q4, QR_FP16, 0, xs[0], n, ys, nullptr), QR_ERR_UNSUPPORTED},
       {qr_allreduce_oneshot(5, QR_FP16, xs, ys, n, nullptr), QR_ERR_UNSUPPORTED},
       {qr_quantize(QR_Q4, QR_FP16, xs[0], n, (uint8_t*)xs[0] + 16, nullptr), QR_ERR_ARG},
+      {qr_quantize_recv(QR_Q4, QR_FP16, 3, xs, n, dev(20), nullptr), QR_ERR_UNSUPPORTED},
+      {qr_quantize_recv(QR_Q4, QR_FP16, 2, xs, n, (uint8_t*)xs[1] + 256, nullptr), QR_ERR_ARG},
+      {qr_quantize_recv(QR_Q4, QR_FP16, 2, xs, n, (uint8_t*)dev(20) + 8, nullptr), QR_ERR_ALIGN},
+      {qr_quantize_recv(QR_Q4, QR_FP16, 2, nullptr, n, dev(20), nullptr), QR_ERR_ARG},
+      {qr_reduce_recv(QR_Q4, QR_FP16, 2, dev(20), n, 2, dev(21), nullptr), QR_ERR_ARG},
+      {qr_reduce_recv(QR_Q4, QR_FP16, 4, dev(20), n, -1, (uint8_t*)dev(20) + 4096, nullptr),
+       QR_ERR_ARG},                                   // reduced image inside the buffer
+      {qr_reduce_recv(QR_Q4, QR_FP16, 8, dev(20), 12, -1, dev(21), nullptr), QR_ERR_SIZE},
+      {qr_reduce_recv((qr_codec)4, QR_FP16, 2, dev(20), n, -1, dev(21), nullptr),
+       QR_ERR_UNSUPPORTED},
       {qr_dequantize(QR_Q4, QR_FP16, xs[0], n, (uint8_t*)ys[0] + 4, nullptr), QR_ERR_ALIGN},
   };
   g_calls.clear();
@@ -220,6 +259,10 @@ void rejections() {
   EXPECT(qr_wire_bytes(QR_FP, nmax) == 2 * nmax);
   EXPECT(qr_wire_bytes(QR_Q8_ASYM, nmax) == align256(align256(nmax) + nmax / 16) + nmax / 16);
   EXPECT(qr_sim_workspace_bytes(8, QR_FP, nmax) == 9 * 2 * nmax);
+  EXPECT(qr_recv_bytes(8, QR_FP, nmax) == 8 * 2 * nmax);
+  EXPECT(qr_recv_bytes(8, QR_Q8_ASYM, nmax) == (nmax / 32 / 256) * 8 * 256 * 36);
+  EXPECT(qr_recv_bytes(9, QR_Q4, 8) == 0 && qr_recv_bytes(0, QR_Q4, 8) == 0);
+  EXPECT(qr_recv_bytes(1, QR_Q4, 8) == 256 * 18);
 }
 
 void failed_launch() {
@@ -249,7 +292,7 @@ void noalloc_paths() {
         void* ys[8];
         for (int r = 0; r < W; r++) xs[r] = dev(r), ys[r] = dev(8 + r);
         const size_t need = qr_sim_workspace_bytes(W, (qr_codec)codec, n);
-        const size_t stride = align256(qr_wire_bytes((qr_codec)codec, n));
+        const size_t red_at = align256(qr_recv_bytes(W, (qr_codec)codec, n));
         g_calls.clear();
         const int before = qr::g_scratch_lookups;
         int rc = qr_allreduce_sim_noalloc(W, QR_FP16, (qr_codec)codec, xs, ys, n, nullptr);
@@ -264,9 +307,9 @@ void noalloc_paths() {
         EXPECT(qr_allreduce_sim(W, QR_FP16, (qr_codec)codec, xs, ys, n, (void*)base, need,
                                 nullptr) == QR_OK);
         EXPECT(mine.size() == g_calls.size());
-        EXPECT(!mine.empty() && mine.back().red == base + W * stride);
+        EXPECT(!mine.empty() && mine.back().red == base + red_at);
         for (size_t i = 0; i < mine.size() && i < g_calls.size(); i++) {
-          EXPECT(strcmp(mine[i].what, g_calls[i].what) == 0);
+          EXPECT(strcmp(mine[i].what, g_calls[i].what) == 0 && mine[i].recv == g_calls[i].recv);
           EXPECT(mine[i].red == g_calls[i].red);
           EXPECT(mine[i].lo == g_calls[i].lo && mine[i].hi == g_calls[i].hi);
           for (int r = 0; r < W; r++)

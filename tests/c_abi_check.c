@@ -126,6 +126,26 @@ static void run_case(int W, int codec, int dtype, size_t n, int staged, uint64_t
       CK(hipMemcpy(hy[r], dy[r], 2 * n, hipMemcpyDeviceToHost));
       expect_equal(hy[r], want[r], n, "staged", W, codec, dtype, r);
     }
+    /* the same through a receive buffer, stage 1 owner by owner */
+    void* recv;
+    CK(hipMalloc(&recv, qr_recv_bytes(W, (qr_codec)codec, n)));
+    for (int r = 0; r < W; r++) CK(hipMemset(dy[r], 0, 2 * n));
+    rc = qr_quantize_recv((qr_codec)codec, (qr_dtype)dtype, W, (const void* const*)dx, n, recv,
+                          NULL);
+    for (int j = 0; j < W && rc == QR_OK; j++)
+      rc = qr_reduce_recv((qr_codec)codec, (qr_dtype)dtype, W, recv, n, j, red, NULL);
+    if (rc == QR_OK)
+      rc = qr_gather_stage2((qr_codec)codec, (qr_dtype)dtype, W, red, n, (void* const*)dy, NULL);
+    if (rc != QR_OK) {
+      printf("receive-buffer call returned %d: %s\n", rc, qr_last_error());
+      failures++;
+    }
+    CK(hipDeviceSynchronize());
+    for (int r = 0; r < W; r++) {
+      CK(hipMemcpy(hy[r], dy[r], 2 * n, hipMemcpyDeviceToHost));
+      expect_equal(hy[r], want[r], n, "recv", W, codec, dtype, r);
+    }
+    CK(hipFree(recv));
     for (int r = 0; r < W; r++) CK(hipFree(wires[r]));
     CK(hipFree(red));
   }

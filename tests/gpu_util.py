@@ -142,3 +142,62 @@ def sample_windows(nb, count=12, width=64, seed=0):
     if nb > w:
         starts.update(int(s) for s in g.integers(0, nb - w, count))
     return sorted((s, s + w) for s in starts)
+
+
+def recv_tile_bytes(codec):
+    """bytes of one rank's tile of 256 blocks in the receive buffer: the
+    tile's codes, scales (and zeros); FP: 256 blocks of raw 16-bit data"""
+    if codec == O.FP:
+        return 256 * 64
+    return 256 * (O.block_code_bytes(codec) + 2 + (2 if codec & 8 else 0))
+
+
+def recv_regions(codec, n, W):
+    """(offset in the receive buffer, rank, start, end in the rank's planar
+    wire image) of every defined byte range, from the layout's definition:
+    tile t of rank r starts at (t*W + r) * T and holds blocks [256t, 256t+256)
+    of that rank: their codes, then their scales, then their zeros"""
+    nb = (n + 31) // 32
+    T = recv_tile_bytes(codec)
+    out = []
+    for t in range((nb + 255) // 256):
+        b0, b1 = 256 * t, min(nb, 256 * t + 256)
+        for r in range(W):
+            base = (t * W + r) * T
+            if codec == O.FP:
+                out.append((base, r, 64 * b0, min(2 * n, 64 * b1)))
+                continue
+            cb = O.block_code_bytes(codec)
+            out.append((base, r, cb * b0, cb * b1))
+            so = O.scale_offset(codec, n)
+            out.append((base + 256 * cb, r, so + 2 * b0, so + 2 * b1))
+            if codec & 8:
+                zo = O.zero_offset(codec, n)
+                out.append((base + 256 * (cb + 2), r, zo + 2 * b0, zo + 2 * b1))
+    return out
+
+
+def recv_from_wires(codec, n, wires, fill=0):
+    """the receive buffer holding W planar wire images (numpy), with the
+    mask of its defined bytes; padding bytes hold `fill`"""
+    W = len(wires)
+    nb = (n + 31) // 32
+    size = ((nb + 255) // 256) * W * recv_tile_bytes(codec)
+    buf = np.full(size, fill, np.uint8)
+    mask = np.zeros(size, bool)
+    for dst, r, a, e in recv_regions(codec, n, W):
+        buf[dst:dst + e - a] = wires[r][a:e]
+        mask[dst:dst + e - a] = True
+    return buf, mask
+
+
+def assert_recv_equal(got, wires, codec, n, what, fill=None):
+    """a receive buffer against W planar wire images: every defined byte
+    equal; with `fill`, every padding byte still holds it"""
+    want, mask = recv_from_wires(codec, n, wires)
+    got = np.asarray(got)
+    assert got.size == want.size, (what, got.size, want.size)
+    assert_bytes_equal(got[mask], want[mask], what)
+    if fill is not None:
+        assert np.all(got[~mask] == fill), (what, "receive-buffer padding written")
+

@@ -27,7 +27,9 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ("qr_quantize", "qr_dequantize", "qr_reduce_stage1", "qr_gather_stage2",
                  "qr_allreduce_sim", "qr_wire_bytes", "qr_sim_workspace_bytes",
-                 "qr_last_error", "qr_quantize_ranks", "qr_allreduce_oneshot"):
+                 "qr_last_error", "qr_quantize_ranks", "qr_allreduce_oneshot",
+                 "qr_recv_bytes", "qr_quantize_recv", "qr_reduce_recv",
+                 "qr_allreduce_sim_noalloc"):
         assert must in names
 
 
@@ -53,7 +55,12 @@ def test_wire_bytes_matches_definition():
     assert qr.qr_wire_bytes(qr.QR_Q4_ASYM, 2048) == 1408
     assert qr.qr_wire_bytes(qr.QR_Q4, 40) == 260
     assert qr.qr_wire_bytes(4, 2048) == 0                     # NONE is not a codec
-    assert qr.qr_sim_workspace_bytes(2, qr.QR_Q8, 2048) == 3 * 2304
+    # receive buffer: one tile of 256 blocks per rank (256 * (32 + 2) bytes),
+    # then the reduced image at the next 256-byte boundary
+    assert qr.qr_recv_bytes(2, qr.QR_Q8, 2048) == 2 * 256 * 34
+    assert qr.qr_recv_bytes(8, qr.QR_Q4_ASYM, n) == (n // 32 // 256) * 8 * 256 * 20
+    assert qr.qr_recv_bytes(4, qr.QR_FP, 8192 * 3 + 8) == 4 * 4 * 256 * 64
+    assert qr.qr_sim_workspace_bytes(2, qr.QR_Q8, 2048) == 2 * 256 * 34 + 2304
     assert qr.qr_sim_workspace_bytes(3, qr.QR_Q8, 2048) == 0
 
 

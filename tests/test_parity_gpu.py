@@ -10,8 +10,9 @@ import torch
 
 import oracle as O
 import pins
-from gpu_util import (assert_bytes_equal, assert_within_ulp, dev16, gpu_staged, host16,
-                      hostu8, oracle_staged, plane_slices, say)
+from gpu_util import (assert_bytes_equal, assert_recv_equal, assert_within_ulp, dev16,
+                      gpu_staged, host16, hostu8, oracle_staged, plane_slices, recv_from_wires,
+                      recv_regions, say)
 from quantized_two_stage_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -53,20 +54,29 @@ def _check_case(qr, codec, dtype, xs_np, label):
     torch.cuda.synchronize()
     for r in range(W):
         assert_within_ulp(host16(ys2[r]), r_ys[r], dtype, "%s sim y[%d]" % (label, r))
-    # the workspace holds the W wire images and the reduced image (whichever
-    # launch path the call took), and the padding between planes is untouched
+    # the workspace holds the receive buffer and the reduced image (whichever
+    # launch path the call took), and no padding byte is written
     wb = qr.qr_wire_bytes(codec, n)
-    stride = (wb + 255) // 256 * 256
+    rb = qr.qr_recv_bytes(W, codec, n)
+    red_at = (rb + 255) // 256 * 256
     wsh = hostu8(ws)
-    planes = plane_slices(codec, n)
-    for r in range(W + 1):
-        img = wsh[r * stride:r * stride + wb]
-        want = r_wires[r] if r < W else r_red
-        keep = np.ones(wb, bool)
-        for name, (a, e) in planes.items():
-            assert_bytes_equal(img[a:e], want[a:e], "%s sim workspace %d %s" % (label, r, name))
-            keep[a:e] = False
-        assert np.all(img[keep] == 0xA7), (label, "workspace padding written", r)
+    assert_recv_equal(wsh[:rb], r_wires, codec, n, "%s sim receive buffer" % label, fill=0xA7)
+    assert np.all(wsh[rb:red_at] == 0xA7), (label, "workspace padding written")
+    img = wsh[red_at:red_at + wb]
+    keep = np.ones(wb, bool)
+    for name, (a, e) in plane_slices(codec, n).items():
+        assert_bytes_equal(img[a:e], r_red[a:e], "%s sim workspace reduced %s" % (label, name))
+        keep[a:e] = False
+    assert np.all(img[keep] == 0xA7), (label, "workspace padding written (reduced)")
+    # the staged calls through a receive buffer: stage 0 writes it as the
+    # layout says, stage 1 reads it back into the same reduced image
+    recv = torch.full((qr.qr_recv_bytes(W, codec, n),), 0xA7, dtype=torch.uint8, device="cuda")
+    qr.qr_quantize_recv(codec, xs, recv, dtype=dtype)
+    red2 = qr.alloc_wire(codec, n)
+    qr.qr_reduce_recv(codec, W, recv, n, red2, dtype)
+    torch.cuda.synchronize()
+    assert_recv_equal(hostu8(recv), r_wires, codec, n, "%s receive buffer" % label, fill=0xA7)
+    assert_bytes_equal(hostu8(red2), r_red, "%s reduced from the receive buffer" % label)
     # inputs are never modified
     for r in range(W):
         assert np.array_equal(host16(xs[r]), xs_np[r]), label
@@ -254,6 +264,19 @@ def test_owner_chunks(qr, W):
             acc |= part
         torch.cuda.synchronize()
         assert_bytes_equal(hostu8(acc), hostu8(full), "union of owners")
+        # the same owners from a receive buffer
+        recv = qr.alloc_recv(W, codec, n)
+        qr.qr_quantize_recv(codec, xs, recv, dtype=O.FP16)
+        acc2 = qr.alloc_wire(codec, n)
+        for j in range(W):
+            part = qr.alloc_wire(codec, n)
+            qr.qr_reduce_recv(codec, W, recv, n, part, O.FP16, owner=j)
+            torch.cuda.synchronize()
+            want = O.stage1(codec, O.FP16, [hostu8(w) for w in wires], n, *O.chunk(W, n, j))
+            assert_bytes_equal(hostu8(part), want, "owner %d from the receive buffer" % j)
+            acc2 |= part
+        torch.cuda.synchronize()
+        assert_bytes_equal(hostu8(acc2), hostu8(full), "union of owners (receive buffer)")
 
 
 def _random_wire(codec, n, g):
@@ -309,11 +332,17 @@ def test_stage1_any_wire(qr, W):
         red = qr.alloc_wire(codec, n)
         qr.qr_reduce_stage1(codec, wires, n, red, O.FP16)
         torch.cuda.synchronize()
+        # the same bytes through a receive buffer
+        rbuf, _ = recv_from_wires(codec, n, imgs)
+        recv = torch.from_numpy(rbuf).cuda()
+        red2 = qr.alloc_wire(codec, n)
+        qr.qr_reduce_recv(codec, W, recv, n, red2, O.FP16)
+        torch.cuda.synchronize()
         want = O.stage1(codec, O.FP16, imgs, n)
-        got = hostu8(red)
-        for name, (a, e) in plane_slices(codec, n).items():
-            assert_bytes_equal(got[a:e], want[a:e], "stage1 any wire %s W%d %s" % (
-                I.CODEC_NAMES[codec], W, name))
+        for got, how in ((hostu8(red), "wires"), (hostu8(red2), "receive buffer")):
+            for name, (a, e) in plane_slices(codec, n).items():
+                assert_bytes_equal(got[a:e], want[a:e], "stage1 any wire (%s) %s W%d %s" % (
+                    how, I.CODEC_NAMES[codec], W, name))
 
 
 @pytest.mark.parametrize("dtype", (O.FP16, O.BF16), ids=("fp16", "bf16"))
@@ -434,12 +463,13 @@ def test_sim_guard_bands(qr):
                 torch.cuda.synchronize()
                 h = hostu8(big_ws)
                 assert np.all(h[:G] == 0xA5) and np.all(h[G + need:] == 0xA5), (codec, W, n)
-                wb = qr.qr_wire_bytes(codec, n)
-                stride = (wb + 255) // 256 * 256
+                rb = qr.qr_recv_bytes(W, codec, n)
+                red_at = (rb + 255) // 256 * 256
                 inner = h[G:G + need].copy()
-                for r in range(W + 1):
-                    for a, e in plane_slices(codec, n).values():
-                        inner[r * stride + a:r * stride + e] = 0xA5
+                for dst, r, a, e in recv_regions(codec, n, W):
+                    inner[dst:dst + e - a] = 0xA5
+                for a, e in plane_slices(codec, n).values():
+                    inner[red_at + a:red_at + e] = 0xA5
                 assert np.all(inner == 0xA5), ("workspace padding written", codec, W, n)
                 want = O.allreduce(codec, O.FP16, xs_np)
                 for r, b in enumerate(big_y):
