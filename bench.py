@@ -1,30 +1,32 @@
 """Benchmark of the simulated two-stage quantized allreduce on one MI355X.
 
-One step = one simulated allreduce per codec of the 64 MB workload (W=2
-ranks, fp16, 32Mi elements per rank, N(0,1) with 0.1% x50 outliers; codecs
-FP, fp8, Q8, Q6, Q4 symmetric), each as its three launches: quantize all
-ranks, fused stage 1, stage 2 -- exactly the launches qr_allreduce_sim makes.
-Inputs are resident in HBM before the timed region starts.
+Workload (default): W=8 simulated ranks, fp16, 64 MB (32 Mi elements) per
+rank buffer, every codec (FP, fp8, Q8, Q6, Q4 symmetric, Q8, Q6, Q4
+asymmetric); 32-element blocks cycling N(0,1) with all-zero, constant,
+single-spike and +-max-finite blocks.  One step = one simulated allreduce per
+codec (qr_allreduce_sim: quantize into the receive buffer, fused stage 1,
+stage 2), eight allreduces.  Inputs are resident in HBM before the timed
+region starts.
 
-Two passes of the same K steps:
-  1. the timed region: each allreduce is one qr_allreduce_sim call (its
-     three launches), nothing else on the stream; `value` and `ms_per_step`
-     come from this pass.
-  2. the instrumented pass: each allreduce as the three staged calls with a
-     HIP event recorded on the launch stream before and after every launch;
-     the per-kernel durations and the roofline come from this pass (an event
-     record between two launches costs the GPU about 2 us, which is why it
-     is kept out of pass 1).
+Passes, in order:
+  1. the timed region: K steps, nothing but the qr_allreduce_sim calls on the
+     stream; `value` (per-rank payload bytes 2n per allreduce, over the step
+     time) and `ms_per_step` come from it;
+  2. the instrumented pass: the same K steps as the three staged calls with a
+     HIP event on the launch stream before and after every launch: the
+     in-pipeline duration of every kernel;
+  3. cold launches: each stage of each codec alone after reading 1 GiB of
+     other data (L2 and the 256 MB Infinity Cache hold none of its bytes),
+     beside the same-bytes references: the stage-1 access pattern without
+     the arithmetic (libqr_pattern.so) and a plain device copy.
 
-Prints one JSON line: effective GB/s = per-rank payload bytes (2n per
-allreduce) / time, per step over all codecs; per-codec microseconds and
-GB/s; per-kernel durations; the roofline of the kernel that takes the most
-time; a cold-cache measurement of stage 1; beside every kernel figure, a
-plain device copy that moves the same number of bytes (`copy_us`, and
-`vs_copy` = copy time / kernel time), the achievable reference at that size;
-and the CPU oracle timed on a bounded sample.  Unless --no-extra: the other workloads (W=8, the bf16
-workload with and without the cast option, and size sweeps from 4 KB to
-64 MB per rank buffer).
+`roofline` is stage 1 (the fused dequantize-sum-requantize kernel), cold: its
+algorithmic bytes per launch, (W+1) * wire bytes, over its event-timed
+duration; `frac` is the lowest over the eight codecs, each codec's figure and
+its access-pattern ceiling beside it.  `cpu_baseline` times the CPU oracle on
+a bounded sample of the same workload.  The one JSON line on stdout carries
+the contract fields and compact per-codec figures; --extra PATH writes the
+other workloads, the size sweeps and the minimum-size table to a file.
 """
 import argparse
 import hashlib
@@ -43,21 +45,25 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "effective GB/s and μs per simulated allreduce, 4KB–64MB, W=2/4/8, per codec"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_two_stage_amd", "csrc", f)
-                  for f in ("qr_kernels.hip", "qr_device.h")]
+                  for f in ("qr_kernels.hip", "qr_device.h", "qr_stage_io.h")]
+STAGES = ("quantize", "stage1", "stage2")
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", type=int, default=2)
-    p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=1 << 25,
-                   help="elements per rank of the oracle's sample")
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=5)
+    p.add_argument("--cold-reps", type=int, default=7)
     p.add_argument("--no-cold", action="store_true")
-    p.add_argument("--no-extra", action="store_true",
-                   help="skip the other workloads (size sweeps, W=8)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=1 << 21,
+                   help="elements per rank of the oracle's sample")
+    p.add_argument("--extra", metavar="PATH",
+                   help="also measure the other workloads, the size sweeps and the "
+                        "minimum-size table, written as JSON to PATH")
+    p.add_argument("--sweep-repeats", type=int, default=3)
     return p.parse_args()
 
 
@@ -78,13 +84,20 @@ def kernel_source_sha():
 def algorithmic_bytes(stage, W, n, wb):
     """bytes the method must move per launch (W ranks, n elements each, wire
     image wb bytes): quantize reads 2n and writes wb per rank; stage 1 reads
-    W wire images and writes one; stage 2 reads the reduced image and writes
-    2n per rank."""
+    W wire images and writes one; stage 2 reads the reduced image once per
+    rank and writes 2n per rank."""
     if stage == "quantize":
         return W * (2 * n + wb)
     if stage == "stage1":
         return (W + 1) * wb
     return W * (wb + 2 * n)
+
+
+def hbm_bytes_stage2(W, n, wb):
+    """stage 2's HBM floor in this simulation: the one reduced image is read
+    once from HBM (the W simulated ranks' re-reads hit the caches) and the W
+    outputs are written"""
+    return wb + W * 2 * n
 
 
 class HipEvents:
@@ -129,36 +142,62 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-_COPY_US = {}
+class Pattern:
+    """libqr_pattern.so: stage 1's loads and stores without the arithmetic"""
+
+    def __init__(self):
+        import ctypes
+        from quantized_two_stage_amd import build as qbuild
+        if not os.path.exists(qbuild.PATTERN_LIB):
+            raise ImportError("libqr_pattern.so is not built (%s)" % qbuild.PATTERN_LIB)
+        self.L = ctypes.CDLL(qbuild.PATTERN_LIB)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        self.L.qrp_stage1_pattern.argtypes = [i32, i32, P, sz, P, P]
+        self.L.qrp_stage1_pattern.restype = i32
+        self.ct = ctypes
+
+    def stage1(self, codec, W, recv, n, red, stream):
+        rc = self.L.qrp_stage1_pattern(codec, W, self.ct.c_void_p(recv.data_ptr()), n,
+                                       self.ct.c_void_p(red.data_ptr()),
+                                       self.ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("qrp_stage1_pattern failed (%d)" % rc)
 
 
-def copy_same_bytes_us(torch, stream, nbytes, flush=None):
-    """Median microseconds of a plain device-to-device copy (torch's copy_)
-    that moves `nbytes` in all: nbytes/2 read and nbytes/2 written.  The
-    achievable reference for a kernel whose algorithmic bytes are nbytes.
-    With `flush` (a 1 GiB tensor), L2 and the Infinity Cache are flushed
-    before each copy, as before a cold kernel."""
-    key = (nbytes, flush is not None)
-    if key not in _COPY_US:
-        half = (nbytes // 2 + 15) // 16 * 16
-        src = torch.ones(half, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        ev = HipEvents(2)
+class Cold:
+    """Cold launches: before each, a read of 1 GiB of other data evicts L2 and
+    the Infinity Cache without leaving dirty lines; the launch alone is
+    bracketed by HIP events; the median of `reps` launches."""
+
+    def __init__(self, torch, stream, reps):
+        self.torch, self.stream, self.reps = torch, stream, reps
+        self.flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        self.ev = HipEvents(2)
+
+    def us(self, fn, reps=None):
         ts = []
-        for _ in range(7):
-            if flush is not None:
-                flush.sum()
-            ev.record(0, stream)
-            dst.copy_(src)
-            ev.record(1, stream)
-            torch.cuda.synchronize()
-            ts.append(ev.ms(0, 1) * 1e3)
-        ev.close()
+        for _ in range(reps or self.reps):
+            self.flush.sum()
+            self.ev.record(0, self.stream)
+            fn()
+            self.ev.record(1, self.stream)
+            self.torch.cuda.synchronize()
+            ts.append(self.ev.ms(0, 1) * 1e3)
+        return float(np.median(ts))
+
+    def copy_us(self, nbytes):
+        """a plain device copy moving nbytes in all (half read, half written)"""
+        half = (nbytes // 2 + 15) // 16 * 16
+        src = self.torch.ones(half, dtype=self.torch.uint8, device="cuda")
+        dst = self.torch.empty_like(src)
+        dst.copy_(src)
+        t = self.us(lambda: dst.copy_(src))
         del src, dst
-        _COPY_US[key] = float(np.median(ts))
-    return _COPY_US[key]
+        return t
+
+    def close(self):
+        self.ev.close()
+        del self.flush
 
 
 SPIN_CYCLES = 400000      # ~0.2 ms of GPU clock: longer than the host needs to enqueue a call
@@ -184,204 +223,167 @@ def time_each(fn, iters, stream):
     return us
 
 
-def measure_workload(qr, I, torch, stream, config, n=None, codecs=None, iters=20,
-                     kernels=True, cold=True, oneshot=True, dtype=None):
-    """One workload of inputs.CONFIGS: per codec, the simulated allreduce
-    (qr_allreduce_sim) timed call by call (median and min us, effective GB/s
-    = 2n bytes / time); optionally the three kernels timed one by one through
-    the staged calls (us, algorithmic GB/s, fraction of HBM peak) and stage 1
-    after a cache flush; and the one-stage allreduce (qr_allreduce_oneshot,
-    key "1stage"), whose algorithmic bytes are W*(W+1)*2n: every rank reads
-    the W buffers and writes its own."""
-    cfg = I.CONFIGS[config]
-    W = cfg["W"]
-    dtype = cfg["dtype"] if dtype is None else dtype
-    n = cfg["n"] if n is None else n
-    codecs = cfg["codecs"] if codecs is None else codecs
-    xs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in I.make(config, n=n)]
+def frac(nbytes, us):
+    return nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS
+
+
+# ---------------------------------------------------------------------------
+# the headline workload
+
+def measure_headline(args, qr, I, torch, stream, log):
+    cfg = I.CONFIGS[args.config]
+    W, n, dtype, codecs = cfg["W"], cfg["n"], cfg["dtype"], cfg["codecs"]
+    log("bench: config %d (%s), generating inputs" % (args.config, cfg["desc"]))
+    xs_np = I.make(args.config)
+    xs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in xs_np]
     ys = [torch.empty_like(xs[0]) for _ in range(W)]
-    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda") if cold else None
-    out = {}
+    bufs = {}
     for c in codecs:
-        wb = qr.qr_wire_bytes(c, n)
-        ws = qr.alloc_workspace(W, c, n)
-        for _ in range(3):
-            qr.qr_allreduce_sim(c, xs, ys, ws, dtype=dtype)
-        us = time_each(lambda: qr.qr_allreduce_sim(c, xs, ys, ws, dtype=dtype), iters, stream)
-        med = float(np.median(us))
-        r = {"us_median": med, "us_min": float(min(us)),
-             "effective_gbps": 2 * n / (med * 1e-6) / 1e9}
-        if kernels or cold:
-            wires = [qr.alloc_wire(c, n) for _ in range(W)]
-            red = qr.alloc_wire(c, n)
-            launches = {
-                "quantize": lambda: qr.qr_quantize_ranks(c, xs, wires, dtype=dtype),
-                "stage1": lambda: qr.qr_reduce_stage1(c, wires, n, red, dtype),
-                "stage2": lambda: qr.qr_gather_stage2(c, red, ys, dtype=dtype)}
-            for f in launches.values():
-                f()
-        if kernels:
-            r["kernels"] = {}
-            for st, f in launches.items():
-                t = float(np.median(time_each(f, iters, stream)))
-                ab = algorithmic_bytes(st, W, n, wb)
-                cu = copy_same_bytes_us(torch, stream, ab)
-                r["kernels"][st] = {"us": t, "gbps": ab / (t * 1e-6) / 1e9,
-                                    "frac": ab / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-                                    "copy_us": cu, "vs_copy": cu / t}
-        if cold:
-            ts = []
-            launches["quantize"]()
-            for _ in range(5):
-                flush.sum()
-                ts += time_each(launches["stage1"], 1, stream)
-            t = float(np.median(ts))
-            ab = algorithmic_bytes("stage1", W, n, wb)
-            cu = copy_same_bytes_us(torch, stream, ab, flush)
-            r["stage1_cold"] = {"us": t, "gbps": ab / (t * 1e-6) / 1e9,
-                                "frac": ab / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-                                "copy_us": cu, "vs_copy": cu / t}
-        if kernels or cold:
-            del wires, red
-        del ws
-        out[I.CODEC_NAMES[c]] = r
-    if oneshot:
-        # the one-stage allreduce: one launch; every simulated rank reads all
-        # W buffers and writes its own output
-        for _ in range(3):
-            qr.qr_allreduce_oneshot(xs, ys, dtype=dtype)
-        us = time_each(lambda: qr.qr_allreduce_oneshot(xs, ys, dtype=dtype), iters, stream)
-        med = float(np.median(us))
-        ab = W * (W + 1) * 2 * n
-        out["1stage"] = {"us_median": med, "us_min": float(min(us)),
-                         "effective_gbps": 2 * n / (med * 1e-6) / 1e9,
-                         "kernels": {"oneshot": {"us": med, "gbps": ab / (med * 1e-6) / 1e9,
-                                                 "frac": ab / (med * 1e-6) / 1e9 /
-                                                 HBM_PEAK_GBPS}}}
-    del xs, ys, flush
-    torch.cuda.empty_cache()
-    return out
+        bufs[c] = dict(ws=qr.alloc_workspace(W, c, n), recv=qr.alloc_recv(W, c, n),
+                       red=qr.alloc_wire(c, n), wb=qr.qr_wire_bytes(c, n))
 
+    def staged(c, ev=None, base=0):
+        b = bufs[c]
+        if ev is not None:
+            ev.record(base, stream)
+        qr.qr_quantize_recv(c, xs, b["recv"], dtype=dtype)
+        if ev is not None:
+            ev.record(base + 1, stream)
+        qr.qr_reduce_recv(c, W, b["recv"], n, b["red"], dtype)
+        if ev is not None:
+            ev.record(base + 2, stream)
+        qr.qr_gather_stage2(c, b["red"], ys, dtype=dtype)
+        if ev is not None:
+            ev.record(base + 3, stream)
 
-def measure_stage1_sizes(qr, I, torch, stream, sizes=(1 << 25, 1 << 27, 1 << 29), reps=5):
-    """Stage 1 alone, cold, at W=2 and fp16 for growing rank buffers (64 MB,
-    256 MB and 1 GiB per rank), every codec of the W=2 workload: the kernel's
-    fraction of HBM peak once the transfer is large enough that launch ramp
-    and drain no longer dominate.  Rank buffers larger than the workload's
-    64 MB repeat its seeded buffers; stage 1's time does not depend on the
-    values.  Beside each figure, a cold device copy of the same bytes."""
-    cfg = I.CONFIGS[2]
-    W, codecs = cfg["W"], cfg["codecs"]
-    base = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in I.make(2)]
-    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
-    out = {}
-    for n in sizes:
-        xs = [b.repeat((n + b.numel() - 1) // b.numel())[:n].contiguous() for b in base]
-        per = {}
+    # the staged calls give what the one-call entry point gives
+    ys_ref = [torch.empty_like(xs[0]) for _ in range(W)]
+    for c in codecs:
+        qr.qr_allreduce_sim(c, xs, ys_ref, bufs[c]["ws"], dtype=dtype)
+        staged(c)
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(ys, ys_ref)), ("staged != one call", c)
+    del ys_ref
+
+    for _ in range(args.warmup):
         for c in codecs:
-            wb = qr.qr_wire_bytes(c, n)
-            wires = [qr.alloc_wire(c, n) for _ in range(W)]
-            red = qr.alloc_wire(c, n)
-            qr.qr_quantize_ranks(c, xs, wires, dtype=I.FP16)
-            qr.qr_reduce_stage1(c, wires, n, red, I.FP16)
-            ev = HipEvents(2)
-            ts = []
-            for _ in range(reps):
-                flush.sum()
-                ev.record(0, stream)
-                qr.qr_reduce_stage1(c, wires, n, red, I.FP16)
-                ev.record(1, stream)
-                torch.cuda.synchronize()
-                ts.append(ev.ms(0, 1) * 1e3)
-            ev.close()
-            t = float(np.median(ts))
-            ab = algorithmic_bytes("stage1", W, n, wb)
-            cu = copy_same_bytes_us(torch, stream, ab, flush)
-            per[I.CODEC_NAMES[c]] = {"us": t, "algorithmic_bytes": ab,
-                                     "gbps": ab / (t * 1e-6) / 1e9,
-                                     "frac": ab / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-                                     "copy_us": cu, "vs_copy": cu / t}
-            del wires, red
-            torch.cuda.empty_cache()
-        out["%d" % (2 * n)] = per
-        del xs
-    del base, flush
-    torch.cuda.empty_cache()
-    return out
+            qr.qr_allreduce_sim(c, xs, ys, bufs[c]["ws"], dtype=dtype)
+    torch.cuda.synchronize()
 
+    # pass 1: the timed region
+    log("bench: timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for c in codecs:
+            qr.qr_allreduce_sim(c, xs, ys, bufs[c]["ws"], dtype=dtype)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
-SWEEP_SIZES = tuple(2 ** k for k in range(11, 26))      # elements: 4 KB .. 64 MB per rank
+    # pass 2: the same steps, staged, with events around every launch
+    nc = len(codecs)
+    evs = HipEvents(4 * nc * args.steps)
+    log("bench: instrumented pass, %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for s in range(args.steps):
+        for ci, c in enumerate(codecs):
+            staged(c, evs, 4 * (s * nc + ci))
+    torch.cuda.synchronize()
+    ms_instr = (time.perf_counter() - t1) * 1e3 / args.steps
+    per = {}
+    for ci, c in enumerate(codecs):
+        d = np.array([[evs.ms(4 * (s * nc + ci) + k, 4 * (s * nc + ci) + k + 1)
+                       for k in range(3)] for s in range(args.steps)]) * 1e3     # us
+        wb = bufs[c]["wb"]
+        per[c] = {"us_per_allreduce": float(d.sum(axis=1).mean()),
+                  "kernels": {st: {"us": float(d[:, k].mean()),
+                                   "frac": frac(algorithmic_bytes(st, W, n, wb), d[:, k].mean())}
+                              for k, st in enumerate(STAGES)}}
+        per[c]["kernels"]["stage2"]["frac_hbm"] = frac(hbm_bytes_stage2(W, n, wb),
+                                                       d[:, 2].mean())
+    evs.close()
 
-
-def min_sizes(sweep):
-    """From a sweep (measure_sweep's result): for every W and codec, the
-    smallest rank buffer (bytes) from which the two-stage allreduce with that
-    codec is faster than the one-stage allreduce at that size and at every
-    larger size of the sweep; None where it is not faster at the largest size.
-    The analogue of the minimum sizes below which the pages' wrapper keeps the
-    one-stage kernel, for this single-GPU simulation (no link time)."""
-    out = {}
-    for Wk, per_size in sweep.items():
-        sizes = sorted(per_size, key=int)
-        row = {}
-        for c in per_size[sizes[0]]:
-            if c == "1stage":
-                continue
-            best = None
-            for sz in reversed(sizes):
-                if per_size[sz][c]["us"] < per_size[sz]["1stage"]["us"]:
-                    best = int(sz)
-                else:
-                    break
-            row[c] = best
-        out[Wk] = row
-    return out
-
-
-def measure_sweep(qr, I, torch, stream, Ws=(2, 4, 8), sizes=SWEEP_SIZES, dtype=0):
-    """The simulated allreduce (qr_allreduce_sim) of every codec, and the
-    one-stage allreduce (key "1stage"), at every size from 4 KB to 64 MB per
-    rank buffer and W = 2, 4, 8.  Buffers drawn as in the W=2 64 MB workload
-    and rounded to the buffer type (`dtype`: 0 fp16, 1 bf16, 2 bf16 buffers
-    through binary16, the cast option); rank r's buffer is the same at every
-    W, and a smaller size is the leading part of the largest.  Per point:
-    median and minimum us per call, timed call by call as in
-    measure_workload."""
-    Wmax, nmax = max(Ws), max(sizes)
-    xs_all = [torch.from_numpy(x.view(np.int16)).to("cuda")
-              for x in I.make(2, W=Wmax, n=nmax, dtype=I.BF16 if dtype else I.FP16)]
-    ys_all = [torch.empty_like(x) for x in xs_all]
-    res = {}
-    for W in Ws:
-        per_size = {}
-        for n in sizes:
-            xs = [x[:n] for x in xs_all[:W]]
-            ys = [y[:n] for y in ys_all[:W]]
-            iters = 100 if 2 * n <= (1 << 20) else 20
+    cold = None
+    if not args.no_cold:
+        log("bench: cold launches, references")
+        pat = Pattern()
+        cl = Cold(torch, stream, args.cold_reps)
+        cold = {}
+        for c in codecs:
+            b = bufs[c]
+            wb = b["wb"]
+            staged(c)
+            torch.cuda.synchronize()
             r = {}
-            for c in I.ALL_CODECS:
-                ws = qr.alloc_workspace(W, c, n)
-                for _ in range(3):
-                    qr.qr_allreduce_sim(c, xs, ys, ws, dtype=dtype)
-                us = time_each(lambda: qr.qr_allreduce_sim(c, xs, ys, ws, dtype=dtype),
-                               iters, stream)
-                r[I.CODEC_NAMES[c]] = {"us": float(np.median(us)), "us_min": float(min(us))}
-                del ws
-            for _ in range(3):
-                qr.qr_allreduce_oneshot(xs, ys, dtype=dtype)
-            us = time_each(lambda: qr.qr_allreduce_oneshot(xs, ys, dtype=dtype), iters, stream)
-            r["1stage"] = {"us": float(np.median(us)), "us_min": float(min(us))}
-            per_size["%d" % (2 * n)] = r
-        res["W%d" % W] = per_size
-    del xs_all, ys_all
-    torch.cuda.empty_cache()
-    return res
+            r["quantize"] = cl.us(lambda: qr.qr_quantize_recv(c, xs, b["recv"], dtype=dtype))
+            r["stage1"] = cl.us(lambda: qr.qr_reduce_recv(c, W, b["recv"], n, b["red"], dtype))
+            r["stage2"] = cl.us(lambda: qr.qr_gather_stage2(c, b["red"], ys, dtype=dtype))
+            r["stage1_pattern"] = cl.us(lambda: pat.stage1(c, W, b["recv"], n, b["red"], stream))
+            ab1 = algorithmic_bytes("stage1", W, n, wb)
+            r["stage1_copy"] = cl.copy_us(ab1)
+            staged(c)           # leave the reduced image the kernels wrote
+            cold[c] = r
+        cl.close()
+    return dict(cfg=cfg, W=W, n=n, dtype=dtype, codecs=codecs, bufs=bufs, xs_np=xs_np,
+                ms_per_step=ms_per_step, ms_per_step_instrumented=ms_instr, per=per,
+                cold=cold)
 
+
+def roofline(h, I):
+    """stage 1 cold, lowest codec; each codec beside it with its access-pattern
+    ceiling; the kernel that takes the most time in the pipeline as a
+    secondary field"""
+    W, n, cold, per = h["W"], h["n"], h["cold"], h["per"]
+    src = cold if cold is not None else {c: {"stage1": per[c]["kernels"]["stage1"]["us"]}
+                                         for c in h["codecs"]}
+    fr = {}
+    for c in h["codecs"]:
+        wb = h["bufs"][c]["wb"]
+        fr[c] = frac(algorithmic_bytes("stage1", W, n, wb), src[c]["stage1"])
+    worst = min(fr, key=fr.get)
+    wb = h["bufs"][worst]["wb"]
+    ab = algorithmic_bytes("stage1", W, n, wb)
+    us = src[worst]["stage1"]
+    kname = "k_sum_fp" if worst == I.FP else "k_stage1"
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        tr = json.load(open(PROFILE_TRAFFIC))
+        ent = tr.get("kernels", {}).get("stage1/" + I.CODEC_NAMES[worst])
+        if ent and tr.get("source_sha") == kernel_source_sha() and \
+                tr.get("workload") == h["cfg"]["desc"]:
+            traffic = ent["bytes"]
+    dom_c, dom_st = max(((c, st) for c in h["codecs"] for st in STAGES),
+                        key=lambda k: per[k[0]]["kernels"][k[1]]["us"])
+    out = {"bound": "hbm", "kernel": "%s (stage 1, receive buffer), %s, %s" % (
+               kname, I.CODEC_NAMES[worst], "cold" if cold is not None else "in pipeline"),
+           "achieved": ab / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+           "frac": fr[worst], "traffic": traffic, "algorithmic_bytes_per_launch": ab,
+           "avg_launch_us": us,
+           "per_codec_frac": {I.CODEC_NAMES[c]: round(fr[c], 4) for c in h["codecs"]}}
+    if cold is not None:
+        out["pattern_frac"] = {I.CODEC_NAMES[c]: round(frac(algorithmic_bytes(
+            "stage1", W, n, h["bufs"][c]["wb"]), cold[c]["stage1_pattern"]), 4)
+            for c in h["codecs"]}
+        out["copy_frac"] = {I.CODEC_NAMES[c]: round(frac(algorithmic_bytes(
+            "stage1", W, n, h["bufs"][c]["wb"]), cold[c]["stage1_copy"]), 4)
+            for c in h["codecs"]}
+        out["in_pipeline_frac"] = {I.CODEC_NAMES[c]: round(
+            per[c]["kernels"]["stage1"]["frac"], 4) for c in h["codecs"]}
+    out["dominant_kernel"] = {"kernel": "%s/%s" % (dom_st, I.CODEC_NAMES[dom_c]),
+                              "us": per[dom_c]["kernels"][dom_st]["us"],
+                              "frac": per[dom_c]["kernels"][dom_st]["frac"]}
+    return out
+
+
+# ---------------------------------------------------------------------------
+# the CPU oracle
 
 def cpu_baseline(codecs, dtype, xs_np, sample, threads):
-    """The oracle as it stands, on blocks [0, sample/32) of every rank (the
-    same computation as the full buffers restricted to those blocks), split
-    over `threads` host threads by block range."""
+    """The oracle as it stands, the full pipeline of every codec on blocks
+    [0, sample/32) of every rank (the computation of the whole buffers
+    restricted to those blocks): once on `threads` host threads split by block
+    range (ctypes releases the GIL), best of 3, and once on one thread."""
     import oracle
     n = xs_np[0].size
     nb = min(sample, n) // 32
@@ -391,30 +393,29 @@ def cpu_baseline(codecs, dtype, xs_np, sample, threads):
     def work(lo, hi, codec):
         oracle.allreduce(codec, dtype, xs_np, int(lo), int(hi), ys=ys)
 
-    t0 = time.perf_counter()
-    for codec in codecs:
-        ts = [threading.Thread(target=work, args=(bounds[i], bounds[i + 1], codec))
-              for i in range(threads)]
-        for t in ts:
-            t.start()
-        for t in ts:
-            t.join()
-    dt = time.perf_counter() - t0
-    payload = len(codecs) * nb * 32 * 2
-    # the same scalar code on one thread, on a sixteenth of the sample
-    nb1 = max(1, nb // 16)
+    def run_threads():
+        t0 = time.perf_counter()
+        for codec in codecs:
+            ts = [threading.Thread(target=work, args=(bounds[i], bounds[i + 1], codec))
+                  for i in range(threads)]
+            for t in ts:
+                t.start()
+            for t in ts:
+                t.join()
+        return time.perf_counter() - t0
+
+    dt = min(run_threads() for _ in range(3))
     t1 = time.perf_counter()
     for codec in codecs:
-        work(0, nb1, codec)
+        work(0, nb, codec)
     dt1 = time.perf_counter() - t1
-    return {"value": payload / dt / 1e9, "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "blocks 0..%d (%d elements = %.1f MB per rank) of each of the %d "
-                      "ranks, all %d codecs, full pipeline; %.2f s wall" % (
-                          nb, nb * 32, nb * 64 / 2 ** 20, len(xs_np), len(codecs), dt),
-            "seconds": dt,
-            "single_thread": {"value": len(codecs) * nb1 * 64 / dt1 / 1e9, "unit": "GB/s",
-                              "sample": "blocks 0..%d, %.2f s" % (nb1, dt1)},
+    payload = len(codecs) * nb * 32 * 2
+    return {"value": payload / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "blocks 0..%d (%d elements = %.1f MiB) of each of the %d ranks, all %d "
+                      "codecs, full pipeline; best of 3 on %d threads %.2f s" % (
+                          nb, nb * 32, nb * 64 / 2 ** 20, len(xs_np), len(codecs), threads, dt),
+            "single_thread": {"value": payload / dt1 / 1e9, "unit": "GB/s",
+                              "seconds": round(dt1, 2)},
             "host": host_info()}
 
 
@@ -432,6 +433,158 @@ def host_info():
             "model": model}
 
 
+# ---------------------------------------------------------------------------
+# other workloads (--extra)
+
+def measure_workload(qr, I, torch, stream, config, n=None, iters=20, cold=True, dtype=None,
+                     oneshot=True):
+    """One workload of inputs.CONFIGS: per codec, qr_allreduce_sim timed call
+    by call (median and min us, effective GB/s = 2n / time), and cold stage 1
+    through the receive buffer; the one-stage allreduce (key "1stage")."""
+    cfg = I.CONFIGS[config]
+    W = cfg["W"]
+    dtype = cfg["dtype"] if dtype is None else dtype
+    n = cfg["n"] if n is None else n
+    xs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in I.make(config, n=n)]
+    ys = [torch.empty_like(xs[0]) for _ in range(W)]
+    cl = Cold(torch, stream, 5) if cold else None
+    out = {}
+    for c in cfg["codecs"]:
+        ws = qr.alloc_workspace(W, c, n)
+        for _ in range(3):
+            qr.qr_allreduce_sim(c, xs, ys, ws, dtype=dtype)
+        us = time_each(lambda: qr.qr_allreduce_sim(c, xs, ys, ws, dtype=dtype), iters, stream)
+        med = float(np.median(us))
+        r = {"us_median": med, "us_min": float(min(us)),
+             "effective_gbps": 2 * n / (med * 1e-6) / 1e9}
+        if cold:
+            recv, red = qr.alloc_recv(W, c, n), qr.alloc_wire(c, n)
+            qr.qr_quantize_recv(c, xs, recv, dtype=dtype)
+            t = cl.us(lambda: qr.qr_reduce_recv(c, W, recv, n, red, dtype))
+            r["stage1_cold_us"] = t
+            r["stage1_cold_frac"] = frac(algorithmic_bytes("stage1", W, n,
+                                                           qr.qr_wire_bytes(c, n)), t)
+            del recv, red
+        del ws
+        out[I.CODEC_NAMES[c]] = r
+    if oneshot:
+        for _ in range(3):
+            qr.qr_allreduce_oneshot(xs, ys, dtype=dtype)
+        us = time_each(lambda: qr.qr_allreduce_oneshot(xs, ys, dtype=dtype), iters, stream)
+        med = float(np.median(us))
+        out["1stage"] = {"us_median": med, "us_min": float(min(us)),
+                         "frac": frac(W * (W + 1) * 2 * n, med)}
+    if cl is not None:
+        cl.close()
+    del xs, ys
+    torch.cuda.empty_cache()
+    return out
+
+
+SWEEP_SIZES = tuple(2 ** k for k in range(11, 26))      # elements: 4 KB .. 64 MB per rank
+
+
+def measure_sweep(qr, I, torch, stream, repeats, Ws=(2, 4, 8), sizes=SWEEP_SIZES, dtype=0):
+    """qr_allreduce_sim of every codec and the one-stage allreduce ("1stage")
+    at every size from 4 KB to 64 MB per rank buffer and W = 2, 4, 8; buffers
+    drawn as in the W=2 64 MB workload, rounded to the buffer type (0 fp16,
+    1 bf16, 2 bf16 through binary16); a smaller size is the leading part of
+    the largest.  Every point is measured `repeats` times, each time the
+    median of a run of calls (100 calls up to 1 MB, 20 above); the point
+    keeps the median of those medians and their spread (max - min)."""
+    Wmax, nmax = max(Ws), max(sizes)
+    xs_all = [torch.from_numpy(x.view(np.int16)).to("cuda")
+              for x in I.make(2, W=Wmax, n=nmax, dtype=I.BF16 if dtype else I.FP16)]
+    ys_all = [torch.empty_like(x) for x in xs_all]
+    res = {}
+    for W in Ws:
+        per_size = {}
+        for n in sizes:
+            xs = [x[:n] for x in xs_all[:W]]
+            ys = [y[:n] for y in ys_all[:W]]
+            iters = 100 if 2 * n <= (1 << 20) else 20
+            calls = {I.CODEC_NAMES[c]: (lambda c=c, ws=qr.alloc_workspace(W, c, n):
+                                        qr.qr_allreduce_sim(c, xs, ys, ws, dtype=dtype))
+                     for c in I.ALL_CODECS}
+            calls["1stage"] = lambda: qr.qr_allreduce_oneshot(xs, ys, dtype=dtype)
+            meds = {k: [] for k in calls}
+            for _ in range(repeats):
+                for k, f in calls.items():
+                    for _ in range(3):
+                        f()
+                    meds[k].append(float(np.median(time_each(f, iters, stream))))
+            per_size["%d" % (2 * n)] = {k: {"us": float(np.median(v)),
+                                            "spread": float(max(v) - min(v))}
+                                        for k, v in meds.items()}
+            del calls
+        res["W%d" % W] = per_size
+    del xs_all, ys_all
+    torch.cuda.empty_cache()
+    return res
+
+
+def min_sizes(sweep):
+    """For every W and codec: the smallest rank buffer (bytes) from which the
+    two-stage allreduce beats the one-stage allreduce at that size and at
+    every larger size of the sweep, a win counting only when it exceeds both
+    points' spread (two-stage median + spread below one-stage median -
+    spread); None where it does not win at the largest size.  The analogue of
+    the minimum sizes below which the pages' wrapper keeps another allreduce,
+    for this single-GPU simulation (no link time)."""
+    out = {}
+    for Wk, per_size in sweep.items():
+        sizes = sorted(per_size, key=int)
+        row = {}
+        for c in per_size[sizes[0]]:
+            if c == "1stage":
+                continue
+            best = None
+            for sz in reversed(sizes):
+                a, b = per_size[sz][c], per_size[sz]["1stage"]
+                if a["us"] + a["spread"] < b["us"] - b["spread"]:
+                    best = int(sz)
+                else:
+                    break
+            row[c] = best
+        out[Wk] = row
+    return out
+
+
+def measure_extra(args, qr, I, torch, stream, log):
+    extra = {}
+    for cid in (2, 4):
+        c = I.CONFIGS[cid]
+        log("bench: config %d (%s)" % (cid, c["desc"]))
+        extra["config%d" % cid] = {"workload": c["desc"], "W": c["W"],
+                                   "elements_per_rank": c["n"],
+                                   "per_codec": measure_workload(qr, I, torch, stream, cid)}
+    c = I.CONFIGS[4]
+    log("bench: config 4 with the bf16->fp16 cast")
+    extra["config4_cast"] = {"workload": c["desc"] + "; bf16 buffers through binary16",
+                             "per_codec": measure_workload(qr, I, torch, stream, 4, cold=False,
+                                                           dtype=qr.QR_BF16_VIA_FP16)}
+    c = I.CONFIGS[3]
+    log("bench: config 3 size sweep")
+    sweep = {}
+    for size in c["sizes"]:
+        sweep["%d" % (2 * size)] = measure_workload(
+            qr, I, torch, stream, 3, n=size, iters=100 if 2 * size <= (1 << 20) else 20,
+            cold=2 * size >= (16 << 20))
+    extra["config3_sweep"] = {"workload": c["desc"], "key": "bytes per rank buffer",
+                              "per_size": sweep}
+    for key, dt in (("sweep_fp16", 0), ("sweep_bf16", 1), ("sweep_bf16_via_fp16", 2)):
+        log("bench: size sweep %s, %d repeats" % (key, args.sweep_repeats))
+        extra[key] = {"key": "W, then bytes per rank buffer; us = median of %d medians, "
+                             "spread = max - min of them" % args.sweep_repeats,
+                      "results": measure_sweep(qr, I, torch, stream, args.sweep_repeats,
+                                               dtype=dt)}
+    extra["min_sizes"] = {k: min_sizes(extra["sweep_" + k]["results"])
+                          for k in ("fp16", "bf16", "bf16_via_fp16")}
+    return extra
+
+
+# ---------------------------------------------------------------------------
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -440,254 +593,73 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
     import torch
     from quantized_two_stage_amd import inputs as I
     from quantized_two_stage_amd import qr
 
     torch.cuda.set_device(0)
-    cfg = I.CONFIGS[args.config]
-    W, n, dtype, codecs = cfg["W"], cfg["n"], cfg["dtype"], cfg["codecs"]
-    print("bench: config %d (%s), generating inputs" % (args.config, cfg["desc"]),
-          file=sys.stderr, flush=True)
-    xs_np = I.make(args.config)
-    xs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in xs_np]
-    ys = [torch.empty_like(xs[0]) for _ in range(W)]
-    bufs = {}
-    for c in codecs:
-        wb = qr.qr_wire_bytes(c, n)
-        bufs[c] = ([qr.alloc_wire(c, n) for _ in range(W)], qr.alloc_wire(c, n), wb)
     stream = torch.cuda.current_stream()
-
-    def one_allreduce(c, ev=None, base=0):
-        wires, red, _ = bufs[c]
-        if ev is not None:
-            ev.record(base, stream)
-        qr.qr_quantize_ranks(c, xs, wires, dtype=dtype)
-        if ev is not None:
-            ev.record(base + 1, stream)
-        qr.qr_reduce_stage1(c, wires, n, red, dtype)
-        if ev is not None:
-            ev.record(base + 2, stream)
-        qr.qr_gather_stage2(c, red, ys, dtype=dtype)
-        if ev is not None:
-            ev.record(base + 3, stream)
-
-    # one workspace per codec for the one-call entry point
-    wss = {c: qr.alloc_workspace(W, c, n) for c in codecs}
-
-    # check once: the staged calls give what the one-call entry point gives
-    ys_ref = [torch.empty_like(xs[0]) for _ in range(W)]
-    qr.qr_allreduce_sim(codecs[0], xs, ys_ref, wss[codecs[0]], dtype=dtype)
-    one_allreduce(codecs[0])
-    torch.cuda.synchronize()
-    assert all(torch.equal(a, b) for a, b in zip(ys, ys_ref)), "staged != one-call"
-    del ys_ref
-
-    for _ in range(args.warmup):
-        for c in codecs:
-            qr.qr_allreduce_sim(c, xs, ys, wss[c], dtype=dtype)
-            one_allreduce(c)
-    torch.cuda.synchronize()
-
-    # pass 1: the timed region
-    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        for c in codecs:
-            qr.qr_allreduce_sim(c, xs, ys, wss[c], dtype=dtype)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    # pass 2: the same steps, staged, with events around every launch
-    nc = len(codecs)
-    evs = HipEvents(4 * nc * args.steps)
-    print("bench: instrumented pass, %d steps" % args.steps, file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for s in range(args.steps):
-        for ci, c in enumerate(codecs):
-            one_allreduce(c, evs, 4 * (s * nc + ci))
-    torch.cuda.synchronize()
-    ms_per_step_instr = (time.perf_counter() - t1) * 1e3 / args.steps
-
-    stages = ("quantize", "stage1", "stage2")
-    kernels, per_codec = [], {}
-    for ci, c in enumerate(codecs):
-        d = np.array([[evs.ms(4 * (s * nc + ci) + k, 4 * (s * nc + ci) + k + 1)
-                       for k in range(3)] for s in range(args.steps)])            # ms
-        avg = d.mean(axis=0)
-        wb = bufs[c][2]
-        us = float(avg.sum() * 1e3)
-        per_codec[I.CODEC_NAMES[c]] = {
-            "us": us, "us_median": float(np.median(d.sum(axis=1)) * 1e3),
-            "effective_gbps": 2 * n / (us * 1e-6) / 1e9}
-        for k, st in enumerate(stages):
-            ab = algorithmic_bytes(st, W, n, wb)
-            cu = copy_same_bytes_us(torch, stream, ab)
-            kernels.append({"kernel": "%s/%s" % (st, I.CODEC_NAMES[c]),
-                            "us": float(avg[k] * 1e3),
-                            "algorithmic_bytes": ab,
-                            "gbps": ab / (avg[k] * 1e-3) / 1e9,
-                            "copy_us": cu, "vs_copy": cu / float(avg[k] * 1e3)})
-    evs.close()
-    total_payload = len(codecs) * 2 * n
-    value = total_payload / (ms_per_step * 1e-3) / 1e9
-    dom = max(kernels, key=lambda k: k["us"])
-    traffic = None
-    if os.path.exists(PROFILE_TRAFFIC) and args.config == 2:    # the profiled workload
-        tr = json.load(open(PROFILE_TRAFFIC))
-        ent = tr.get("kernels", {}).get(dom["kernel"])
-        if ent and tr.get("source_sha") == kernel_source_sha():
-            traffic = ent["bytes"]
-    roofline = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["gbps"],
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dom["gbps"] / HBM_PEAK_GBPS,
-                "traffic": traffic, "algorithmic_bytes_per_launch": dom["algorithmic_bytes"],
-                "avg_launch_us": dom["us"], "copy_same_bytes_us": dom["copy_us"],
-                "vs_copy": dom["vs_copy"]}
-
-    # plain device copies: 64 MB (fits the 256 MB Infinity Cache, like the
-    # workload's own buffers) and 1 GiB (streams from HBM)
-    copy_gbps = {}
-    for size in (64 << 20, 1 << 30):
-        src = torch.empty(size, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 20 if size < (1 << 30) else 5
-        e0.record(stream)
-        for _ in range(reps):
-            dst.copy_(src)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        copy_gbps["%dMiB" % (size >> 20)] = 2 * size * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        del src, dst
-
-    # the floor of a call's time as time_each measures it: one launch of a
-    # kernel that writes a single element
-    tiny = torch.zeros(1, dtype=torch.int32, device="cuda")
-    for _ in range(3):
-        tiny.zero_()
-    launch_floor_us = float(np.median(time_each(lambda: tiny.zero_(), 100, stream)))
-    del tiny
-
-    cold = None
-    if not args.no_cold:
-        # stage 1 with L2 and the 256 MB Infinity Cache flushed before each
-        # timed launch by reading 1 GiB of other data (a read leaves no dirty
-        # lines to write back during the timed kernel)
-        flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
-        cold = {}
-        for c in codecs:
-            wires, red, wb = bufs[c]
-            qr.qr_quantize_ranks(c, xs, wires, dtype=dtype)
-            ts = []
-            ce = HipEvents(2)
-            for _ in range(5):
-                flush.sum()
-                ce.record(0, stream)
-                qr.qr_reduce_stage1(c, wires, n, red, dtype)
-                ce.record(1, stream)
-                torch.cuda.synchronize()
-                ts.append(ce.ms(0, 1))
-            ce.close()
-            us = float(np.median(ts) * 1e3)
-            ab = algorithmic_bytes("stage1", W, n, wb)
-            cu = copy_same_bytes_us(torch, stream, ab, flush)
-            cold["stage1/" + I.CODEC_NAMES[c]] = {"us": us, "gbps": ab / (us * 1e-6) / 1e9,
-                                                  "frac": ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-                                                  "copy_us": cu, "vs_copy": cu / us}
-        del flush
-
-    extra = None
-    if not args.no_extra:
-        extra = {}
-        for cid in (2, 5, 4):
-            c = I.CONFIGS[cid]
-            print("bench: config %d (%s)" % (cid, c["desc"]), file=sys.stderr, flush=True)
-            extra["config%d" % cid] = {
-                "workload": c["desc"], "W": c["W"], "elements_per_rank": c["n"],
-                "per_codec": measure_workload(qr, I, torch, stream, cid, cold=not args.no_cold)}
-        # the bf16 -> fp16 cast option (buffer type 2) on the bf16 workload
-        c = I.CONFIGS[4]
-        print("bench: config 4 with the bf16->fp16 cast", file=sys.stderr, flush=True)
-        extra["config4_cast"] = {
-            "workload": c["desc"] + "; bf16 buffers through binary16 (cast option)",
-            "W": c["W"], "elements_per_rank": c["n"],
-            "per_codec": measure_workload(qr, I, torch, stream, 4, cold=False,
-                                          dtype=qr.QR_BF16_VIA_FP16)}
-        print("bench: stage 1 alone, cold, W=2, 64 MB .. 1 GiB per rank", file=sys.stderr,
-              flush=True)
-        extra["stage1_sizes"] = {
-            "workload": "stage 1 alone, cold caches, W=2 fp16, codecs of the W=2 64 MB workload; "
-                        "rank buffers beyond 64 MB repeat its seeded buffers",
-            "key": "bytes per rank buffer",
-            "results": measure_stage1_sizes(qr, I, torch, stream)}
-        c = I.CONFIGS[3]
-        print("bench: config 3 size sweep (%s)" % c["desc"], file=sys.stderr, flush=True)
-        sweep = {}
-        for size in c["sizes"]:
-            iters = 100 if 2 * size <= (1 << 20) else 20
-            r = measure_workload(qr, I, torch, stream, 3, n=size, iters=iters,
-                                 kernels=False, cold=False)
-            sweep["%d" % (2 * size)] = r
-        extra["config3_sweep"] = {"workload": c["desc"], "W": c["W"],
-                                  "key": "bytes per rank buffer", "per_size": sweep}
-        print("bench: size sweep, W=2/4/8, every codec, fp16", file=sys.stderr, flush=True)
-        extra["sweep_fp16"] = {
-            "workload": "fp16 buffers drawn as the W=2 64 MB workload, 4 KB..64 MB per rank, "
-                        "W=2/4/8, every codec and the one-stage allreduce; us per call "
-                        "(median, min)",
-            "key": "W, then bytes per rank buffer",
-            "results": measure_sweep(qr, I, torch, stream)}
-        print("bench: size sweep, bf16 and bf16 through fp16", file=sys.stderr, flush=True)
-        for key, dt, what in (("sweep_bf16", I.BF16, "bf16 buffers"),
-                              ("sweep_bf16_via_fp16", 2, "bf16 buffers through binary16 "
-                                                         "(the cast option)")):
-            extra[key] = {
-                "workload": "%s drawn as the W=2 64 MB workload, 4 KB..64 MB per rank, "
-                            "W=2/4/8, every codec and the one-stage allreduce; us per call "
-                            "(median, min)" % what,
-                "key": "W, then bytes per rank buffer",
-                "results": measure_sweep(qr, I, torch, stream, dtype=dt)}
-        extra["min_sizes"] = {
-            "what": "per buffer type, W and codec: the smallest rank buffer (bytes) from which "
-                    "the two-stage allreduce is faster than the one-stage allreduce at every "
-                    "larger size of the sweep (null: not faster at 64 MB)",
-            "fp16": min_sizes(extra["sweep_fp16"]["results"]),
-            "bf16": min_sizes(extra["sweep_bf16"]["results"]),
-            "bf16_via_fp16": min_sizes(extra["sweep_bf16_via_fp16"]["results"])}
+    h = measure_headline(args, qr, I, torch, stream, log)
+    W, n, codecs = h["W"], h["n"], h["codecs"]
+    value = len(codecs) * 2 * n / (h["ms_per_step"] * 1e-3) / 1e9
+    roof = roofline(h, I)
 
     cpu = None
     if not args.no_cpu_baseline:
-        threads = min(16, os.cpu_count() or 1)
-        print("bench: CPU oracle on a sample, %d threads" % threads, file=sys.stderr,
-              flush=True)
-        cpu = cpu_baseline(codecs, dtype, xs_np, args.cpu_sample, threads)
+        threads = min(16, len(os.sched_getaffinity(0)))
+        log("bench: CPU oracle on a sample, %d threads" % threads)
+        cpu = cpu_baseline(codecs, h["dtype"], h["xs_np"], args.cpu_sample, threads)
+
+    stages = {}
+    for c in codecs:
+        k = h["per"][c]["kernels"]
+        e = {"us_per_allreduce": round(h["per"][c]["us_per_allreduce"], 2)}
+        for st in STAGES:
+            e[st] = {"us": round(k[st]["us"], 2), "frac": round(k[st]["frac"], 4)}
+        e["stage2"]["frac_hbm"] = round(k["stage2"]["frac_hbm"], 4)
+        if h["cold"] is not None:
+            cd = h["cold"][c]
+            wb = h["bufs"][c]["wb"]
+            for st in STAGES:
+                e[st]["cold_us"] = round(cd[st], 2)
+                e[st]["cold_frac"] = round(frac(algorithmic_bytes(st, W, n, wb), cd[st]), 4)
+            e["stage2"]["cold_frac_hbm"] = round(frac(hbm_bytes_stage2(W, n, wb),
+                                                      cd["stage2"]), 4)
+        stages[I.CODEC_NAMES[c]] = e
+
+    extra = None
+    if args.extra:
+        extra = measure_extra(args, qr, I, torch, stream, log)
+        extra["headline_stages"] = stages
+        with open(args.extra, "w") as f:
+            json.dump(extra, f, indent=1)
+        log("bench: other workloads written to %s" % args.extra)
+
+    for name, e in stages.items():
+        log("  %-4s %8.1f us/allreduce  stage0 %.3f  stage1 %.3f (cold %s)  stage2 %.3f" % (
+            name, e["us_per_allreduce"], e["quantize"]["frac"], e["stage1"]["frac"],
+            e["stage1"].get("cold_frac"), e["stage2"]["frac"]))
 
     out = {
-        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
-        "ms_per_step_instrumented": ms_per_step_instr,
+        "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(h["ms_per_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "W=%d simulated ranks, %s, %d elements (%d MB) per rank, "
-                               "codecs %s, 32-element blocks; %s" % (
-                                   W, "fp16" if dtype == 0 else "bf16", n, 2 * n >> 20,
-                                   "/".join(I.CODEC_NAMES[c] for c in codecs), cfg["desc"]),
-                   "W": W, "elements_per_rank": n, "buffer_dtype": "fp16" if dtype == 0
-                   else "bf16", "codecs": [I.CODEC_NAMES[c] for c in codecs],
+        "config": {"workload": "W=%d simulated ranks, %s, %d elements (%d MB) per rank, all "
+                               "%d codecs, 32-element blocks: %s" % (
+                                   W, "fp16" if h["dtype"] == 0 else "bf16", n, 2 * n >> 20,
+                                   len(codecs), h["cfg"]["desc"]),
+                   "W": W, "elements_per_rank": n,
+                   "buffer_dtype": "fp16" if h["dtype"] == 0 else "bf16",
                    "allreduces_per_step": len(codecs)},
-        "roofline": roofline,
+        "roofline": roof,
         "cpu_baseline": cpu,
-        "per_codec": per_codec,
-        "kernels": kernels,
-        "stage1_cold": cold,
-        "other_workloads": extra,
-        "device_copy_gbps": copy_gbps,
-        "launch_floor_us": launch_floor_us,
+        "us_per_allreduce": {I.CODEC_NAMES[c]: round(h["per"][c]["us_per_allreduce"], 1)
+                             for c in codecs},
+        "ms_per_step_instrumented": round(h["ms_per_step_instrumented"], 4),
         "kernel_source_sha": kernel_source_sha(),
     }
     print(json.dumps(out), flush=True)

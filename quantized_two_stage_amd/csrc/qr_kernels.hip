@@ -39,6 +39,7 @@
 #include "qr.h"
 #include "qr_device.h"
 #include "qr_internal.h"
+#include "qr_stage_io.h"
 
 // The workspace of qr_allreduce_sim_noalloc: one buffer per GPU, held for the
 // life of the process.  In host code `scratch` names a host-side stand-in,
@@ -48,87 +49,6 @@ static __device__ __align__(256) uint8_t scratch[QR_SCRATCH_BYTES];
 
 namespace qr {
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kPerLane = 4;        // quarters / chunks per lane (k_quantize,
-                                   // k_dequant and the FP kernels)
-
-// Tuning knobs (compile-time; the defaults are the measured best on MI355X):
-// QR_NT_STORE bit mask of the stages (1 = stage 0, 2 = stage 1, 4 = stage 2)
-//             whose streamed outputs are written with non-temporal stores.
-//             Default 5: the wire images of stage 0 (read once, by another
-//             rank) and the outputs of stage 2 (the result).  Lines written
-//             through the caches stay dirty there and the next kernel pays
-//             for their write-back; stage 1's reduced image is kept cached
-//             because stage 2 reads it W times.
-// QR_NT_LOAD  bit mask of the stages whose read-once inputs are loaded with
-//             non-temporal loads (default none: no gain measured).
-#ifndef QR_NT_STORE
-#define QR_NT_STORE 5
-#endif
-#ifndef QR_NT_LOAD
-#define QR_NT_LOAD 0
-#endif
-constexpr int kStage0 = 1, kStage1 = 2, kStage2 = 4;
-constexpr int kKeep = 0;           // store policy: always through the caches
-
-template <int Stage, typename V>
-__device__ __forceinline__ void st_out(V* p, V v) {
-  if constexpr ((QR_NT_STORE & Stage) != 0)
-    __builtin_nontemporal_store(v, p);
-  else
-    *p = v;
-}
-template <int Stage, typename V>
-__device__ __forceinline__ V ld_in(const V* p) {
-  if constexpr ((QR_NT_LOAD & Stage) != 0)
-    return __builtin_nontemporal_load(p);
-  else
-    return *p;
-}
-
-struct Geo {
-  uint32_t n;        // elements per rank
-  uint32_t nb;       // blocks per rank
-  uint32_t off_s;    // scale plane offset
-  uint32_t off_z;    // zero plane offset
-  uint64_t tstride;  // receive buffer: bytes from one tile of a rank to its next (W tiles)
-};
-
-// Byte offsets of block blk's codes, scale and zero from a rank's base
-// pointer.  Recv == false: the planar wire image (codes at blk * CB, scales
-// and zeros in their planes).  Recv == true: the rank's tiles in the receive
-// buffer, the base being its first tile; tile t = blk / kTileBlocks starts
-// t * tstride further and holds kTileBlocks blocks' codes, then their scales,
-// then their zeros.  FP (raw data) uses code() alone, with CB = 64.
-template <int CB, bool Recv>
-struct WireAt {
-  static constexpr uint32_t kTB = kTileBlocks;
-  __device__ static __forceinline__ uint64_t tile(const Geo& g, uint32_t blk) {
-    return (uint64_t)(blk / kTB) * g.tstride;
-  }
-  __device__ static __forceinline__ uint64_t code(const Geo& g, uint32_t blk) {
-    if constexpr (Recv) return tile(g, blk) + (blk % kTB) * (uint32_t)CB;
-    return (uint64_t)blk * CB;
-  }
-  __device__ static __forceinline__ uint64_t scale(const Geo& g, uint32_t blk) {
-    if constexpr (Recv) return tile(g, blk) + kTB * CB + (blk % kTB) * 2u;
-    return g.off_s + (uint64_t)blk * 2;
-  }
-  __device__ static __forceinline__ uint64_t zero(const Geo& g, uint32_t blk) {
-    if constexpr (Recv) return tile(g, blk) + kTB * (CB + 2) + (blk % kTB) * 2u;
-    return g.off_z + (uint64_t)blk * 2;
-  }
-};
-template <int C, bool Recv>
-using At = WireAt<CodecT<C>::block_bytes, Recv>;
-
-__device__ __forceinline__ uint32_t ld_u16(const uint8_t* p) {
-  return *reinterpret_cast<const uint16_t*>(p);
-}
-__device__ __forceinline__ void st_u16(uint8_t* p, uint32_t v) {
-  *reinterpret_cast<uint16_t*>(p) = (uint16_t)v;
-}
 
 // Bytes of codes of quarter j (0..3) of a block: 8 codes = 8*b bits starting
 // at bit 8*b*j of the block's bitstring.  Returned as words with the first
@@ -347,30 +267,39 @@ __device__ __forceinline__ bool tile_full(uint32_t wg, uint32_t n) {
 
 // a workgroup quantizes 256 blocks of rank blockIdx.y: one tile of the
 // receive buffer
+// The (tile, rank) a stage-0 workgroup takes.  Into W planar wire images:
+// blockIdx = (tile, rank), so that consecutive workgroups read and write
+// consecutive tiles of one rank.  Into the receive buffer: workgroup
+// t*W + r takes tile t of rank r, so that consecutive workgroups write
+// consecutive tiles of the buffer (the rank-major order writes it at a
+// stride of W tiles, which made stage 0 4-9% slower at W=8, 64 MB per rank).
+template <bool Recv>
+__device__ __forceinline__ void s0_item(int W, uint32_t& tile, int& r) {
+  if constexpr (Recv) {
+    tile = blockIdx.x / (uint32_t)W;
+    r = (int)(blockIdx.x % (uint32_t)W);
+  } else {
+    tile = blockIdx.x;
+    r = blockIdx.y;
+  }
+}
+
 template <int C, int D, bool Recv>
-__global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires, Geo g) {
+__global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires, Geo g, int W) {
   static_assert(kPerLane == 4, "one block per lane of the quad");
   static_assert(kThreads * kPerLane / 4 == kTileBlocks, "a workgroup's blocks are one tile");
-  const int r = blockIdx.y;
-  const uint32_t q0 = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
+  uint32_t tile;
+  int r;
+  s0_item<Recv>(W, tile, r);
+  const uint32_t q0 = tile * (kThreads * kPerLane) + threadIdx.x;
   u32x4 raw[4];
-  if (tile_full(blockIdx.x, g.n)) {
+  if (tile_full(tile, g.n)) {
     load_tile<true>(xs.p[r], q0, g.n, raw);
     quantize_tile<C, D, true, Recv>(raw, q0, wires.p[r], g);
   } else {
     load_tile<false>(xs.p[r], q0, g.n, raw);
     quantize_tile<C, D, false, Recv>(raw, q0, wires.p[r], g);
   }
-}
-
-// Byte offset of 16-byte chunk c of a rank's raw data (the FP codec's wire):
-// planar, or in the rank's tiles of the receive buffer (a tile holds the
-// kTileBlocks * 4 chunks of its blocks).
-template <bool Recv>
-__device__ __forceinline__ uint64_t fp_chunk(uint64_t tstride, uint32_t c) {
-  constexpr uint32_t kTC = kTileBlocks * 4;
-  if constexpr (Recv) return (uint64_t)(c / kTC) * tstride + (c % kTC) * 16u;
-  return (uint64_t)c * 16;
 }
 
 // stages 0 and 2 of FP: dst.p[r] <- src.p[r], 16-byte chunks, four per
@@ -381,13 +310,15 @@ __device__ __forceinline__ uint64_t fp_chunk(uint64_t tstride, uint32_t c) {
 // tiles of the receive buffer
 template <int Stage, int Din, int Dout, bool Recv>
 __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
-                                                   uint32_t nchunks, uint64_t tstride) {
+                                                   uint32_t nchunks, uint64_t tstride, int W) {
   static_assert(kThreads * kPerLane == kTileBlocks * 4, "a workgroup's chunks are one tile");
   constexpr int kS = Stage == 0 ? kStage0 : kStage2;
-  const int r = blockIdx.y;
+  uint32_t tile;
+  int r;
+  s0_item<Recv>(W, tile, r);
   const u32x4* s = reinterpret_cast<const u32x4*>(src.p[r]);
   uint8_t* d = dst.p[r];
-  const uint32_t base = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
+  const uint32_t base = tile * (kThreads * kPerLane) + threadIdx.x;
   u32x4 q[kPerLane];
 #pragma unroll
   for (int j = 0; j < kPerLane; j++) {
@@ -408,45 +339,6 @@ __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
 
 // ---------------------------------------------------------------------------
 // stage 1: one block per lane
-
-// the W code blocks and scales (and zeros) of one block index
-template <int C, int W>
-struct S1In {
-  uint32_t cw[W][CodecT<C>::words];
-  uint32_t sh[W], zh[W];     // binary16 scale and zero bits
-};
-
-// the W ranks' code blocks and scales (and zeros) of block blk; Recv: from
-// the ranks' tiles of the receive buffer (the W tiles of one workgroup's
-// blocks are consecutive there, so the workgroup reads one contiguous range)
-template <int C, int W, bool Recv>
-__device__ __forceinline__ void s1_load(const InPtrs& wires, uint32_t blk, const Geo& g,
-                                        S1In<C, W>& in) {
-  using T = CodecT<C>;
-  const uint64_t co = At<C, Recv>::code(g, blk);
-  const uint64_t so = At<C, Recv>::scale(g, blk), zo = At<C, Recv>::zero(g, blk);
-#pragma unroll
-  for (int r = 0; r < W; r++) {
-    const uint8_t* cb = wires.p[r] + co;
-    if constexpr (T::words == 6) {
-#pragma unroll
-      for (int k = 0; k < 3; k++) {
-        const u32x2 q = ld_in<kStage1>(reinterpret_cast<const u32x2*>(cb) + k);
-        in.cw[r][2 * k] = q.x;
-        in.cw[r][2 * k + 1] = q.y;
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < T::words / 4; k++) {
-        const u32x4 q = ld_in<kStage1>(reinterpret_cast<const u32x4*>(cb) + k);
-        in.cw[r][4 * k] = q.x; in.cw[r][4 * k + 1] = q.y;
-        in.cw[r][4 * k + 2] = q.z; in.cw[r][4 * k + 3] = q.w;
-      }
-    }
-    in.sh[r] = ld_u16(wires.p[r] + so);
-    in.zh[r] = T::asym ? ld_u16(wires.p[r] + zo) : 0u;
-  }
-}
 
 // Full: the block holds 32 elements (no partial-block handling)
 template <int C, int W, bool Full>
@@ -502,21 +394,7 @@ __device__ __forceinline__ void s1_reduce_store(const S1In<C, W>& in, uint8_t* r
       w[k] = first <= 0 ? 0u : first >= 32 ? w[k] : w[k] & ((1u << first) - 1u);
     }
   }
-  // the reduced image is a planar wire image
-  uint8_t* cb = red + At<C, false>::code(g, blk);
-  const uint64_t so = At<C, false>::scale(g, blk), zo = At<C, false>::zero(g, blk);
-  if constexpr (T::words == 6) {
-#pragma unroll
-    for (int k = 0; k < 3; k++)
-      st_out<kStage1>(reinterpret_cast<u32x2*>(cb) + k, u32x2{w[2 * k], w[2 * k + 1]});
-  } else {
-#pragma unroll
-    for (int k = 0; k < T::words / 4; k++)
-      st_out<kStage1>(reinterpret_cast<u32x4*>(cb) + k,
-                      u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]});
-  }
-  st_u16(red + so, p.s);
-  if constexpr (T::asym) st_u16(red + zo, p.z);
+  s1_store<C>(red, blk, g, w, p.s, p.z);
 }
 
 // one lane per block
@@ -854,13 +732,15 @@ void q_launch(int W, const InPtrs& xs, const OutPtrs& wires, const Layout& L, hi
     // the FP wire holds the buffer's raw elements (binary16 under the cast)
     constexpr int Dw = D == kBF16H ? kF16 : D;
     constexpr int Din = D == kBF16H ? kBF16 : D;
-    hipLaunchKernelGGL((k_copy<0, Din, Dw, Recv>), dim3(groups(L.n / 8, kThreads * kPerLane), W),
-                       dim3(kThreads), 0, st, xs, wires, (uint32_t)(L.n / 8),
-                       geo(L, W, Recv).tstride);
+    const unsigned tiles = groups(L.n / 8, kThreads * kPerLane);
+    const dim3 grid = Recv ? dim3(tiles * W) : dim3(tiles, W);
+    hipLaunchKernelGGL((k_copy<0, Din, Dw, Recv>), grid, dim3(kThreads), 0, st, xs, wires,
+                       (uint32_t)(L.n / 8), geo(L, W, Recv).tstride, W);
   } else {
-    hipLaunchKernelGGL((k_quantize<C, D, Recv>),
-                       dim3(groups(4 * L.nb, kThreads * kPerLane), W),
-                       dim3(kThreads), 0, st, xs, wires, geo(L, W, Recv));
+    const unsigned tiles = groups(4 * L.nb, kThreads * kPerLane);
+    const dim3 grid = Recv ? dim3(tiles * W) : dim3(tiles, W);
+    hipLaunchKernelGGL((k_quantize<C, D, Recv>), grid, dim3(kThreads), 0, st, xs, wires,
+                       geo(L, W, Recv), W);
   }
 }
 
@@ -883,7 +763,7 @@ void dq_dispatch(int W, const uint8_t* wire, const OutPtrs& ys, const Layout& L,
     constexpr int Dout = D == kBF16H ? kBF16 : D;
     hipLaunchKernelGGL((k_copy<2, Dw, Dout, false>),
                        dim3(groups(L.n / 8, kThreads * kPerLane), W), dim3(kThreads), 0, st,
-                       src, ys, (uint32_t)(L.n / 8), 0ull);
+                       src, ys, (uint32_t)(L.n / 8), 0ull, W);
   } else {
     hipLaunchKernelGGL((k_dequant<C, D>), dim3(groups(L.n / 8, kThreads * kPerLane), W),
                        dim3(kThreads), 0, st, wire, ys, geo(L));

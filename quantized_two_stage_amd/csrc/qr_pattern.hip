@@ -1,0 +1,135 @@
+// qr_pattern.hip -- the benchmark's access-pattern reference for stage 1, built
+// into its own library (libqr_pattern.so), not into libqr.so.
+//
+// qrp_stage1_pattern issues exactly the loads and stores of the stage-1
+// kernel that reads a receive buffer (the same grid, the same lanes, the same
+// addresses and access widths, through the helpers of qr_stage_io.h) and
+// replaces the dequantize-sum-requantize arithmetic by an XOR of the W ranks'
+// words.  Its time is what the memory system needs for stage 1's bytes in
+// stage 1's pattern: the ceiling the benchmark reports beside the kernel.
+#include <stdint.h>
+
+#include "qr.h"
+#include "qr_device.h"
+#include "qr_internal.h"
+#include "qr_stage_io.h"
+
+namespace qr {
+namespace {
+
+template <int C, int W>
+__global__ __launch_bounds__(kThreads) void k_stage1_pattern(InPtrs wires, uint8_t* red,
+                                                             uint32_t nb, Geo g) {
+  using T = CodecT<C>;
+  const uint32_t blk = blockIdx.x * kThreads + threadIdx.x;
+  if (blk >= nb) return;
+  S1In<C, W> in;
+  s1_load<C, W, true>(wires, blk, g, in);
+  uint32_t w[T::words];
+  uint32_t s = in.sh[0], z = in.zh[0];
+#pragma unroll
+  for (int k = 0; k < T::words; k++) w[k] = in.cw[0][k];
+#pragma unroll
+  for (int r = 1; r < W; r++) {
+#pragma unroll
+    for (int k = 0; k < T::words; k++) w[k] ^= in.cw[r][k];
+    s ^= in.sh[r];
+    z ^= in.zh[r];
+  }
+  s1_store<C>(red, blk, g, w, s, z);
+}
+
+// the FP codec's stage 1 (k_sum_fp over a receive buffer): the same 16-byte
+// chunks, four per lane, W loads each, one store
+template <int W>
+__global__ __launch_bounds__(kThreads) void k_sum_pattern(InPtrs xs, uint8_t* red,
+                                                          uint32_t nchunks, uint64_t tstride) {
+  const uint32_t base = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
+  u32x4 q[kPerLane][W];
+#pragma unroll
+  for (int j = 0; j < kPerLane; j++) {
+    const uint32_t c = base + j * kThreads;
+    const uint64_t off = fp_chunk<true>(tstride, c < nchunks ? c : 0u);
+#pragma unroll
+    for (int r = 0; r < W; r++)
+      q[j][r] = ld_in<kStage1>(reinterpret_cast<const u32x4*>(xs.p[r] + off));
+  }
+#pragma unroll
+  for (int j = 0; j < kPerLane; j++) {
+    const uint32_t c = base + j * kThreads;
+    if (c >= nchunks) break;
+    u32x4 o = q[j][0];
+#pragma unroll
+    for (int r = 1; r < W; r++) o ^= q[j][r];
+    st_out<kStage1>(reinterpret_cast<u32x4*>(red) + c, o);
+  }
+}
+
+size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <int C, int W>
+void launch(const InPtrs& in, uint8_t* red, size_t n, hipStream_t st) {
+  const size_t nb = (n + 31) / 32;
+  if constexpr (C == kFP) {
+    const uint32_t nc = (uint32_t)(n / 8);
+    hipLaunchKernelGGL((k_sum_pattern<W>), dim3((nc + kThreads * kPerLane - 1) /
+                                                (kThreads * kPerLane)),
+                       dim3(kThreads), 0, st, in, red, nc,
+                       (uint64_t)W * kTileBlocks * 64);
+  } else {
+    using T = CodecT<C>;
+    const size_t off_s = a256(nb * T::block_bytes);
+    const size_t off_z = a256(off_s + 2 * nb);
+    const uint64_t tile = (uint64_t)kTileBlocks * (T::block_bytes + 2 + (T::asym ? 2 : 0));
+    const Geo g{(uint32_t)n, (uint32_t)nb, (uint32_t)off_s, (uint32_t)off_z, W * tile};
+    hipLaunchKernelGGL((k_stage1_pattern<C, W>), dim3((unsigned)((nb + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, st, in, red, (uint32_t)nb, g);
+  }
+}
+
+template <int C>
+void by_w(int W, const InPtrs& in, uint8_t* red, size_t n, hipStream_t st) {
+  if (W == 2) launch<C, 2>(in, red, n, st);
+  if (W == 4) launch<C, 4>(in, red, n, st);
+  if (W == 8) launch<C, 8>(in, red, n, st);
+}
+
+}  // namespace
+}  // namespace qr
+
+extern "C" {
+
+/* The stage-1 access pattern over a receive buffer `recv` of W ranks (as
+ * qr_quantize_recv writes it) into `reduced` (a wire image): the loads and
+ * stores of qr_reduce_recv over all blocks, no arithmetic.  Returns 0, or -1
+ * for an unsupported codec or W, a null or unaligned pointer, or a size that
+ * is not a positive multiple of 8 elements; -6 for a failed launch. */
+int qrp_stage1_pattern(int codec, int W, const void* recv, size_t n, void* reduced,
+                       void* stream) {
+  using namespace qr;
+  if (!(W == 2 || W == 4 || W == 8) || n == 0 || n % 8 != 0 || n > QR_MAX_BYTES / 2 ||
+      recv == nullptr || reduced == nullptr || ((uintptr_t)recv & 15u) != 0 ||
+      ((uintptr_t)reduced & 15u) != 0)
+    return -1;
+  const size_t cb = codec == QR_FP ? 64 : (codec & 7) == QR_Q6 ? 24 : (codec & 7) == QR_Q4 ? 16 : 32;
+  const size_t tile = (size_t)kTileBlocks * (codec == QR_FP ? cb : cb + 2 + ((codec & 8) ? 2 : 0));
+  InPtrs in{};
+  for (int r = 0; r < W; r++) in.p[r] = static_cast<const uint8_t*>(recv) + (size_t)r * tile;
+  uint8_t* red = static_cast<uint8_t*>(reduced);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  switch (codec) {
+    case QR_FP: by_w<kFP>(W, in, red, n, st); break;
+    case QR_Q8: by_w<kQ8>(W, in, red, n, st); break;
+    case QR_Q6: by_w<kQ6>(W, in, red, n, st); break;
+    case QR_Q4: by_w<kQ4>(W, in, red, n, st); break;
+    case QR_FP8: by_w<kFP8>(W, in, red, n, st); break;
+    case QR_Q8_ASYM: by_w<kQ8A>(W, in, red, n, st); break;
+    case QR_Q6_ASYM: by_w<kQ6A>(W, in, red, n, st); break;
+    case QR_Q4_ASYM: by_w<kQ4A>(W, in, red, n, st); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+}  // extern "C"

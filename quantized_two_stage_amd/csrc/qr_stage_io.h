@@ -1,0 +1,170 @@
+// qr_stage_io.h -- launch geometry, wire-data addressing and the stage-1
+// loads and stores of the gfx950 kernels, shared by qr_kernels.hip and the
+// benchmark's access-pattern reference (qr_pattern.hip), so that the
+// reference issues exactly the loads and stores of the stage-1 kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qr_device.h"
+#include "qr_internal.h"
+
+namespace qr {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPerLane = 4;        // quarters / chunks per lane (k_quantize,
+                                   // k_dequant and the FP kernels)
+
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X):
+// QR_NT_STORE bit mask of the stages (1 = stage 0, 2 = stage 1, 4 = stage 2)
+//             whose streamed outputs are written with non-temporal stores.
+//             Default 5: the wire images of stage 0 (read once, by another
+//             rank) and the outputs of stage 2 (the result).  Lines written
+//             through the caches stay dirty there and the next kernel pays
+//             for their write-back; stage 1's reduced image is kept cached
+//             because stage 2 reads it W times.
+// QR_NT_LOAD  bit mask of the stages whose read-once inputs are loaded with
+//             non-temporal loads (default none: no gain measured).
+#ifndef QR_NT_STORE
+#define QR_NT_STORE 5
+#endif
+#ifndef QR_NT_LOAD
+#define QR_NT_LOAD 0
+#endif
+constexpr int kStage0 = 1, kStage1 = 2, kStage2 = 4;
+constexpr int kKeep = 0;           // store policy: always through the caches
+
+template <int Stage, typename V>
+__device__ __forceinline__ void st_out(V* p, V v) {
+  if constexpr ((QR_NT_STORE & Stage) != 0)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+template <int Stage, typename V>
+__device__ __forceinline__ V ld_in(const V* p) {
+  if constexpr ((QR_NT_LOAD & Stage) != 0)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+struct Geo {
+  uint32_t n;        // elements per rank
+  uint32_t nb;       // blocks per rank
+  uint32_t off_s;    // scale plane offset
+  uint32_t off_z;    // zero plane offset
+  uint64_t tstride;  // receive buffer: bytes from one tile of a rank to its next (W tiles)
+};
+
+// Byte offsets of block blk's codes, scale and zero from a rank's base
+// pointer.  Recv == false: the planar wire image (codes at blk * CB, scales
+// and zeros in their planes).  Recv == true: the rank's tiles in the receive
+// buffer, the base being its first tile; tile t = blk / kTileBlocks starts
+// t * tstride further and holds kTileBlocks blocks' codes, then their scales,
+// then their zeros.  FP (raw data) uses code() alone, with CB = 64.
+template <int CB, bool Recv>
+struct WireAt {
+  static constexpr uint32_t kTB = kTileBlocks;
+  __device__ static __forceinline__ uint64_t tile(const Geo& g, uint32_t blk) {
+    return (uint64_t)(blk / kTB) * g.tstride;
+  }
+  __device__ static __forceinline__ uint64_t code(const Geo& g, uint32_t blk) {
+    if constexpr (Recv) return tile(g, blk) + (blk % kTB) * (uint32_t)CB;
+    return (uint64_t)blk * CB;
+  }
+  __device__ static __forceinline__ uint64_t scale(const Geo& g, uint32_t blk) {
+    if constexpr (Recv) return tile(g, blk) + kTB * CB + (blk % kTB) * 2u;
+    return g.off_s + (uint64_t)blk * 2;
+  }
+  __device__ static __forceinline__ uint64_t zero(const Geo& g, uint32_t blk) {
+    if constexpr (Recv) return tile(g, blk) + kTB * (CB + 2) + (blk % kTB) * 2u;
+    return g.off_z + (uint64_t)blk * 2;
+  }
+};
+template <int C, bool Recv>
+using At = WireAt<CodecT<C>::block_bytes, Recv>;
+
+__device__ __forceinline__ uint32_t ld_u16(const uint8_t* p) {
+  return *reinterpret_cast<const uint16_t*>(p);
+}
+__device__ __forceinline__ void st_u16(uint8_t* p, uint32_t v) {
+  *reinterpret_cast<uint16_t*>(p) = (uint16_t)v;
+}
+
+// Byte offset of 16-byte chunk c of a rank's raw data (the FP codec's wire):
+// planar, or in the rank's tiles of the receive buffer (a tile holds the
+// kTileBlocks * 4 chunks of its blocks).
+template <bool Recv>
+__device__ __forceinline__ uint64_t fp_chunk(uint64_t tstride, uint32_t c) {
+  constexpr uint32_t kTC = kTileBlocks * 4;
+  if constexpr (Recv) return (uint64_t)(c / kTC) * tstride + (c % kTC) * 16u;
+  return (uint64_t)c * 16;
+}
+
+// the W code blocks and scales (and zeros) of one block index
+template <int C, int W>
+struct S1In {
+  uint32_t cw[W][CodecT<C>::words];
+  uint32_t sh[W], zh[W];     // binary16 scale and zero bits
+};
+
+// the W ranks' code blocks and scales (and zeros) of block blk; Recv: from
+// the ranks' tiles of the receive buffer (the W tiles of one workgroup's
+// blocks are consecutive there, so the workgroup reads one contiguous range)
+template <int C, int W, bool Recv>
+__device__ __forceinline__ void s1_load(const InPtrs& wires, uint32_t blk, const Geo& g,
+                                        S1In<C, W>& in) {
+  using T = CodecT<C>;
+  const uint64_t co = At<C, Recv>::code(g, blk);
+  const uint64_t so = At<C, Recv>::scale(g, blk), zo = At<C, Recv>::zero(g, blk);
+#pragma unroll
+  for (int r = 0; r < W; r++) {
+    const uint8_t* cb = wires.p[r] + co;
+    if constexpr (T::words == 6) {
+#pragma unroll
+      for (int k = 0; k < 3; k++) {
+        const u32x2 q = ld_in<kStage1>(reinterpret_cast<const u32x2*>(cb) + k);
+        in.cw[r][2 * k] = q.x;
+        in.cw[r][2 * k + 1] = q.y;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < T::words / 4; k++) {
+        const u32x4 q = ld_in<kStage1>(reinterpret_cast<const u32x4*>(cb) + k);
+        in.cw[r][4 * k] = q.x; in.cw[r][4 * k + 1] = q.y;
+        in.cw[r][4 * k + 2] = q.z; in.cw[r][4 * k + 3] = q.w;
+      }
+    }
+    in.sh[r] = ld_u16(wires.p[r] + so);
+    in.zh[r] = T::asym ? ld_u16(wires.p[r] + zo) : 0u;
+  }
+}
+
+// the reduced block's codes w, scale s and zero z into the reduced image (a
+// planar wire image)
+template <int C>
+__device__ __forceinline__ void s1_store(uint8_t* red, uint32_t blk, const Geo& g,
+                                         const uint32_t (&w)[CodecT<C>::words], uint32_t s,
+                                         uint32_t z) {
+  using T = CodecT<C>;
+  uint8_t* cb = red + At<C, false>::code(g, blk);
+  const uint64_t so = At<C, false>::scale(g, blk), zo = At<C, false>::zero(g, blk);
+  if constexpr (T::words == 6) {
+#pragma unroll
+    for (int k = 0; k < 3; k++)
+      st_out<kStage1>(reinterpret_cast<u32x2*>(cb) + k, u32x2{w[2 * k], w[2 * k + 1]});
+  } else {
+#pragma unroll
+    for (int k = 0; k < T::words / 4; k++)
+      st_out<kStage1>(reinterpret_cast<u32x4*>(cb) + k,
+                      u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]});
+  }
+  st_u16(red + so, s);
+  if constexpr (T::asym) st_u16(red + zo, z);
+}
+
+}  // namespace
+}  // namespace qr

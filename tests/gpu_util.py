@@ -201,3 +201,42 @@ def assert_recv_equal(got, wires, codec, n, what, fill=None):
     if fill is not None:
         assert np.all(got[~mask] == fill), (what, "receive-buffer padding written")
 
+
+def oracle_threads():
+    """host threads for the oracle: the CPUs this process may use, at most 16"""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_whole(codec, dtype, xs_np, threads=None):
+    """The oracle over whole buffers, split by block range over host threads
+    (the oracle is called on each range; ctypes releases the GIL): the W
+    planar wire images, the reduced image, and the output every rank gets
+    (stage 2 dequantizes the one reduced image on every rank)."""
+    import threading
+    O.lib()                  # loaded once, before the threads
+    W, n = len(xs_np), xs_np[0].size
+    nb = (n + 31) // 32
+    T = threads or oracle_threads()
+    bounds = np.linspace(0, nb, T + 1).astype(np.int64)
+    wb = O.wire_bytes(codec, n)
+    wires = [np.zeros(wb, np.uint8) for _ in range(W)]
+    red = np.zeros(wb, np.uint8)
+    y = np.zeros(n, np.uint16)
+
+    def par(fn):
+        ts = [threading.Thread(target=fn, args=(int(bounds[i]), int(bounds[i + 1])))
+              for i in range(T) if bounds[i] < bounds[i + 1]]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+
+    def q(lo, hi):
+        for r in range(W):
+            O.quantize(codec, dtype, xs_np[r], lo, hi, wire=wires[r])
+    par(q)
+    par(lambda lo, hi: O.stage1(codec, dtype, wires, n, lo, hi, reduced=red))
+    par(lambda lo, hi: O.dequantize(codec, dtype, red, n, lo, hi, y=y))
+    return wires, red, y
+

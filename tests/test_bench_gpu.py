@@ -1,6 +1,6 @@
-"""bench.py's output contract, on the GPU: a short run prints one JSON line
-with every field the benchmark driver reads (metric, value, unit, steps,
-timing, config, the roofline of the dominant kernel and the CPU oracle
+"""bench.py's output contract, on the GPU: a short run prints one short JSON
+line with every field the benchmark driver reads (metric, value, unit, steps,
+timing, config, the roofline of the stage-1 kernel and the CPU oracle
 baseline), with values of the right kind."""
 import json
 import os
@@ -15,13 +15,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_bench_prints_the_contract_line():
-    print("running bench.py --steps 2 --warmup 1 --no-extra --no-cold", flush=True)
+    print("running bench.py --steps 2 --warmup 1 --cold-reps 1", flush=True)
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "2",
-                          "--warmup", "1", "--no-extra", "--no-cold", "--cpu-sample", "65536"],
+                          "--warmup", "1", "--cold-reps", "1", "--cpu-sample", "65536"],
                          capture_output=True, text=True, timeout=240, cwd=ROOT)
     assert res.returncode == 0, res.stderr[-3000:]
     lines = [ln for ln in res.stdout.splitlines() if ln.strip()]
     assert len(lines) == 1, res.stdout[-2000:]
+    assert len(lines[0]) < 6000, len(lines[0])       # the driver keeps a few KB of stdout
     d = json.loads(lines[0])
     for key, kind in (("metric", str), ("value", float), ("unit", str), ("n_gpus", int),
                       ("steps", int), ("warmup", int), ("ms_per_step", float),
@@ -37,6 +38,9 @@ def test_bench_prints_the_contract_line():
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert 0 < r["achieved"] and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-9
     assert r["traffic"] is None or r["traffic"] > 0
+    assert r["frac"] == min(r["per_codec_frac"].values()) or \
+        abs(r["frac"] - min(r["per_codec_frac"].values())) < 1e-4
+    assert set(r["per_codec_frac"]) == set(r["pattern_frac"])
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1
     assert isinstance(c["unit"], str) and isinstance(c["sample"], str)

@@ -42,8 +42,9 @@ def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
 
 
 def test_min_sizes_takes_the_size_from_which_the_lead_holds():
-    def pt(one, q4, q8):
-        return {"1stage": {"us": one}, "q4": {"us": q4}, "q8": {"us": q8}}
+    def pt(one, q4, q8, spread=0.0):
+        return {"1stage": {"us": one, "spread": spread}, "q4": {"us": q4, "spread": spread},
+                "q8": {"us": q8, "spread": spread}}
     sweep = {"W2": {"4096": pt(5.0, 5.1, 5.2),
                     "8388608": pt(12.0, 11.0, 13.0),     # q4 ahead, q8 behind
                     "16777216": pt(20.0, 21.0, 19.0),    # q4 behind again, q8 ahead
@@ -53,3 +54,21 @@ def test_min_sizes_takes_the_size_from_which_the_lead_holds():
     assert got == {"q4": 33554432, "q8": 16777216}
     sweep["W2"]["67108864"]["q8"]["us"] = 90.0          # behind at the largest size
     assert bench.min_sizes(sweep)["W2"]["q8"] is None
+
+
+def test_min_sizes_counts_only_leads_beyond_the_spread():
+    def pt(one, q4, s1, s4):
+        return {"1stage": {"us": one, "spread": s1}, "q4": {"us": q4, "spread": s4}}
+    sweep = {"W8": {"2097152": pt(10.0, 9.0, 0.4, 0.4),   # 9.4 < 9.6: a lead
+                    "4194304": pt(20.0, 19.0, 0.6, 0.5),  # 19.5 < 19.4 fails: a tie
+                    "8388608": pt(40.0, 30.0, 1.0, 1.0),
+                    "16777216": pt(80.0, 60.0, 1.0, 1.0)}}
+    assert bench.min_sizes(sweep)["W8"]["q4"] == 8388608
+    sweep["W8"]["4194304"]["1stage"]["spread"] = 0.2      # 19.5 < 19.8: a lead
+    assert bench.min_sizes(sweep)["W8"]["q4"] == 2097152
+
+
+def test_stage2_hbm_bytes_read_the_reduced_image_once():
+    n, wb = 1 << 25, 18874368
+    assert bench.hbm_bytes_stage2(8, n, wb) == wb + 8 * 2 * n
+    assert bench.hbm_bytes_stage2(8, n, wb) < bench.algorithmic_bytes("stage2", 8, n, wb)

@@ -1,16 +1,17 @@
 """Parity at the workloads' full sizes, in the launch configuration the
-benchmark times (one qr_allreduce_sim call per codec), checked against the
-oracle on sampled block windows (first, last and random blocks; the oracle
-computes those blocks alone), and by properties that hold at any size: every
-rank's output is identical, inputs are untouched, and the staged entry points
-give the same wire planes and outputs as the one-call pipeline."""
+benchmark times (one qr_allreduce_sim call per codec), against the oracle run
+over the whole buffers (threaded by block range): every output element of
+every rank, every byte of the receive buffer and of the reduced image in the
+call's workspace, and the planar staged calls' wire images, all bit-exact.
+Inputs are untouched.  At the largest rank buffer the library takes (2 GiB),
+sampled block windows instead."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
-from gpu_util import (assert_within_ulp, assert_wire_blocks, dev16, host16, hostu8,
-                      sample_windows, say)
+from gpu_util import (assert_bytes_equal, assert_recv_equal, assert_within_ulp, dev16, host16,
+                      hostu8, oracle_whole, plane_slices, sample_windows, say)
 from quantized_two_stage_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -39,13 +40,18 @@ def _data(cfg, n=None):
     return _cache[key]
 
 
-def _check_full(qr, cfg, codec, n=None, windows=12, staged=True, dtype=None):
+def _planes_equal(got, want, codec, n, what):
+    for name, (a, e) in plane_slices(codec, n).items():
+        assert_bytes_equal(got[a:e], want[a:e], "%s %s" % (what, name))
+
+
+def _check_full(qr, cfg, codec, n=None, staged=True, dtype=None):
+    """one qr_allreduce_sim call against the oracle over the whole buffers"""
     c = I.CONFIGS[cfg]
     W = c["W"]
     dtype = c["dtype"] if dtype is None else dtype
     xs_np, xs = _data(cfg, n)
     n = xs_np[0].size
-    nb = (n + 31) // 32
     label = "cfg%d %s W%d n%d dtype%d" % (cfg, I.CODEC_NAMES[codec], W, n, dtype)
     say("full", label)
     ys = [torch.empty_like(xs[0]) for _ in range(W)]
@@ -53,48 +59,38 @@ def _check_full(qr, cfg, codec, n=None, windows=12, staged=True, dtype=None):
     ws.fill_(0xA7)           # no reliance on what an earlier call left there
     qr.qr_allreduce_sim(codec, xs, ys, ws, dtype=dtype)
     torch.cuda.synchronize()
-    y0 = host16(ys[0])
-    for r in range(1, W):
-        assert torch.equal(ys[r], ys[0]), (label, "rank outputs differ", r)
-    for (lo, hi) in sample_windows(nb, count=windows, seed=cfg * 100 + codec):
-        want = O.allreduce(codec, dtype, xs_np, lo, hi)[0]
-        e0, e1 = 32 * lo, min(32 * hi, n)
-        assert_within_ulp(y0[e0:e1], want[e0:e1], dtype, "%s y blocks %d..%d" % (label, lo, hi))
+    say("full", label, "oracle")
+    r_wires, r_red, r_y = oracle_whole(codec, dtype, xs_np)
+    say("full", label, "compare")
+    for r in range(W):
+        assert_within_ulp(host16(ys[r]), r_y, dtype, "%s y[%d]" % (label, r))
+    wsh = hostu8(ws)
+    rb = qr.qr_recv_bytes(W, codec, n)
+    red_at = (rb + 255) // 256 * 256
+    assert_recv_equal(wsh[:rb], r_wires, codec, n, label + " receive buffer", fill=0xA7)
+    _planes_equal(wsh[red_at:red_at + qr.qr_wire_bytes(codec, n)], r_red, codec, n,
+                  label + " reduced")
+    del ws, wsh
     if staged:
+        # the planar staged calls: W separate wire images
         wires = [qr.alloc_wire(codec, n) for _ in range(W)]
         qr.qr_quantize_ranks(codec, xs, wires, dtype=dtype)
         red = qr.alloc_wire(codec, n)
         qr.qr_reduce_stage1(codec, wires, n, red, dtype)
-        ys2 = [torch.empty_like(xs[0]) for _ in range(W)]
-        qr.qr_gather_stage2(codec, red, ys2, dtype=dtype)
         torch.cuda.synchronize()
         for r in range(W):
-            assert torch.equal(ys2[r], ys[0]), (label, "staged != one call")
-        gw = [hostu8(w) for w in wires]
-        gr = hostu8(red)
-        for (lo, hi) in sample_windows(nb, count=4, seed=cfg * 100 + codec + 1):
-            rw = [O.quantize(codec, dtype, x, lo, hi) for x in xs_np]
-            for r in range(W):
-                assert_wire_blocks(gw[r], rw[r], codec, n, lo, hi, "%s wire[%d]" % (label, r))
-            rr = O.stage1(codec, dtype, rw, n, lo, hi)
-            assert_wire_blocks(gr, rr, codec, n, lo, hi, label + " reduced")
-        del wires, red, ys2
+            _planes_equal(hostu8(wires[r]), r_wires[r], codec, n, "%s wire[%d]" % (label, r))
+        _planes_equal(hostu8(red), r_red, codec, n, label + " planar reduced")
+        del wires, red
     for r in range(W):
         assert torch.equal(xs[r], dev16(xs_np[r])), (label, "input modified")
+    del ys
+    torch.cuda.empty_cache()
 
 
 def test_config1_full(qr):
-    """4 KB per rank, W=2, Q8: small enough to compare everything."""
-    xs_np, xs = _data(1)
-    n = xs_np[0].size
-    ys = [torch.empty_like(xs[0]) for _ in range(2)]
-    ws = qr.alloc_workspace(2, O.Q8, n)
-    say("cfg1")
-    qr.qr_allreduce_sim(O.Q8, xs, ys, ws, dtype=O.FP16)
-    torch.cuda.synchronize()
-    want = O.allreduce(O.Q8, O.FP16, xs_np)
-    for r in range(2):
-        assert_within_ulp(host16(ys[r]), want[r], O.FP16, "cfg1 y")
+    """4 KB per rank, W=2, Q8"""
+    _check_full(qr, 1, O.Q8)
 
 
 @pytest.mark.parametrize("codec", I.CONFIGS[2]["codecs"],
@@ -105,18 +101,7 @@ def test_config2_full(qr, codec):
 
 @pytest.mark.parametrize("n", I.CONFIGS[3]["sizes"])
 def test_config3_sweep(qr, n):
-    if n <= 1 << 16:                       # whole-buffer comparison
-        xs_np, xs = _data(3, n)
-        ys = [torch.empty_like(xs[0]) for _ in range(4)]
-        ws = qr.alloc_workspace(4, O.Q4A, n)
-        say("cfg3 full compare n", n)
-        qr.qr_allreduce_sim(O.Q4A, xs, ys, ws, dtype=O.BF16)
-        torch.cuda.synchronize()
-        want = O.allreduce(O.Q4A, O.BF16, xs_np)
-        for r in range(4):
-            assert_within_ulp(host16(ys[r]), want[r], O.BF16, "cfg3 n%d y" % n)
-    else:
-        _check_full(qr, 3, O.Q4A, n=n, windows=6, staged=(n == 1 << 25))
+    _check_full(qr, 3, O.Q4A, n=n, staged=(n in (1 << 11, 1 << 25)))
 
 
 def test_config4_full(qr):
@@ -161,7 +146,7 @@ def test_max_size(qr, codec):
 def test_cast_option_full(qr, cfg, codec):
     """the bf16 workloads with the bf16 -> fp16 cast option (buffer type 2):
     64 MB (configuration 3's largest size) and 16 MB W=8"""
-    _check_full(qr, cfg, codec, n=(1 << 25) if cfg == 3 else None, windows=8,
+    _check_full(qr, cfg, codec, n=(1 << 25) if cfg == 3 else None, staged=False,
                 dtype=O.BF16_VIA_FP16)
 
 
@@ -173,9 +158,8 @@ FUSED_EDGE = 2 * 1024 * 1024          # elements: 4 MiB per rank, the single-lau
                          ids=[I.CODEC_NAMES[c] for c in (O.FP, O.FP8, O.Q8, O.Q6, O.Q4, O.Q8A,
                                                            O.Q6A, O.Q4A)])
 def test_sim_launch_paths(qr, codec, n):
-    """qr_allreduce_sim at the size where it switches from one launch to
-    three, W=2 fp16, W=4 bf16 and W=8 bf16: every element equals the staged
-    calls', sampled blocks equal the oracle's"""
-    _check_full(qr, 2, codec, n=n, windows=6)
-    _check_full(qr, 3, codec, n=n, windows=6)
-    _check_full(qr, 4, codec, n=n, windows=6)
+    """qr_allreduce_sim on both sides of the size where it switches from one
+    launch to three, W=2 fp16, W=4 bf16 and W=8 bf16"""
+    _check_full(qr, 2, codec, n=n, staged=False)
+    _check_full(qr, 3, codec, n=n, staged=False)
+    _check_full(qr, 4, codec, n=n, staged=False)

@@ -36,13 +36,21 @@ def _case(k):
     return codec, dtype, W, n, cfg, owner
 
 
-def _inputs(cfg, W, n, dtype, k):
+def _inputs(cfg, W, n, dtype, k, codec):
     bits = I.BF16 if dtype else I.FP16
     xs = [I.to_bits(I.draw(cfg, r + 100 * (k + 1), n), bits) for r in range(W)]
     if dtype == O.BF16_VIA_FP16:
-        # the cast option's contract: bf16 inputs within the binary16 range
-        xs = [np.where((x & 0x7F80) >= 0x4780, x & 0x807F | 0x4700, x).astype(np.uint16)
-              for x in xs]
+        # The cast option's contract: for the quantized codecs, bf16 inputs
+        # within the binary16 range (beyond it they become inf on entry).  The
+        # FP codec and the one-stage allreduce carry an inf through, so there
+        # only negative magnitudes of 2^16 and more are brought into range:
+        # positive ones become +inf and every sum holding one is +inf (+inf
+        # plus -inf, a NaN, is outside the contract).
+        for i, x in enumerate(xs):
+            big = (x & 0x7F80) >= 0x4780
+            if codec == O.FP:
+                big &= (x & 0x8000) != 0
+            xs[i] = np.where(big, x & 0x807F | 0x4700, x).astype(np.uint16)
     return xs
 
 
@@ -53,7 +61,7 @@ def test_random_cases(qr, block):
         label = "case %d: codec %d dtype %d W %d n %d gen %d owner %d" % (
             k, codec, dtype, W, n, cfg, owner)
         say(label)
-        xs_np = _inputs(cfg, W, n, dtype, k)
+        xs_np = _inputs(cfg, W, n, dtype, k, codec)
         xs = [dev16(x) for x in xs_np]
         want_wires = [O.quantize(codec, dtype, x) for x in xs_np]
         want_red = O.stage1(codec, dtype, want_wires, n)
