@@ -171,7 +171,9 @@ class Cold:
 
     def __init__(self, torch, stream, reps):
         self.torch, self.stream, self.reps = torch, stream, reps
-        self.flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        # binary32, so that sum() is one reduction reading the 1 GiB (an
+        # integer sum would first write a widened copy: dirty lines)
+        self.flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         self.ev = HipEvents(2)
 
     def us(self, fn, reps=None):
