@@ -238,8 +238,8 @@ __device__ __forceinline__ void pack_bits(const uint32_t (&c)[N],
 // Scaled values t[i] (v*inv, or (v-z)*inv) -> packed codes.  `sat` marks a
 // block whose scale or zero saturated at the binary16 range, the only case in
 // which t can leave the code range (see block_params): then t is clamped
-// first, as the definition does; otherwise the clamp is the identity and
-// skipped.
+// first, as the definition does (one v_med3_f32: t is never NaN, the inputs
+// being finite), otherwise the clamp is the identity and skipped.
 template <int C, int N>
 __device__ __forceinline__ void encode(float (&t)[N], bool sat,
                                        uint32_t (&w)[(N * CodecT<C>::bits + 31) / 32]) {
@@ -247,7 +247,7 @@ __device__ __forceinline__ void encode(float (&t)[N], bool sat,
   if (sat) {
     const float lo = T::asym ? 0.0f : -T::qmax;
 #pragma unroll
-    for (int i = 0; i < N; i++) t[i] = fminf(fmaxf(t[i], lo), T::qmax);
+    for (int i = 0; i < N; i++) t[i] = __builtin_amdgcn_fmed3f(t[i], lo, T::qmax);
   }
   if constexpr (T::fp8) {
 #pragma unroll

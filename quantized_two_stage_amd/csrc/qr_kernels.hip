@@ -274,9 +274,9 @@ __device__ __forceinline__ bool tile_full(uint32_t wg, uint32_t n) {
 // consecutive tiles of the buffer (the rank-major order writes it at a
 // stride of W tiles, which made stage 0 4-9% slower at W=8, 64 MB per rank).
 template <bool Recv>
-__device__ __forceinline__ void s0_item(int W, uint32_t& tile, int& r) {
+__device__ __forceinline__ void s0_item(int W, uint32_t tile0, uint32_t& tile, int& r) {
   if constexpr (Recv) {
-    tile = blockIdx.x / (uint32_t)W;
+    tile = tile0 + blockIdx.x / (uint32_t)W;
     r = (int)(blockIdx.x % (uint32_t)W);
   } else {
     tile = blockIdx.x;
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires,
   static_assert(kThreads * kPerLane / 4 == kTileBlocks, "a workgroup's blocks are one tile");
   uint32_t tile;
   int r;
-  s0_item<Recv>(W, tile, r);
+  s0_item<Recv>(W, g.tile0, tile, r);
   const uint32_t q0 = tile * (kThreads * kPerLane) + threadIdx.x;
   u32x4 raw[4];
   if (tile_full(tile, g.n)) {
@@ -310,12 +310,13 @@ __global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires,
 // tiles of the receive buffer
 template <int Stage, int Din, int Dout, bool Recv>
 __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
-                                                   uint32_t nchunks, uint64_t tstride, int W) {
+                                                   uint32_t nchunks, uint32_t tstride,
+                                                   uint32_t tile0, int W) {
   static_assert(kThreads * kPerLane == kTileBlocks * 4, "a workgroup's chunks are one tile");
   constexpr int kS = Stage == 0 ? kStage0 : kStage2;
   uint32_t tile;
   int r;
-  s0_item<Recv>(W, tile, r);
+  s0_item<Recv>(W, tile0, tile, r);
   const u32x4* s = reinterpret_cast<const u32x4*>(src.p[r]);
   uint8_t* d = dst.p[r];
   const uint32_t base = tile * (kThreads * kPerLane) + threadIdx.x;
@@ -333,7 +334,8 @@ __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
       for (int k = 0; k < 4; k++)
         q[j][k] = st16x2<Dout>(ld16<Din>(q[j][k] & 0xffffu), ld16<Din>(q[j][k] >> 16));
     }
-    if (c < nchunks) st_out<kS>(reinterpret_cast<u32x4*>(d + fp_chunk<Recv>(tstride, c)), q[j]);
+    if (c < nchunks)
+      st_out<kS>(reinterpret_cast<u32x4*>(d + fp_chunk<Recv>(tstride, tile0, c)), q[j]);
   }
 }
 
@@ -426,13 +428,13 @@ __global__ __launch_bounds__(kThreads) void k_stage1(InPtrs wires, uint8_t* red,
 template <int D, int W, int Stage, bool Recv>
 __global__ __launch_bounds__(kThreads) void k_sum_fp(InPtrs xs, OutPtrs outs,
                                                      uint32_t c_lo, uint32_t c_hi,
-                                                     uint64_t tstride) {
+                                                     uint32_t tstride, uint32_t tile0) {
   const uint32_t base = c_lo + blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
   u32x4 q[kPerLane][W];
 #pragma unroll
   for (int j = 0; j < kPerLane; j++) {
     const uint32_t c = base + j * kThreads;
-    const uint64_t off = fp_chunk<Recv>(tstride, c < c_hi ? c : c_lo);
+    const uint32_t off = fp_chunk<Recv>(tstride, tile0, c < c_hi ? c : c_lo);
 #pragma unroll
     for (int r = 0; r < W; r++)
       q[j][r] = ld_in<kStage1>(reinterpret_cast<const u32x4*>(xs.p[r] + off));
@@ -570,8 +572,8 @@ __device__ __forceinline__ void fused_tile(const InPtrs& xs, const OutPtrs& wire
     const uint32_t blk = ql >> 2;
     uint32_t w[W][IO::nw];
     float sc[W], zc[W];
-    const uint64_t co = At<C, true>::code(g, blk);
-    const uint64_t so = At<C, true>::scale(g, blk), zo = At<C, true>::zero(g, blk);
+    const uint32_t co = At<C, true>::code(g, blk);
+    const uint32_t so = At<C, true>::scale(g, blk), zo = At<C, true>::zero(g, blk);
 #pragma unroll
     for (int r = 0; r < W; r++) {
       IO::load(wires.p[r] + co, ql & 3, w[r]);
@@ -624,12 +626,12 @@ __global__ __launch_bounds__(kThreads) void k_fused(InPtrs xs, OutPtrs wires, ui
 template <int D, int W>
 __global__ __launch_bounds__(kThreads) void k_fused_fp(InPtrs xs, OutPtrs wires, uint8_t* red,
                                                        OutPtrs ys, uint32_t nchunks,
-                                                       uint64_t tstride) {
+                                                       uint32_t tstride) {
   constexpr int Dw = D == kBF16H ? kF16 : D;      // the wire's element type
   constexpr int Dx = D == kBF16H ? kBF16 : D;     // the buffers' element type
   const uint32_t c = blockIdx.x * kThreads + threadIdx.x;
   const bool has = c < nchunks;
-  const uint64_t wo = fp_chunk<true>(tstride, c);
+  const uint32_t wo = fp_chunk<true>(tstride, 0u, c);
   if (has) {
 #pragma unroll
     for (int r = 0; r < W; r++) {
@@ -676,33 +678,59 @@ __global__ __launch_bounds__(kThreads) void k_fused_fp(InPtrs xs, OutPtrs wires,
 // ---------------------------------------------------------------------------
 // dispatch
 
-// tstride: in the receive buffer, W tiles separate a rank's consecutive tiles
-Geo geo(const Layout& L, int W = 0, bool recv = false) {
+// tstride: in the receive buffer, W tiles separate a rank's consecutive
+// tiles; tile0: the tile the ranks' base pointers of this launch point at
+Geo geo(const Layout& L, int W = 0, bool recv = false, size_t tile0 = 0) {
   return Geo{(uint32_t)L.n, (uint32_t)L.nb, (uint32_t)L.off_s, (uint32_t)L.off_z,
-             recv ? (uint64_t)W * L.tile_bytes : 0ull};
+             recv ? (uint32_t)(W * L.tile_bytes) : 0u, (uint32_t)tile0};
 }
 
 unsigned groups(size_t items, size_t per_group) {
   return (unsigned)((items + per_group - 1) / per_group);
 }
 
+// Tiles of the receive buffer one launch takes: the kernels address a rank's
+// tiles by 32-bit offsets from the launch's first tile, so a launch spans at
+// most (2^32 - 1) / (W * tile_bytes) - 1 tiles (every workload of up to
+// about 1 GiB per rank buffer is one launch).
+size_t recv_tiles_per_launch(int W, const Layout& L) {
+  const uint64_t stride = (uint64_t)W * L.tile_bytes;
+  return (size_t)(0xffffffffull / stride - 1);
+}
+
+// the ranks' base pointers at tile t0 of a receive buffer
+template <typename P>
+P at_tile(const P& base, int W, const Layout& L, size_t t0) {
+  P out = base;
+  for (int r = 0; r < W; r++) out.p[r] = base.p[r] + t0 * (size_t)W * L.tile_bytes;
+  return out;
+}
+
 template <int C, int D, int W, bool Recv>
 void s1_launch(const InPtrs& wires, uint8_t* red, size_t blk_lo, size_t blk_hi,
                const Layout& L, hipStream_t st) {
-  if constexpr (C == kFP) {
-    // block-granular range in 8-element chunks (a partial last block holds
-    // fewer than 4 chunks)
-    const uint32_t c_lo = (uint32_t)(4 * blk_lo);
-    const uint32_t c_hi = (uint32_t)(blk_hi * 4 < L.n / 8 ? blk_hi * 4 : L.n / 8);
-    OutPtrs out{};
-    out.p[0] = red;
-    hipLaunchKernelGGL((k_sum_fp<D, W, kStage1, Recv>),
-                       dim3(groups(c_hi - c_lo, kThreads * kPerLane)), dim3(kThreads), 0, st,
-                       wires, out, c_lo, c_hi, geo(L, W, Recv).tstride);
-  } else {
-    hipLaunchKernelGGL((k_stage1<C, D, W, Recv>), dim3(groups(blk_hi - blk_lo, kThreads)),
-                       dim3(kThreads), 0, st, wires, red, (uint32_t)blk_lo,
-                       (uint32_t)blk_hi, geo(L, W, Recv));
+  // launches over tile ranges [t0, t1) of the receive buffer (one range for
+  // W separate wire images, whose offsets always fit)
+  const size_t per = Recv ? recv_tiles_per_launch(W, L) : L.ntiles + 1;
+  for (size_t t0 = blk_lo / kTileBlocks; t0 * kTileBlocks < blk_hi; t0 += per) {
+    const size_t lo = blk_lo > t0 * kTileBlocks ? blk_lo : t0 * kTileBlocks;
+    const size_t hi = blk_hi < (t0 + per) * kTileBlocks ? blk_hi : (t0 + per) * kTileBlocks;
+    const InPtrs w = Recv ? at_tile(wires, W, L, t0) : wires;
+    const Geo g = geo(L, W, Recv, Recv ? t0 : 0);
+    if constexpr (C == kFP) {
+      // block-granular range in 8-element chunks (a partial last block
+      // holds fewer than 4 chunks)
+      const uint32_t c_lo = (uint32_t)(4 * lo);
+      const uint32_t c_hi = (uint32_t)(hi * 4 < L.n / 8 ? hi * 4 : L.n / 8);
+      OutPtrs out{};
+      out.p[0] = red;
+      hipLaunchKernelGGL((k_sum_fp<D, W, kStage1, Recv>),
+                         dim3(groups(c_hi - c_lo, kThreads * kPerLane)), dim3(kThreads), 0, st,
+                         w, out, c_lo, c_hi, g.tstride, g.tile0);
+    } else {
+      hipLaunchKernelGGL((k_stage1<C, D, W, Recv>), dim3(groups(hi - lo, kThreads)),
+                         dim3(kThreads), 0, st, w, red, (uint32_t)lo, (uint32_t)hi, g);
+    }
   }
 }
 
@@ -728,19 +756,25 @@ void s1_by_w(int W, const InPtrs& wires, bool recv, uint8_t* red, size_t lo, siz
 
 template <int C, int D, bool Recv>
 void q_launch(int W, const InPtrs& xs, const OutPtrs& wires, const Layout& L, hipStream_t st) {
-  if constexpr (C == kFP) {
-    // the FP wire holds the buffer's raw elements (binary16 under the cast)
-    constexpr int Dw = D == kBF16H ? kF16 : D;
-    constexpr int Din = D == kBF16H ? kBF16 : D;
-    const unsigned tiles = groups(L.n / 8, kThreads * kPerLane);
-    const dim3 grid = Recv ? dim3(tiles * W) : dim3(tiles, W);
-    hipLaunchKernelGGL((k_copy<0, Din, Dw, Recv>), grid, dim3(kThreads), 0, st, xs, wires,
-                       (uint32_t)(L.n / 8), geo(L, W, Recv).tstride, W);
-  } else {
-    const unsigned tiles = groups(4 * L.nb, kThreads * kPerLane);
-    const dim3 grid = Recv ? dim3(tiles * W) : dim3(tiles, W);
-    hipLaunchKernelGGL((k_quantize<C, D, Recv>), grid, dim3(kThreads), 0, st, xs, wires,
-                       geo(L, W, Recv), W);
+  // a workgroup quantizes one tile of one rank; into the receive buffer over
+  // tile ranges [t0, t1) as for stage 1
+  const size_t tiles = C == kFP ? groups(L.n / 8, kThreads * kPerLane)
+                                : groups(4 * L.nb, kThreads * kPerLane);
+  const size_t per = Recv ? recv_tiles_per_launch(W, L) : tiles + 1;
+  for (size_t t0 = 0; t0 < tiles; t0 += per) {
+    const size_t nt = tiles - t0 < per ? tiles - t0 : per;
+    const OutPtrs w = Recv ? at_tile(wires, W, L, t0) : wires;
+    const Geo g = geo(L, W, Recv, Recv ? t0 : 0);
+    const dim3 grid = Recv ? dim3((unsigned)(nt * W)) : dim3((unsigned)nt, W);
+    if constexpr (C == kFP) {
+      // the FP wire holds the buffer's raw elements (binary16 under the cast)
+      constexpr int Dw = D == kBF16H ? kF16 : D;
+      constexpr int Din = D == kBF16H ? kBF16 : D;
+      hipLaunchKernelGGL((k_copy<0, Din, Dw, Recv>), grid, dim3(kThreads), 0, st, xs, w,
+                         (uint32_t)(L.n / 8), g.tstride, g.tile0, W);
+    } else {
+      hipLaunchKernelGGL((k_quantize<C, D, Recv>), grid, dim3(kThreads), 0, st, xs, w, g, W);
+    }
   }
 }
 
@@ -763,7 +797,7 @@ void dq_dispatch(int W, const uint8_t* wire, const OutPtrs& ys, const Layout& L,
     constexpr int Dout = D == kBF16H ? kBF16 : D;
     hipLaunchKernelGGL((k_copy<2, Dw, Dout, false>),
                        dim3(groups(L.n / 8, kThreads * kPerLane), W), dim3(kThreads), 0, st,
-                       src, ys, (uint32_t)(L.n / 8), 0ull, W);
+                       src, ys, (uint32_t)(L.n / 8), 0u, 0u, W);
   } else {
     hipLaunchKernelGGL((k_dequant<C, D>), dim3(groups(L.n / 8, kThreads * kPerLane), W),
                        dim3(kThreads), 0, st, wire, ys, geo(L));
@@ -847,7 +881,7 @@ template <int D, int W>
 void oneshot_launch(const InPtrs& xs, const OutPtrs& ys, size_t n, hipStream_t st) {
   const uint32_t nc = (uint32_t)(n / 8);
   hipLaunchKernelGGL((k_sum_fp<D, W, kStage2, false>), dim3(groups(nc, kThreads * kPerLane), W),
-                     dim3(kThreads), 0, st, xs, ys, 0u, nc, 0ull);
+                     dim3(kThreads), 0, st, xs, ys, 0u, nc, 0u, 0u);
 }
 
 template <int D>

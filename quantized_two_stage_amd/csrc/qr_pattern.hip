@@ -43,13 +43,13 @@ __global__ __launch_bounds__(kThreads) void k_stage1_pattern(InPtrs wires, uint8
 // chunks, four per lane, W loads each, one store
 template <int W>
 __global__ __launch_bounds__(kThreads) void k_sum_pattern(InPtrs xs, uint8_t* red,
-                                                          uint32_t nchunks, uint64_t tstride) {
+                                                          uint32_t nchunks, uint32_t tstride) {
   const uint32_t base = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
   u32x4 q[kPerLane][W];
 #pragma unroll
   for (int j = 0; j < kPerLane; j++) {
     const uint32_t c = base + j * kThreads;
-    const uint64_t off = fp_chunk<true>(tstride, c < nchunks ? c : 0u);
+    const uint32_t off = fp_chunk<true>(tstride, 0u, c < nchunks ? c : 0u);
 #pragma unroll
     for (int r = 0; r < W; r++)
       q[j][r] = ld_in<kStage1>(reinterpret_cast<const u32x4*>(xs.p[r] + off));
@@ -75,13 +75,13 @@ void launch(const InPtrs& in, uint8_t* red, size_t n, hipStream_t st) {
     hipLaunchKernelGGL((k_sum_pattern<W>), dim3((nc + kThreads * kPerLane - 1) /
                                                 (kThreads * kPerLane)),
                        dim3(kThreads), 0, st, in, red, nc,
-                       (uint64_t)W * kTileBlocks * 64);
+                       (uint32_t)(W * kTileBlocks * 64));
   } else {
     using T = CodecT<C>;
     const size_t off_s = a256(nb * T::block_bytes);
     const size_t off_z = a256(off_s + 2 * nb);
-    const uint64_t tile = (uint64_t)kTileBlocks * (T::block_bytes + 2 + (T::asym ? 2 : 0));
-    const Geo g{(uint32_t)n, (uint32_t)nb, (uint32_t)off_s, (uint32_t)off_z, W * tile};
+    const uint32_t tile = kTileBlocks * (T::block_bytes + 2 + (T::asym ? 2 : 0));
+    const Geo g{(uint32_t)n, (uint32_t)nb, (uint32_t)off_s, (uint32_t)off_z, W * tile, 0u};
     hipLaunchKernelGGL((k_stage1_pattern<C, W>), dim3((unsigned)((nb + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, st, in, red, (uint32_t)nb, g);
   }
@@ -111,6 +111,10 @@ int qrp_stage1_pattern(int codec, int W, const void* recv, size_t n, void* reduc
       recv == nullptr || reduced == nullptr || ((uintptr_t)recv & 15u) != 0 ||
       ((uintptr_t)reduced & 15u) != 0)
     return -1;
+  // one launch: the receive buffer's offsets must fit in 32 bits
+  const size_t tiles = ((n + 31) / 32 + kTileBlocks - 1) / kTileBlocks;
+  const size_t cb0 = codec == QR_FP ? 64 : (codec & 7) == QR_Q6 ? 24 : (codec & 7) == QR_Q4 ? 16 : 32;
+  if ((tiles + 1) * (size_t)W * kTileBlocks * (cb0 + 4) >= ((size_t)1 << 32)) return -1;
   const size_t cb = codec == QR_FP ? 64 : (codec & 7) == QR_Q6 ? 24 : (codec & 7) == QR_Q4 ? 16 : 32;
   const size_t tile = (size_t)kTileBlocks * (codec == QR_FP ? cb : cb + 2 + ((codec & 8) ? 2 : 0));
   InPtrs in{};

@@ -56,32 +56,37 @@ struct Geo {
   uint32_t nb;       // blocks per rank
   uint32_t off_s;    // scale plane offset
   uint32_t off_z;    // zero plane offset
-  uint64_t tstride;  // receive buffer: bytes from one tile of a rank to its next (W tiles)
+  uint32_t tstride;  // receive buffer: bytes from one tile of a rank to its next (W tiles)
+  uint32_t tile0;    // receive buffer: the tile the ranks' base pointers point at
 };
 
 // Byte offsets of block blk's codes, scale and zero from a rank's base
-// pointer.  Recv == false: the planar wire image (codes at blk * CB, scales
-// and zeros in their planes).  Recv == true: the rank's tiles in the receive
-// buffer, the base being its first tile; tile t = blk / kTileBlocks starts
-// t * tstride further and holds kTileBlocks blocks' codes, then their scales,
-// then their zeros.  FP (raw data) uses code() alone, with CB = 64.
+// pointer, in 32 bits (a uniform 64-bit base plus a 32-bit offset: the
+// loads and stores take the base in scalar registers and one offset register
+// serves every rank).  Recv == false: the planar wire image (codes at
+// blk * CB, scales and zeros in their planes; a wire image is below 4 GiB).
+// Recv == true: the rank's tiles in the receive buffer, the base being its
+// tile tile0; tile t = blk / kTileBlocks starts (t - tile0) * tstride further
+// and holds kTileBlocks blocks' codes, then their scales, then their zeros
+// (the host launches tile ranges whose offsets stay below 4 GiB).  FP (raw
+// data) uses code() alone, with CB = 64.
 template <int CB, bool Recv>
 struct WireAt {
   static constexpr uint32_t kTB = kTileBlocks;
-  __device__ static __forceinline__ uint64_t tile(const Geo& g, uint32_t blk) {
-    return (uint64_t)(blk / kTB) * g.tstride;
+  __device__ static __forceinline__ uint32_t tile(const Geo& g, uint32_t blk) {
+    return (blk / kTB - g.tile0) * g.tstride;
   }
-  __device__ static __forceinline__ uint64_t code(const Geo& g, uint32_t blk) {
+  __device__ static __forceinline__ uint32_t code(const Geo& g, uint32_t blk) {
     if constexpr (Recv) return tile(g, blk) + (blk % kTB) * (uint32_t)CB;
-    return (uint64_t)blk * CB;
+    return blk * (uint32_t)CB;
   }
-  __device__ static __forceinline__ uint64_t scale(const Geo& g, uint32_t blk) {
+  __device__ static __forceinline__ uint32_t scale(const Geo& g, uint32_t blk) {
     if constexpr (Recv) return tile(g, blk) + kTB * CB + (blk % kTB) * 2u;
-    return g.off_s + (uint64_t)blk * 2;
+    return g.off_s + blk * 2u;
   }
-  __device__ static __forceinline__ uint64_t zero(const Geo& g, uint32_t blk) {
+  __device__ static __forceinline__ uint32_t zero(const Geo& g, uint32_t blk) {
     if constexpr (Recv) return tile(g, blk) + kTB * (CB + 2) + (blk % kTB) * 2u;
-    return g.off_z + (uint64_t)blk * 2;
+    return g.off_z + blk * 2u;
   }
 };
 template <int C, bool Recv>
@@ -94,14 +99,15 @@ __device__ __forceinline__ void st_u16(uint8_t* p, uint32_t v) {
   *reinterpret_cast<uint16_t*>(p) = (uint16_t)v;
 }
 
-// Byte offset of 16-byte chunk c of a rank's raw data (the FP codec's wire):
-// planar, or in the rank's tiles of the receive buffer (a tile holds the
-// kTileBlocks * 4 chunks of its blocks).
+// Byte offset (32 bits, as above) of 16-byte chunk c of a rank's raw data
+// (the FP codec's wire): planar, or in the rank's tiles of the receive
+// buffer from its tile tile0 (a tile holds the kTileBlocks * 4 chunks of its
+// blocks).
 template <bool Recv>
-__device__ __forceinline__ uint64_t fp_chunk(uint64_t tstride, uint32_t c) {
+__device__ __forceinline__ uint32_t fp_chunk(uint32_t tstride, uint32_t tile0, uint32_t c) {
   constexpr uint32_t kTC = kTileBlocks * 4;
-  if constexpr (Recv) return (uint64_t)(c / kTC) * tstride + (c % kTC) * 16u;
-  return (uint64_t)c * 16;
+  if constexpr (Recv) return (c / kTC - tile0) * tstride + (c % kTC) * 16u;
+  return c * 16u;
 }
 
 // the W code blocks and scales (and zeros) of one block index
@@ -118,8 +124,8 @@ template <int C, int W, bool Recv>
 __device__ __forceinline__ void s1_load(const InPtrs& wires, uint32_t blk, const Geo& g,
                                         S1In<C, W>& in) {
   using T = CodecT<C>;
-  const uint64_t co = At<C, Recv>::code(g, blk);
-  const uint64_t so = At<C, Recv>::scale(g, blk), zo = At<C, Recv>::zero(g, blk);
+  const uint32_t co = At<C, Recv>::code(g, blk);
+  const uint32_t so = At<C, Recv>::scale(g, blk), zo = At<C, Recv>::zero(g, blk);
 #pragma unroll
   for (int r = 0; r < W; r++) {
     const uint8_t* cb = wires.p[r] + co;
@@ -140,6 +146,12 @@ __device__ __forceinline__ void s1_load(const InPtrs& wires, uint32_t blk, const
     }
     in.sh[r] = ld_u16(wires.p[r] + so);
     in.zh[r] = T::asym ? ld_u16(wires.p[r] + zo) : 0u;
+    // Loads issue rank by rank, and all before any arithmetic.  Loads
+    // retire in issue order, so rank 0's sum can start once its own three
+    // have landed; left to itself the scheduler groups all codes before all
+    // scales and zeros, or holds back the last ranks' loads to save
+    // registers, and either way more of the latency is exposed at W=8.
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -151,7 +163,7 @@ __device__ __forceinline__ void s1_store(uint8_t* red, uint32_t blk, const Geo& 
                                          uint32_t z) {
   using T = CodecT<C>;
   uint8_t* cb = red + At<C, false>::code(g, blk);
-  const uint64_t so = At<C, false>::scale(g, blk), zo = At<C, false>::zero(g, blk);
+  const uint32_t so = At<C, false>::scale(g, blk), zo = At<C, false>::zero(g, blk);
   if constexpr (T::words == 6) {
 #pragma unroll
     for (int k = 0; k < 3; k++)
