@@ -715,6 +715,7 @@ void s1_launch(const InPtrs& wires, uint8_t* red, size_t blk_lo, size_t blk_hi,
   for (size_t t0 = blk_lo / kTileBlocks; t0 * kTileBlocks < blk_hi; t0 += per) {
     const size_t lo = blk_lo > t0 * kTileBlocks ? blk_lo : t0 * kTileBlocks;
     const size_t hi = blk_hi < (t0 + per) * kTileBlocks ? blk_hi : (t0 + per) * kTileBlocks;
+    if (hi <= lo) continue;                       // an owner's empty chunk: no launch
     const InPtrs w = Recv ? at_tile(wires, W, L, t0) : wires;
     const Geo g = geo(L, W, Recv, Recv ? t0 : 0);
     if constexpr (C == kFP) {

@@ -242,8 +242,10 @@ def test_golden_fixtures_gpu(qr):
 def test_owner_chunks(qr, W):
     """stage 1 for each owner writes exactly its chunk; together they give
     the full reduced image.  847 blocks: at W=2 owner 1 starts at block 424,
-    off a 256-block workgroup tile, and spans full and partial tiles."""
-    for codec, n in [(c, m) for m in (32 * 37 + 16, 32 * 846 + 16)
+    off a 256-block workgroup tile, and spans full and partial tiles.  6
+    blocks: at W=4 and W=8 the last owners' chunks are empty (nothing is
+    launched and nothing written)."""
+    for codec, n in [(c, m) for m in (32 * 5 + 8, 32 * 37 + 16, 32 * 846 + 16)
                      for c in (O.FP, O.Q4, O.Q6A, O.FP8, O.Q8)]:
         xs_np = _inputs(5, W, n, O.FP16, salt=1)
         say("owners", codec, W, n)
