@@ -442,7 +442,9 @@ def measure_workload(qr, I, torch, stream, config, n=None, iters=20, cold=True, 
                      oneshot=True):
     """One workload of inputs.CONFIGS: per codec, qr_allreduce_sim timed call
     by call (median and min us, effective GB/s = 2n / time), and cold stage 1
-    through the receive buffer; the one-stage allreduce (key "1stage")."""
+    through the receive buffer beside the cold access pattern of the same
+    launch (its loads and stores alone); the one-stage allreduce (key
+    "1stage")."""
     cfg = I.CONFIGS[config]
     W = cfg["W"]
     dtype = cfg["dtype"] if dtype is None else dtype
@@ -450,6 +452,7 @@ def measure_workload(qr, I, torch, stream, config, n=None, iters=20, cold=True, 
     xs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in I.make(config, n=n)]
     ys = [torch.empty_like(xs[0]) for _ in range(W)]
     cl = Cold(torch, stream, 5) if cold else None
+    pat = Pattern() if cold else None
     out = {}
     for c in cfg["codecs"]:
         ws = qr.alloc_workspace(W, c, n)
@@ -464,8 +467,12 @@ def measure_workload(qr, I, torch, stream, config, n=None, iters=20, cold=True, 
             qr.qr_quantize_recv(c, xs, recv, dtype=dtype)
             t = cl.us(lambda: qr.qr_reduce_recv(c, W, recv, n, red, dtype))
             r["stage1_cold_us"] = t
-            r["stage1_cold_frac"] = frac(algorithmic_bytes("stage1", W, n,
-                                                           qr.qr_wire_bytes(c, n)), t)
+            ab = algorithmic_bytes("stage1", W, n, qr.qr_wire_bytes(c, n))
+            r["stage1_cold_frac"] = frac(ab, t)
+            tp = cl.us(lambda: pat.stage1(c, W, recv, n, red, stream))
+            r["pattern_cold_us"] = tp
+            r["pattern_cold_frac"] = frac(ab, tp)
+            r["stage1_vs_pattern"] = tp / t
             del recv, red
         del ws
         out[I.CODEC_NAMES[c]] = r
@@ -525,15 +532,22 @@ def measure_sweep(qr, I, torch, stream, repeats, Ws=(2, 4, 8), sizes=SWEEP_SIZES
     return res
 
 
-def min_sizes(sweep):
+MIN_SIZE_MARGIN = 0.20
+
+
+def min_sizes(sweep, margin=MIN_SIZE_MARGIN):
     """For every W and codec: the smallest rank buffer (bytes) from which the
     two-stage allreduce beats the one-stage allreduce at that size and at
-    every larger size of the sweep, a win counting only when it exceeds both
+    every larger size of the sweep; None where it does not win at the
+    largest size.  A win needs both: the two-stage median at most
+    (1 - margin) times the one-stage median, and the gap wider than both
     points' spread (two-stage median + spread below one-stage median -
-    spread); None where it does not win at the largest size.  The analogue of
-    the minimum sizes below which the pages' wrapper keeps another allreduce,
-    for this single-GPU simulation (no link time)."""
-    out = {}
+    spread).  The analogue of the minimum sizes below which the pages'
+    wrapper keeps another allreduce, for this single-GPU simulation (no link
+    time).  Also returns the deciding points (every point the rule looked
+    at) whose time ratio lies within 1% of 1 - margin, where a repeat run
+    may decide the other way."""
+    out, marginal = {}, []
     for Wk, per_size in sweep.items():
         sizes = sorted(per_size, key=int)
         row = {}
@@ -543,13 +557,17 @@ def min_sizes(sweep):
             best = None
             for sz in reversed(sizes):
                 a, b = per_size[sz][c], per_size[sz]["1stage"]
-                if a["us"] + a["spread"] < b["us"] - b["spread"]:
+                ratio = a["us"] / b["us"]
+                if abs(ratio - (1 - margin)) < 0.01:
+                    marginal.append({"W": Wk, "codec": c, "bytes": int(sz),
+                                     "ratio": round(ratio, 4)})
+                if a["us"] + a["spread"] < b["us"] - b["spread"] and ratio <= 1 - margin:
                     best = int(sz)
                 else:
                     break
             row[c] = best
         out[Wk] = row
-    return out
+    return out, marginal
 
 
 def measure_extra(args, qr, I, torch, stream, log):
@@ -580,8 +598,13 @@ def measure_extra(args, qr, I, torch, stream, log):
                              "spread = max - min of them" % args.sweep_repeats,
                       "results": measure_sweep(qr, I, torch, stream, args.sweep_repeats,
                                                dtype=dt)}
-    extra["min_sizes"] = {k: min_sizes(extra["sweep_" + k]["results"])
-                          for k in ("fp16", "bf16", "bf16_via_fp16")}
+    extra["min_sizes_rule"] = ("two-stage at most %.2f x the one-stage median and ahead "
+                               "by more than both spreads, at the size and every larger one"
+                               % (1 - MIN_SIZE_MARGIN))
+    extra["min_sizes"], extra["min_sizes_marginal"] = {}, {}
+    for k in ("fp16", "bf16", "bf16_via_fp16"):
+        extra["min_sizes"][k], extra["min_sizes_marginal"][k] = min_sizes(
+            extra["sweep_" + k]["results"])
     return extra
 
 

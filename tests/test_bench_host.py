@@ -46,14 +46,14 @@ def test_min_sizes_takes_the_size_from_which_the_lead_holds():
         return {"1stage": {"us": one, "spread": spread}, "q4": {"us": q4, "spread": spread},
                 "q8": {"us": q8, "spread": spread}}
     sweep = {"W2": {"4096": pt(5.0, 5.1, 5.2),
-                    "8388608": pt(12.0, 11.0, 13.0),     # q4 ahead, q8 behind
-                    "16777216": pt(20.0, 21.0, 19.0),    # q4 behind again, q8 ahead
-                    "33554432": pt(40.0, 30.0, 35.0),
-                    "67108864": pt(80.0, 60.0, 70.0)}}
-    got = bench.min_sizes(sweep)["W2"]
-    assert got == {"q4": 33554432, "q8": 16777216}
+                    "8388608": pt(12.0, 9.0, 13.0),      # q4 ahead, q8 behind
+                    "16777216": pt(20.0, 21.0, 15.0),    # q4 behind again, q8 ahead
+                    "33554432": pt(40.0, 30.0, 30.0),
+                    "67108864": pt(80.0, 60.0, 60.0)}}
+    got, _ = bench.min_sizes(sweep, margin=0.2)
+    assert got["W2"] == {"q4": 33554432, "q8": 16777216}
     sweep["W2"]["67108864"]["q8"]["us"] = 90.0          # behind at the largest size
-    assert bench.min_sizes(sweep)["W2"]["q8"] is None
+    assert bench.min_sizes(sweep, margin=0.2)[0]["W2"]["q8"] is None
 
 
 def test_min_sizes_counts_only_leads_beyond_the_spread():
@@ -63,9 +63,23 @@ def test_min_sizes_counts_only_leads_beyond_the_spread():
                     "4194304": pt(20.0, 19.0, 0.6, 0.5),  # 19.5 < 19.4 fails: a tie
                     "8388608": pt(40.0, 30.0, 1.0, 1.0),
                     "16777216": pt(80.0, 60.0, 1.0, 1.0)}}
-    assert bench.min_sizes(sweep)["W8"]["q4"] == 8388608
+    assert bench.min_sizes(sweep, margin=0.0)[0]["W8"]["q4"] == 8388608
     sweep["W8"]["4194304"]["1stage"]["spread"] = 0.2      # 19.5 < 19.8: a lead
-    assert bench.min_sizes(sweep)["W8"]["q4"] == 2097152
+    assert bench.min_sizes(sweep, margin=0.0)[0]["W8"]["q4"] == 2097152
+
+
+def test_min_sizes_needs_the_margin_and_reports_points_near_it():
+    def pt(one, q4):
+        return {"1stage": {"us": one, "spread": 0.0}, "q4": {"us": q4, "spread": 0.0}}
+    sweep = {"W4": {"4194304": pt(10.0, 8.5),      # 15 % ahead: short of a 20 % margin
+                    "8388608": pt(20.0, 16.05),    # 19.75 % ahead: short, and marginal
+                    "16777216": pt(40.0, 30.0)}}   # 25 % ahead
+    tab, marginal = bench.min_sizes(sweep, margin=0.2)
+    assert tab["W4"]["q4"] == 16777216
+    assert [m["bytes"] for m in marginal] == [8388608]
+    # the default margin is the one the benchmark reports
+    assert bench.min_sizes(sweep)[0] == tab
+    assert bench.min_sizes(sweep, margin=0.1)[0]["W4"]["q4"] == 4194304
 
 
 def test_stage2_hbm_bytes_read_the_reduced_image_once():
