@@ -55,7 +55,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=5)
-    p.add_argument("--cold-reps", type=int, default=7)
+    p.add_argument("--cold-reps", type=int, default=15)
     p.add_argument("--no-cold", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=1 << 21,
@@ -187,15 +187,24 @@ class Cold:
             ts.append(self.ev.ms(0, 1) * 1e3)
         return float(np.median(ts))
 
-    def copy_us(self, nbytes):
-        """a plain device copy moving nbytes in all (half read, half written)"""
+    def us_interleaved(self, fns, reps=None):
+        """{name: median us} of cold launches of several functions taken in
+        turn, one launch of each per round, so that they see the same drift of
+        the machine's state"""
+        ts = {k: [] for k in fns}
+        for _ in range(reps or self.reps):
+            for k, fn in fns.items():
+                ts[k].append(self.us(fn, 1))
+        return {k: float(np.median(v)) for k, v in ts.items()}
+
+    def copy_fn(self, nbytes):
+        """a plain device copy moving nbytes in all (half read, half written),
+        as a function to time, and the buffers to free afterwards"""
         half = (nbytes // 2 + 15) // 16 * 16
         src = self.torch.ones(half, dtype=self.torch.uint8, device="cuda")
         dst = self.torch.empty_like(src)
         dst.copy_(src)
-        t = self.us(lambda: dst.copy_(src))
-        del src, dst
-        return t
+        return (lambda: dst.copy_(src)), (src, dst)
 
     def close(self):
         self.ev.close()
@@ -319,11 +328,23 @@ def measure_headline(args, qr, I, torch, stream, log):
             torch.cuda.synchronize()
             r = {}
             r["quantize"] = cl.us(lambda: qr.qr_quantize_recv(c, xs, b["recv"], dtype=dtype))
-            r["stage1"] = cl.us(lambda: qr.qr_reduce_recv(c, W, b["recv"], n, b["red"], dtype))
             r["stage2"] = cl.us(lambda: qr.qr_gather_stage2(c, b["red"], ys, dtype=dtype))
-            r["stage1_pattern"] = cl.us(lambda: pat.stage1(c, W, b["recv"], n, b["red"], stream))
+            # stage 1 and its references, in turn: the access pattern alone,
+            # a plain copy of the same bytes, and the same stage 1 from W
+            # separate wire images (W streams instead of the receive
+            # buffer's one)
             ab1 = algorithmic_bytes("stage1", W, n, wb)
-            r["stage1_copy"] = cl.copy_us(ab1)
+            copy, keep = cl.copy_fn(ab1)
+            wires = [qr.alloc_wire(c, n) for _ in range(W)]
+            qr.qr_quantize_ranks(c, xs, wires, dtype=dtype)
+            red2 = qr.alloc_wire(c, n)
+            t = cl.us_interleaved({
+                "stage1": lambda: qr.qr_reduce_recv(c, W, b["recv"], n, b["red"], dtype),
+                "stage1_pattern": lambda: pat.stage1(c, W, b["recv"], n, red2, stream),
+                "stage1_copy": copy,
+                "stage1_planar": lambda: qr.qr_reduce_stage1(c, wires, n, red2, dtype)})
+            r.update(t)
+            del wires, keep, red2
             staged(c)           # leave the reduced image the kernels wrote
             cold[c] = r
         cl.close()
@@ -451,7 +472,7 @@ def measure_workload(qr, I, torch, stream, config, n=None, iters=20, cold=True, 
     n = cfg["n"] if n is None else n
     xs = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in I.make(config, n=n)]
     ys = [torch.empty_like(xs[0]) for _ in range(W)]
-    cl = Cold(torch, stream, 5) if cold else None
+    cl = Cold(torch, stream, 11) if cold else None
     pat = Pattern() if cold else None
     out = {}
     for c in cfg["codecs"]:
@@ -465,11 +486,15 @@ def measure_workload(qr, I, torch, stream, config, n=None, iters=20, cold=True, 
         if cold:
             recv, red = qr.alloc_recv(W, c, n), qr.alloc_wire(c, n)
             qr.qr_quantize_recv(c, xs, recv, dtype=dtype)
-            t = cl.us(lambda: qr.qr_reduce_recv(c, W, recv, n, red, dtype))
+            red2 = qr.alloc_wire(c, n)
+            tt = cl.us_interleaved({
+                "k": lambda: qr.qr_reduce_recv(c, W, recv, n, red, dtype),
+                "p": lambda: pat.stage1(c, W, recv, n, red2, stream)})
+            t, tp = tt["k"], tt["p"]
+            del red2
             r["stage1_cold_us"] = t
             ab = algorithmic_bytes("stage1", W, n, qr.qr_wire_bytes(c, n))
             r["stage1_cold_frac"] = frac(ab, t)
-            tp = cl.us(lambda: pat.stage1(c, W, recv, n, red, stream))
             r["pattern_cold_us"] = tp
             r["pattern_cold_frac"] = frac(ab, tp)
             r["stage1_vs_pattern"] = tp / t
@@ -653,6 +678,10 @@ def main():
                 e[st]["cold_frac"] = round(frac(algorithmic_bytes(st, W, n, wb), cd[st]), 4)
             e["stage2"]["cold_frac_hbm"] = round(frac(hbm_bytes_stage2(W, n, wb),
                                                       cd["stage2"]), 4)
+            ab1 = algorithmic_bytes("stage1", W, n, wb)
+            for key in ("pattern", "copy", "planar"):
+                e["stage1"][key + "_cold_us"] = round(cd["stage1_" + key], 2)
+                e["stage1"][key + "_cold_frac"] = round(frac(ab1, cd["stage1_" + key]), 4)
         stages[I.CODEC_NAMES[c]] = e
 
     extra = None
@@ -664,9 +693,11 @@ def main():
         log("bench: other workloads written to %s" % args.extra)
 
     for name, e in stages.items():
-        log("  %-4s %8.1f us/allreduce  stage0 %.3f  stage1 %.3f (cold %s)  stage2 %.3f" % (
-            name, e["us_per_allreduce"], e["quantize"]["frac"], e["stage1"]["frac"],
-            e["stage1"].get("cold_frac"), e["stage2"]["frac"]))
+        log("  %-4s %8.1f us/allreduce  stage0 %.3f  stage1 %.3f (cold %s, pattern %s, "
+            "W wire images %s)  stage2 %.3f" % (
+                name, e["us_per_allreduce"], e["quantize"]["frac"], e["stage1"]["frac"],
+                e["stage1"].get("cold_frac"), e["stage1"].get("pattern_cold_frac"),
+                e["stage1"].get("planar_cold_frac"), e["stage2"]["frac"]))
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,

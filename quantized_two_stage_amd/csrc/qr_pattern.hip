@@ -11,6 +11,7 @@
 
 #include "qr.h"
 #include "qr_device.h"
+#include "qr_pattern.h"
 #include "qr_internal.h"
 #include "qr_stage_io.h"
 
@@ -99,11 +100,7 @@ void by_w(int W, const InPtrs& in, uint8_t* red, size_t n, hipStream_t st) {
 
 extern "C" {
 
-/* The stage-1 access pattern over a receive buffer `recv` of W ranks (as
- * qr_quantize_recv writes it) into `reduced` (a wire image): the loads and
- * stores of qr_reduce_recv over all blocks, no arithmetic.  Returns 0, or -1
- * for an unsupported codec or W, a null or unaligned pointer, or a size that
- * is not a positive multiple of 8 elements; -6 for a failed launch. */
+// declared, with its arguments, in qr_pattern.h
 int qrp_stage1_pattern(int codec, int W, const void* recv, size_t n, void* reduced,
                        void* stream) {
   using namespace qr;
@@ -111,12 +108,16 @@ int qrp_stage1_pattern(int codec, int W, const void* recv, size_t n, void* reduc
       recv == nullptr || reduced == nullptr || ((uintptr_t)recv & 15u) != 0 ||
       ((uintptr_t)reduced & 15u) != 0)
     return -1;
-  // one launch: the receive buffer's offsets must fit in 32 bits
-  const size_t tiles = ((n + 31) / 32 + kTileBlocks - 1) / kTileBlocks;
-  const size_t cb0 = codec == QR_FP ? 64 : (codec & 7) == QR_Q6 ? 24 : (codec & 7) == QR_Q4 ? 16 : 32;
-  if ((tiles + 1) * (size_t)W * kTileBlocks * (cb0 + 4) >= ((size_t)1 << 32)) return -1;
+  if (!(codec == QR_FP || codec == QR_Q8 || codec == QR_Q6 || codec == QR_Q4 ||
+        codec == QR_FP8 || codec == QR_Q8_ASYM || codec == QR_Q6_ASYM || codec == QR_Q4_ASYM))
+    return -1;
+  // bytes of one rank's tile of the receive buffer: the codes (FP: the raw
+  // data) of 256 blocks, then their scales and zeros
   const size_t cb = codec == QR_FP ? 64 : (codec & 7) == QR_Q6 ? 24 : (codec & 7) == QR_Q4 ? 16 : 32;
   const size_t tile = (size_t)kTileBlocks * (codec == QR_FP ? cb : cb + 2 + ((codec & 8) ? 2 : 0));
+  // one launch: the receive buffer's offsets must fit in 32 bits
+  const size_t tiles = ((n + 31) / 32 + kTileBlocks - 1) / kTileBlocks;
+  if ((tiles + 1) * (size_t)W * tile >= ((size_t)1 << 32)) return -1;
   InPtrs in{};
   for (int r = 0; r < W; r++) in.p[r] = static_cast<const uint8_t*>(recv) + (size_t)r * tile;
   uint8_t* red = static_cast<uint8_t*>(reduced);

@@ -244,3 +244,28 @@ def test_binding_refuses_tensors_the_kernels_would_overrun():
         with pytest.raises(ValueError) as e:
             call()
         assert msg in str(e.value), (msg, str(e.value))
+
+
+def test_pattern_library_exports_its_header_and_rejects():
+    """libqr_pattern.so (the stage-1 access pattern the benchmark times) loads,
+    exports every function include/qr_pattern.h declares, and refuses invalid
+    arguments with -1 before launching (fake pointers, never touched)."""
+    from quantized_two_stage_amd import build as qbuild
+    src = open(os.path.join(ROOT, "include", "qr_pattern.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(qrp_[a-z0-9_]+)\s*\(", src)))
+    assert names == ["qrp_stage1_pattern"]
+    L = ctypes.CDLL(qbuild.PATTERN_LIB)
+    for name in names:
+        assert hasattr(L, name), name
+    f = L.qrp_stage1_pattern
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    good = dict(codec=3, W=8, recv=1 << 20, n=1 << 10, red=1 << 24)
+    bad = [dict(codec=4), dict(codec=12), dict(W=3), dict(W=1), dict(n=0), dict(n=12),
+           dict(recv=0), dict(red=0), dict(recv=(1 << 20) + 8), dict(red=(1 << 24) + 4),
+           dict(n=1 << 30)]        # offsets beyond 32 bits at W=8
+    for b in bad:
+        a = dict(good, **b)
+        assert f(a["codec"], a["W"], a["recv"], a["n"], a["red"], None) == -1, b
