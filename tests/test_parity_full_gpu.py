@@ -11,7 +11,7 @@ import torch
 
 import oracle as O
 from gpu_util import (assert_bytes_equal, assert_recv_equal, assert_within_ulp, dev16, host16,
-                      hostu8, oracle_whole, plane_slices, sample_windows, say)
+                      hostu8, oracle_whole, plane_slices, recv_tile_bytes, sample_windows, say)
 from quantized_two_stage_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -137,6 +137,40 @@ def test_max_size(qr, codec):
         want = O.allreduce(codec, dtype, loc)[0]
         assert_within_ulp(host16(ys[0][e0:e1]), want, dtype, "max y %d..%d" % (lo, hi))
         assert torch.equal(ys[1][e0:e1], ys[0][e0:e1])
+    del xs, ys, ws
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("codec", (O.FP, O.Q8A))
+def test_max_size_w8(qr, codec):
+    """n = 2^30 elements per rank at W = 8: a receive buffer of 16 GiB (FP) or
+    9.7 GiB (Q8A), whose 32-bit offsets split stages 0 and 1 into 5 or 3
+    launches over tile ranges.  Windows of blocks straddle every split (the
+    split points computed here from the layout: a launch spans
+    (2^32 - 1) // (W * tile bytes) - 1 tiles), besides the first, the last and
+    random ones; outputs of ranks 0 and 7 against the oracle."""
+    n, W, dtype = 1 << 30, 8, O.FP16
+    say("max size W=8", codec)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8484 + codec)
+    xs = [torch.randn(n, generator=g, device="cuda", dtype=torch.float32)
+          .to(torch.float16).view(torch.int16) for _ in range(W)]
+    ys = [torch.empty_like(xs[0]) for _ in range(W)]
+    ws = qr.alloc_workspace(W, codec, n)
+    qr.qr_allreduce_sim(codec, xs, ys, ws, dtype=dtype)
+    torch.cuda.synchronize()
+    nb = n // 32
+    per = (2 ** 32 - 1) // (W * recv_tile_bytes(codec)) - 1
+    splits = list(range(per * 256, nb, per * 256))
+    assert len(splits) == (4 if codec == O.FP else 2)
+    windows = sample_windows(nb, count=4, seed=codec) + [(b - 32, b + 32) for b in splits]
+    for (lo, hi) in windows:
+        e0, e1 = 32 * lo, 32 * hi
+        loc = [host16(x[e0:e1]) for x in xs]
+        want = O.allreduce(codec, dtype, loc)[0]
+        for r in (0, W - 1):
+            assert_within_ulp(host16(ys[r][e0:e1]), want, dtype,
+                              "max W=8 rank %d y %d..%d" % (r, lo, hi))
     del xs, ys, ws
     torch.cuda.empty_cache()
 
