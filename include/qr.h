@@ -217,10 +217,11 @@ int qr_allreduce_oneshot(int W, qr_dtype dtype, const void* const* xs,
 
 /* qr_allreduce_sim without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
- * harnesses that forbid hipMalloc).  The W wire images and the reduced image
- * go to a device buffer of QR_SCRATCH_BYTES that the library holds in every
- * GPU it runs on, from the first call on that GPU until the process ends; the
- * call itself allocates nothing and frees nothing.  The GPU is the current
+ * harnesses that forbid hipMalloc).  The receive buffer and the reduced image
+ * (the workspace of qr_allreduce_sim) go to a device buffer of
+ * QR_SCRATCH_BYTES that the library holds in every GPU it runs on, from the
+ * first call on that GPU until the process ends; the call itself allocates
+ * nothing and frees nothing.  The GPU is the current
  * device (hipGetDevice), which `stream` must belong to.  Outputs, launches
  * and argument rules are those of qr_allreduce_sim; additionally the call
  * fails with QR_ERR_WORKSPACE, writing nothing, when
@@ -228,7 +229,7 @@ int qr_allreduce_oneshot(int W, qr_dtype dtype, const void* const* xs,
  * GPU uses the same buffer: calls on that GPU must not overlap in time (on
  * two streams, or from two threads, without ordering between them), or they
  * race on it.  Nothing in the buffer needs to start at zero; it keeps the
- * last call's wire images. */
+ * last call's receive buffer and reduced image. */
 int qr_allreduce_sim_noalloc(int W, qr_dtype dtype, qr_codec codec,
                              const void* const* xs, void* const* ys, size_t n,
                              void* stream);
