@@ -534,6 +534,74 @@ __device__ __forceinline__ void add_codes(float (&acc)[N], const uint32_t* w, fl
   }
 }
 
+// The binary16 value in the low half of h, times k, in binary32 (one
+// v_fma_mix_f32: the conversion is exact, and so is the product for k a power
+// of two).  The addend is -0 (the inline constant 0, negated by the source
+// modifier), so that -0 * k stays -0 (with +0 it would round to +0).  The
+// high half of h is ignored.
+__device__ __forceinline__ float h2f_times(uint32_t h, float k) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, neg(0) op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(k));
+  return r;
+}
+
+// fma_mix16 with the addend given as the binary16 value in the low half of
+// zh, converted exactly inside the same instruction: fma(h, S, z) rounded
+// once, as fma_mix16(h2, S, h2f(zh)).
+template <bool Hi>
+__device__ __forceinline__ float fma_mix16h(uint32_t h2, float S, uint32_t zh) {
+  float r;
+  if constexpr (Hi)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,1]"
+        : "=v"(r) : "v"(h2), "v"(S), "v"(zh));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,1]"
+        : "=v"(r) : "v"(h2), "v"(S), "v"(zh));
+  return r;
+}
+
+// add_codes for the asymmetric 4- and 6-bit codes with the rank's scale and
+// zero taken as their binary16 bits: S0 = s * 2^24 and S4 = s * 2^20 come from
+// one v_fma_mix_f32 each (h2f_times) and the zero enters every term as a
+// binary16 operand (fma_mix16h), which saves the two conversions and two
+// multiplies per rank that the binary32 forms need.  The terms and sums are
+// those of add_codes, bit for bit.
+template <int C, int N>
+__device__ __forceinline__ void add_codes_asym(float (&acc)[N], const uint32_t* w, float S0,
+                                               float S4, uint32_t zh, bool first) {
+  using T = CodecT<C>;
+  static_assert(T::asym && (T::bits == 4 || T::bits == 6), "asymmetric 4- and 6-bit codes");
+  if constexpr (T::bits == 4) {
+#pragma unroll
+    for (int k = 0; k < N / 8; k++) {
+      const uint32_t a = w[k] & 0x000f000fu, b = w[k] & 0x00f000f0u;
+      const uint32_t c = (w[k] >> 8) & 0x000f000fu, d = (w[k] >> 8) & 0x00f000f0u;
+      float x[8];
+      x[0] = fma_mix16h<false>(a, S0, zh);
+      x[4] = fma_mix16h<true>(a, S0, zh);
+      x[1] = fma_mix16h<false>(b, S4, zh);
+      x[5] = fma_mix16h<true>(b, S4, zh);
+      x[2] = fma_mix16h<false>(c, S0, zh);
+      x[6] = fma_mix16h<true>(c, S0, zh);
+      x[3] = fma_mix16h<false>(d, S4, zh);
+      x[7] = fma_mix16h<true>(d, S4, zh);
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[8 * k + i] = first ? x[i] : acc[8 * k + i] + x[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+      const int off = 6 * i, k = off >> 5, sh = off & 31;
+      const uint32_t f = sh + 6 <= 32
+                             ? __builtin_amdgcn_ubfe(w[k], sh, 6)
+                             : __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(w[k + 1], w[k], sh),
+                                                     0, 6);
+      const float t = fma_mix16h<false>(f, S0, zh);
+      acc[i] = first ? t : acc[i] + t;
+    }
+  }
+}
+
 // max and min of a whole block p[0..32): one chain each, so that every pair
 // of new values takes one v_max3/v_min3
 __device__ __forceinline__ void block_max_min(const float* p, float& mx, float& mn) {

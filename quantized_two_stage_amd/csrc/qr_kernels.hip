@@ -357,6 +357,25 @@ __device__ __forceinline__ void s1_reduce_store(const S1In<C, W>& in, uint8_t* r
   float acc[kBlock];
 #pragma unroll
   for (int r = 0; r < W; r++) {
+    if constexpr (T::asym && (T::bits == 4 || T::bits == 6)) {
+      // scale and zero straight from their binary16 bits (add_codes_asym)
+      const float S0 = h2f_times(in.sh[r], 16777216.0f);
+      const float S4 = T::bits == 4 ? h2f_times(in.sh[r], 1048576.0f) : 0.0f;
+      if constexpr (T::bits == 6 || W > 4) {
+        add_codes_asym<C, kBlock>(acc, in.cw[r], S0, S4, in.zh[r], r == 0);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          float a8[8];
+#pragma unroll
+          for (int i = 0; i < 8; i++) a8[i] = acc[8 * k + i];
+          add_codes_asym<C, 8>(a8, in.cw[r] + k, S0, S4, in.zh[r], r == 0);
+#pragma unroll
+          for (int i = 0; i < 8; i++) acc[8 * k + i] = a8[i];
+        }
+      }
+      continue;
+    }
     const float sc = h2f(in.sh[r]) * T::unpack_scale;
     const float zc = T::asym ? h2f(in.zh[r]) : 0.0f;
     if constexpr (T::bits == 6 || W > 4) {

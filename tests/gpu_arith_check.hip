@@ -33,6 +33,13 @@
 //      flipped, read as a binary16 subnormal, fma'd with s * 2^24 and -32s,
 //      == q * s exactly for every 6-bit code q and every positive finite
 //      binary16 scale s
+//  14. h2f_times(h, k) (v_fma_mix_f32 reading the low half) == h2f(h) * k
+//      exactly for every non-NaN binary16 h, k = 2^24 and 2^20, whatever the
+//      high half holds
+//  15. fma_mix16h<Hi>(f, S, zh) (the addend read as binary16) ==
+//      fmaf(f * 2^-24, S, h2f(zh)) for every field f < 1024 in either half and
+//      every finite binary16 zh, with S = s * 2^24 or s * 2^20 for a binary16
+//      scale s drawn per case, junk in the other halves
 // Prints one line per check and exits 0 only if every count is zero.
 // Grid-stride loops with explicit bounds; counters in one small array.
 #include <hip/hip_runtime.h>
@@ -44,7 +51,8 @@
 using namespace qr;
 
 enum { kDiv = 0, kRcp = 6, kRint = 7, kEnc = 8, kDec = 9, kBf = 10, kF2h = 11, kMixCvt = 12,
-       kMixFma = 13, kRByte = 14, kOffI4 = 15, kSymMix = 16, kSym6Mix = 17, kSlots = 18 };
+       kMixFma = 13, kRByte = 14, kOffI4 = 15, kSymMix = 16, kSym6Mix = 17, kH2fTimes = 18,
+       kMixFmaH = 19, kSlots = 20 };
 
 __device__ void miss(uint32_t* c, int slot) { atomicAdd(&c[slot], 1u); }
 
@@ -227,6 +235,38 @@ __global__ void k_sym6_mix(uint32_t* c) {
       miss(c, kSym6Mix);
 }
 
+__global__ void k_h2f_times(uint32_t* c) {
+  const uint32_t p = blockIdx.x * blockDim.x + threadIdx.x;     // 0..65535
+  if (p >= 65536u || (p & 0x7fffu) > 0x7c00u) return;             // NaN patterns
+  const uint32_t junk = hash32(p) & 0xffffu;
+  const float ks[2] = {16777216.0f, 1048576.0f};
+  for (int k = 0; k < 2; k++)
+    if (__builtin_bit_cast(uint32_t, h2f_times((junk << 16) | p, ks[k])) !=
+        __builtin_bit_cast(uint32_t, h2f(p) * ks[k]))
+      miss(c, kH2fTimes);
+}
+
+__global__ void k_mix_fma_h(uint32_t* c) {
+  const uint64_t n = 1024ull * 65536ull;                           // field x zero pattern
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint32_t f = (uint32_t)(i & 1023u), zb = (uint32_t)(i >> 10);
+    if ((zb & 0x7fffu) >= 0x7c00u) continue;                       // z finite
+    const uint32_t hsh = hash32((uint32_t)i);
+    const uint32_t sb = hsh % 0x7bffu + 1u;                        // 0x0001 .. 0x7bff
+    const float S = h2f(sb) * ((hsh >> 31) ? 1048576.0f : 16777216.0f);
+    const float want = __builtin_fmaf((float)f * 5.9604644775390625e-8f, S, h2f(zb));
+    const uint32_t junk = hash32((uint32_t)i ^ 0x9e3779b9u);
+    const uint32_t zh = (junk & 0xffff0000u) | zb;
+    if (__builtin_bit_cast(uint32_t, fma_mix16h<false>(((junk & 0xffffu) << 16) | f, S, zh)) !=
+        __builtin_bit_cast(uint32_t, want))
+      miss(c, kMixFmaH);
+    if (__builtin_bit_cast(uint32_t, fma_mix16h<true>((f << 16) | (junk & 0xffffu), S, zh)) !=
+        __builtin_bit_cast(uint32_t, want))
+      miss(c, kMixFmaH);
+  }
+}
+
 __global__ void k_bf(uint32_t* c) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32); i += stride) {
@@ -301,6 +341,8 @@ int main() {
   k_off_i4<<<8192, 256>>>(c);
   k_sym_mix<<<(16 * 0x7bff + 255) / 256, 256>>>(c);
   k_sym6_mix<<<(64 * 0x7bff + 255) / 256, 256>>>(c);
+  k_h2f_times<<<256, 256>>>(c);
+  k_mix_fma_h<<<8192, 256>>>(c);
   CK(hipGetLastError());
   CK(hipDeviceSynchronize());
   uint32_t h[kSlots];
@@ -327,8 +369,11 @@ int main() {
          " scales, both halves, both nibble positions\n", h[kSymMix]);
   printf("symmetric 6-bit fma_mix term: %u mismatches over all codes x positive finite binary16"
          " scales, both halves\n", h[kSym6Mix]);
+  printf("h2f_times: %u mismatches over all non-NaN binary16 x (2^24, 2^20)\n", h[kH2fTimes]);
+  printf("fma_mix16h (binary16 addend): %u mismatches over all fields < 1024 x all finite"
+         " binary16 zeros, both halves\n", h[kMixFmaH]);
   total += h[kRcp] + h[kRint] + h[kEnc] + h[kDec] + h[kBf] + h[kF2h] + h[kMixCvt] + h[kMixFma] +
-           h[kRByte] + h[kOffI4] + h[kSymMix] + h[kSym6Mix];
+           h[kRByte] + h[kOffI4] + h[kSymMix] + h[kSym6Mix] + h[kH2fTimes] + h[kMixFmaH];
   printf("%s\n", total == 0 ? "ALL OK" : "MISMATCHES");
   return total == 0 ? 0 : 1;
 }
