@@ -40,7 +40,17 @@ def test_bench_prints_the_contract_line():
     assert r["traffic"] is None or r["traffic"] > 0
     assert r["frac"] == min(r["per_codec_frac"].values()) or \
         abs(r["frac"] - min(r["per_codec_frac"].values())) < 1e-4
-    assert set(r["per_codec_frac"]) == set(r["pattern_frac"])
+    assert set(r["per_codec_frac"]) == set(r["pattern_frac"]) == set(r["copy_frac"]) == \
+        set(r["in_pipeline_frac"])
+    # traffic: the calibrated counters of profiles/traffic.json, reported only
+    # while the kernel sources are those the counters were taken on
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        tj = json.load(f)
+    codec = r["kernel"].split(",")[-2].strip()          # "<kernel> (...), <codec>, cold"
+    if tj["source_sha"] == d["kernel_source_sha"]:
+        assert r["traffic"] == tj["kernels"]["stage1/" + codec]["bytes"]
+    else:
+        assert r["traffic"] is None
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1
     assert isinstance(c["unit"], str) and isinstance(c["sample"], str)
