@@ -17,19 +17,21 @@
 // as alternative to custom allreduce" (vLLM PR #16804, PR description).
 //
 // Every kernel streams HBM; nothing is a contraction, so no MFMA and no LDS.
-//   - k_quantize and k_dequant give each lane one quarter block (8 elements
-//     = 16 contiguous bytes of 16-bit data, consecutive lanes on consecutive
-//     quarters), four quarters per lane issued before any is used.  A quad
-//     of lanes holds the quarters of four blocks: it reduces each block's
-//     max/min with DPP quad permutes, lane j derives block j's scale, and
-//     1/s reaches the other lanes by a DPP broadcast (a few instructions,
-//     instead of a round trip through LDS).
+//   - k_quantize and k_dequant work on quarter blocks (8 elements = 16
+//     contiguous bytes of 16-bit data, consecutive lanes on consecutive
+//     quarters).  k_quantize takes four quarters per lane, issued before any
+//     is used, so that a quad of lanes holds the quarters of four blocks: it
+//     reduces each block's max/min with DPP quad permutes, lane j derives
+//     block j's scale, and 1/s reaches the other lanes by a DPP broadcast (a
+//     few instructions, instead of a round trip through LDS).  k_dequant
+//     takes kS2PerLane quarters per lane.
 //   - k_stage1 gives each lane a whole block: W code blocks of 16/24/32
 //     contiguous bytes and W scales in, one code block and scale out; the
 //     per-block work (max/min, two divisions, rounding of the scale) is done
 //     once, which matters because this kernel is the one closest to the
 //     VALU limit (W=2, 4-bit codes: 1.7 bytes of HBM per element).
-//   - the FP kernels give each lane 16-byte chunks, four per lane.
+//   - the FP kernels give each lane 16-byte chunks, four per lane
+//     (kS2PerLane in stage 2).
 //   - k_fused gives each lane one quarter block of every rank (a workgroup
 //     holds 64 blocks) and quantizes four ranks at a time as the four slots
 //     of the quad quantizer.
@@ -314,20 +316,23 @@ __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
                                                    uint32_t tile0, int W) {
   static_assert(kThreads * kPerLane == kTileBlocks * 4, "a workgroup's chunks are one tile");
   constexpr int kS = Stage == 0 ? kStage0 : kStage2;
+  // stage 0 (into the receive buffer, or planar) keeps one tile per
+  // workgroup; stage 2 (planar) takes kS2PerLane chunks per lane
+  constexpr int K = Stage == 0 ? kPerLane : kS2PerLane;
   uint32_t tile;
   int r;
   s0_item<Recv>(W, tile0, tile, r);
   const u32x4* s = reinterpret_cast<const u32x4*>(src.p[r]);
   uint8_t* d = dst.p[r];
-  const uint32_t base = tile * (kThreads * kPerLane) + threadIdx.x;
-  u32x4 q[kPerLane];
+  const uint32_t base = tile * (kThreads * K) + threadIdx.x;
+  u32x4 q[K];
 #pragma unroll
-  for (int j = 0; j < kPerLane; j++) {
+  for (int j = 0; j < K; j++) {
     const uint32_t c = base + j * kThreads;
     q[j] = ld_in<kS>(s + (c < nchunks ? c : 0u));
   }
 #pragma unroll
-  for (int j = 0; j < kPerLane; j++) {
+  for (int j = 0; j < K; j++) {
     const uint32_t c = base + j * kThreads;
     if constexpr (Din != Dout) {
 #pragma unroll
@@ -479,18 +484,18 @@ __global__ __launch_bounds__(kThreads) void k_sum_fp(InPtrs xs, OutPtrs outs,
 }
 
 // ---------------------------------------------------------------------------
-// stage 2 / dequantize: one quarter block per lane, kPerLane quarters
+// stage 2 / dequantize: quarter blocks, kS2PerLane per lane
 
-// quarters q0 + 256u (u = 0..3) of the wire -> y; Full: all hold 8 elements
-template <int C, int D, bool Full, int Stage = kStage2>
+// quarters q0 + 256u (u < U) of the wire -> y; Full: all hold 8 elements
+template <int C, int D, bool Full, int Stage = kStage2, int U = kS2PerLane>
 __device__ __forceinline__ void dequant_tile(const uint8_t* wire, uint8_t* y, uint32_t q0,
                                              uint32_t nq, const Geo& g) {
   using T = CodecT<C>;
   using IO = QuarterIO<C>;
-  uint32_t w[kPerLane][IO::nw];
-  float s[kPerLane], z[kPerLane];
+  uint32_t w[U][IO::nw];
+  float s[U], z[U];
 #pragma unroll
-  for (int u = 0; u < kPerLane; u++) {
+  for (int u = 0; u < U; u++) {
     const uint32_t q = Full || q0 + u * kThreads < nq ? q0 + u * kThreads : 0u;  // no branch
     const uint32_t blk = q >> 2;
     IO::load(wire + (size_t)blk * T::block_bytes, q & 3, w[u]);
@@ -498,7 +503,7 @@ __device__ __forceinline__ void dequant_tile(const uint8_t* wire, uint8_t* y, ui
     z[u] = T::asym ? h2f(ld_u16(wire + g.off_z + (size_t)blk * 2)) : 0.0f;
   }
 #pragma unroll
-  for (int u = 0; u < kPerLane; u++) {
+  for (int u = 0; u < U; u++) {
     const uint32_t q = q0 + u * kThreads;
     if (!Full && q >= nq) break;
     float cv[8];
@@ -518,8 +523,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* wire, OutPt
                                                       Geo g) {
   const int r = blockIdx.y;
   const uint32_t nq = (g.n + 7) / 8;                // quarters that hold data
-  const uint32_t q0 = blockIdx.x * (kThreads * kPerLane) + threadIdx.x;
-  if (tile_full(blockIdx.x, g.n))
+  const uint32_t q0 = blockIdx.x * (kThreads * kS2PerLane) + threadIdx.x;
+  if (8ull * ((uint64_t)blockIdx.x + 1ull) * (kThreads * kS2PerLane) <= (uint64_t)g.n)
     dequant_tile<C, D, true>(wire, ys.p[r], q0, nq, g);
   else
     dequant_tile<C, D, false>(wire, ys.p[r], q0, nq, g);
@@ -816,10 +821,10 @@ void dq_dispatch(int W, const uint8_t* wire, const OutPtrs& ys, const Layout& L,
     constexpr int Dw = D == kBF16H ? kF16 : D;
     constexpr int Dout = D == kBF16H ? kBF16 : D;
     hipLaunchKernelGGL((k_copy<2, Dw, Dout, false>),
-                       dim3(groups(L.n / 8, kThreads * kPerLane), W), dim3(kThreads), 0, st,
+                       dim3(groups(L.n / 8, kThreads * kS2PerLane), W), dim3(kThreads), 0, st,
                        src, ys, (uint32_t)(L.n / 8), 0u, 0u, W);
   } else {
-    hipLaunchKernelGGL((k_dequant<C, D>), dim3(groups(L.n / 8, kThreads * kPerLane), W),
+    hipLaunchKernelGGL((k_dequant<C, D>), dim3(groups(L.n / 8, kThreads * kS2PerLane), W),
                        dim3(kThreads), 0, st, wire, ys, geo(L));
   }
 }

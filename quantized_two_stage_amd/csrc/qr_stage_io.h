@@ -14,8 +14,17 @@ namespace qr {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerLane = 4;        // quarters / chunks per lane (k_quantize,
-                                   // k_dequant and the FP kernels)
+constexpr int kPerLane = 4;        // quarters / chunks per lane (k_quantize and
+                                   // the FP kernels of stages 0 and 1)
+// Quarters (16-byte chunks of output) per lane of stage 2 (k_dequant and the
+// FP stage-2 copy).  One: four times the workgroups of the four-per-lane
+// form, which measured 2% faster over the W=8 64 MB allreduces (stage 2 is
+// the writes of W outputs; more, smaller workgroups keep more of them in
+// flight).
+#ifndef QR_S2_U
+#define QR_S2_U 1
+#endif
+constexpr int kS2PerLane = QR_S2_U;
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X):
 // QR_NT_STORE bit mask of the stages (1 = stage 0, 2 = stage 1, 4 = stage 2)
