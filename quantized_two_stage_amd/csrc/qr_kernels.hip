@@ -19,12 +19,12 @@
 // Every kernel streams HBM; nothing is a contraction, so no MFMA and no LDS.
 //   - k_quantize and k_dequant work on quarter blocks (8 elements = 16
 //     contiguous bytes of 16-bit data, consecutive lanes on consecutive
-//     quarters).  k_quantize takes four quarters per lane, issued before any
-//     is used, so that a quad of lanes holds the quarters of four blocks: it
-//     reduces each block's max/min with DPP quad permutes, lane j derives
-//     block j's scale, and 1/s reaches the other lanes by a DPP broadcast (a
-//     few instructions, instead of a round trip through LDS).  k_dequant
-//     takes kS2PerLane quarters per lane.
+//     quarters).  k_quantize takes kS0PerLane quarters per lane, issued
+//     before any is used, so that a quad of lanes holds the quarters of that
+//     many blocks: it reduces each block's max/min with DPP quad permutes,
+//     lane j derives the scale of block j mod kS0PerLane, and 1/s reaches the
+//     other lanes by a DPP broadcast (a few instructions, instead of a round
+//     trip through LDS).  k_dequant takes kS2PerLane quarters per lane.
 //   - k_stage1 gives each lane a whole block: W code blocks of 16/24/32
 //     contiguous bytes and W scales in, one code block and scale out; the
 //     per-block work (max/min, two divisions, rounding of the scale) is done
@@ -79,12 +79,12 @@ struct QuarterIO {
 };
 
 // ---------------------------------------------------------------------------
-// stage 0: one quarter block per lane, kPerLane = 4 quarters per lane.  For
-// each u the four lanes of a quad hold the four quarters of one block, so a
-// quad covers four blocks.  Every lane reduces the max/min of all four
-// blocks across the quad, then lane j alone derives the scale (and zero) of
-// block j and hands 1/s, the zero and two flags to the others (DPP quad
-// broadcasts): each block's divisions and roundings run once, not four times.
+// stage 0: quarter blocks, U = kS0PerLane per lane.  For each u the four
+// lanes of a quad hold the four quarters of one block, so a quad covers U
+// blocks.  Every lane reduces the max/min of all U blocks across the quad,
+// then lane j derives the scale (and zero) of block j mod U and hands 1/s,
+// the zero and two flags to the others (DPP quad broadcasts): with U = 4 each
+// block's divisions and roundings run once, with U = 2 twice.
 
 // max/min with a quad neighbour in one instruction: the DPP permute is the
 // first source of v_max_f32/v_min_f32 itself.  (Written as a permute and an
@@ -222,24 +222,30 @@ __device__ __forceinline__ void quantize_core(float (&v)[U][8], uint8_t* const (
   }
 }
 
-// four quarters q0 + 256u (u = 0..3) of one wire image: a quad holds the
-// quarters of four blocks, one per slot
-template <int C, int Stage, bool Full, bool Recv>
-__device__ __forceinline__ void quantize_quarters(float (&v)[4][8], uint32_t q0,
+// U quarters q0 + 256u (u < U) of one wire image: in slot u a quad holds the
+// four quarters of one block, and lane j derives (and lane j < U stores) the
+// parameters of slot j mod U
+template <int C, int Stage, bool Full, bool Recv, int U>
+__device__ __forceinline__ void quantize_quarters(float (&v)[U][8], uint32_t q0,
                                                   uint32_t q_end, uint8_t* wire,
                                                   const Geo& g) {
-  uint8_t* const wp[4] = {wire, wire, wire, wire};
-  const uint32_t qs[4] = {q0, q0 + kThreads, q0 + 2 * kThreads, q0 + 3 * kThreads};
-  quantize_core<C, Stage, Full, 4, Recv>(v, wp, qs, wire, q0 + (threadIdx.x & 3) * kThreads,
-                                         q_end, g);
+  uint8_t* wp[U];
+  uint32_t qs[U];
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    wp[u] = wire;
+    qs[u] = q0 + u * kThreads;
+  }
+  quantize_core<C, Stage, Full, U, Recv>(v, wp, qs, wire,
+                                         q0 + ((threadIdx.x & 3) % U) * kThreads, q_end, g);
 }
 
-template <int C, int D, bool Full, bool Recv, int Stage = kStage0>
-__device__ __forceinline__ void quantize_tile(const u32x4 (&raw)[4], uint32_t q0,
+template <int C, int D, bool Full, bool Recv, int U, int Stage = kStage0>
+__device__ __forceinline__ void quantize_tile(const u32x4 (&raw)[U], uint32_t q0,
                                               uint8_t* wire, const Geo& g) {
-  float v[4][8];
+  float v[U][8];
 #pragma unroll
-  for (int u = 0; u < 4; u++) {
+  for (int u = 0; u < U; u++) {
     const uint32_t rw[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
     for (int k = 0; k < 4; k++) {
@@ -247,60 +253,57 @@ __device__ __forceinline__ void quantize_tile(const u32x4 (&raw)[4], uint32_t q0
       v[u][2 * k + 1] = ld16<D>(rw[k] >> 16);
     }
   }
-  quantize_quarters<C, Stage, Full, Recv>(v, q0, 4 * g.nb, wire, g);
+  quantize_quarters<C, Stage, Full, Recv, U>(v, q0, 4 * g.nb, wire, g);
 }
 
-template <bool Full>
+template <bool Full, int U>
 __device__ __forceinline__ void load_tile(const uint8_t* x, uint32_t q0, uint32_t n,
-                                          u32x4 (&raw)[4]) {
+                                          u32x4 (&raw)[U]) {
 #pragma unroll
-  for (int u = 0; u < 4; u++) {
+  for (int u = 0; u < U; u++) {
     const uint32_t q = q0 + u * kThreads;
     raw[u] = ld_in<kStage0>(reinterpret_cast<const u32x4*>(x) + (Full || 8 * q < n ? q : 0u));
   }
 }
 
-// true when every quarter of workgroup `wg` (quarters wg*1024 .. +1023) holds
-// 8 elements of an n-element buffer: a uniform branch to the path without
-// per-quarter range checks
-__device__ __forceinline__ bool tile_full(uint32_t wg, uint32_t n) {
-  return 8ull * ((uint64_t)wg + 1ull) * (kThreads * kPerLane) <= (uint64_t)n;
-}
-
-// a workgroup quantizes 256 blocks of rank blockIdx.y: one tile of the
-// receive buffer
-// The (tile, rank) a stage-0 workgroup takes.  Into W planar wire images:
-// blockIdx = (tile, rank), so that consecutive workgroups read and write
-// consecutive tiles of one rank.  Into the receive buffer: workgroup
-// t*W + r takes tile t of rank r, so that consecutive workgroups write
-// consecutive tiles of the buffer (the rank-major order writes it at a
+// The (unit, rank) a stage-0 workgroup takes, a unit being the
+// kThreads * K quarters or chunks the workgroup covers (4 / K units per tile
+// of the receive buffer).  Into W planar wire images: blockIdx = (unit,
+// rank), so that consecutive workgroups read and write consecutive units of
+// one rank.  Into the receive buffer: workgroup (t*W + r) * (4/K) + k takes
+// unit k of tile t of rank r, so that consecutive workgroups write
+// consecutive bytes of the buffer (the rank-major order writes it at a
 // stride of W tiles, which made stage 0 4-9% slower at W=8, 64 MB per rank).
-template <bool Recv>
-__device__ __forceinline__ void s0_item(int W, uint32_t tile0, uint32_t& tile, int& r) {
+template <bool Recv, int K>
+__device__ __forceinline__ void s0_item(int W, uint32_t tile0, uint32_t& unit, int& r) {
+  constexpr uint32_t per = 4 / K;               // units per tile
   if constexpr (Recv) {
-    tile = tile0 + blockIdx.x / (uint32_t)W;
-    r = (int)(blockIdx.x % (uint32_t)W);
+    const uint32_t tw = blockIdx.x / per;         // (tile - tile0) * W + r
+    unit = (tile0 + tw / (uint32_t)W) * per + blockIdx.x % per;
+    r = (int)(tw % (uint32_t)W);
   } else {
-    tile = blockIdx.x;
+    unit = blockIdx.x;
     r = blockIdx.y;
   }
 }
 
 template <int C, int D, bool Recv>
 __global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires, Geo g, int W) {
-  static_assert(kPerLane == 4, "one block per lane of the quad");
-  static_assert(kThreads * kPerLane / 4 == kTileBlocks, "a workgroup's blocks are one tile");
-  uint32_t tile;
+  constexpr int U = kS0PerLane;
+  static_assert(kThreads == kTileBlocks && 4 % U == 0, "4 / U workgroups per tile");
+  uint32_t unit;
   int r;
-  s0_item<Recv>(W, g.tile0, tile, r);
-  const uint32_t q0 = tile * (kThreads * kPerLane) + threadIdx.x;
-  u32x4 raw[4];
-  if (tile_full(tile, g.n)) {
-    load_tile<true>(xs.p[r], q0, g.n, raw);
-    quantize_tile<C, D, true, Recv>(raw, q0, wires.p[r], g);
+  s0_item<Recv, U>(W, g.tile0, unit, r);
+  const uint32_t q0 = unit * (kThreads * U) + threadIdx.x;
+  u32x4 raw[U];
+  // uniform: every quarter of the workgroup holds 8 elements (the path
+  // without per-quarter range checks)
+  if (8ull * ((uint64_t)unit + 1ull) * (kThreads * U) <= (uint64_t)g.n) {
+    load_tile<true, U>(xs.p[r], q0, g.n, raw);
+    quantize_tile<C, D, true, Recv, U>(raw, q0, wires.p[r], g);
   } else {
-    load_tile<false>(xs.p[r], q0, g.n, raw);
-    quantize_tile<C, D, false, Recv>(raw, q0, wires.p[r], g);
+    load_tile<false, U>(xs.p[r], q0, g.n, raw);
+    quantize_tile<C, D, false, Recv, U>(raw, q0, wires.p[r], g);
   }
 }
 
@@ -319,12 +322,12 @@ __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
   // stage 0 (into the receive buffer, or planar) keeps one tile per
   // workgroup; stage 2 (planar) takes kS2PerLane chunks per lane
   constexpr int K = Stage == 0 ? kPerLane : kS2PerLane;
-  uint32_t tile;
+  uint32_t unit;
   int r;
-  s0_item<Recv>(W, tile0, tile, r);
+  s0_item<Recv, Stage == 0 ? kPerLane : 4>(W, tile0, unit, r);
   const u32x4* s = reinterpret_cast<const u32x4*>(src.p[r]);
   uint8_t* d = dst.p[r];
-  const uint32_t base = tile * (kThreads * K) + threadIdx.x;
+  const uint32_t base = unit * (kThreads * K) + threadIdx.x;
   u32x4 q[K];
 #pragma unroll
   for (int j = 0; j < K; j++) {
@@ -790,7 +793,9 @@ void q_launch(int W, const InPtrs& xs, const OutPtrs& wires, const Layout& L, hi
     const size_t nt = tiles - t0 < per ? tiles - t0 : per;
     const OutPtrs w = Recv ? at_tile(wires, W, L, t0) : wires;
     const Geo g = geo(L, W, Recv, Recv ? t0 : 0);
-    const dim3 grid = Recv ? dim3((unsigned)(nt * W)) : dim3((unsigned)nt, W);
+    // quantized: 4 / kS0PerLane workgroups per tile; FP: one
+    const size_t per = C == kFP ? 1 : 4 / kS0PerLane;
+    const dim3 grid = Recv ? dim3((unsigned)(nt * W * per)) : dim3((unsigned)(nt * per), W);
     if constexpr (C == kFP) {
       // the FP wire holds the buffer's raw elements (binary16 under the cast)
       constexpr int Dw = D == kBF16H ? kF16 : D;

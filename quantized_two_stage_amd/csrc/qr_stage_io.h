@@ -25,6 +25,15 @@ constexpr int kPerLane = 4;        // quarters / chunks per lane (k_quantize and
 #define QR_S2_U 1
 #endif
 constexpr int kS2PerLane = QR_S2_U;
+// Quarters per lane of k_quantize (1, 2 or 4; a quad of lanes holds one
+// block per quarter slot, and lane j derives slot j mod U's parameters).
+// Two: half a tile per workgroup, which measured 1% faster than four over the
+// W=8 64 MB allreduces and the same at W=2; with one, every lane of a quad
+// derives the same block's parameters, and stage 0 was 2-8% slower.
+#ifndef QR_S0_U
+#define QR_S0_U 2
+#endif
+constexpr int kS0PerLane = QR_S0_U;
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X):
 // QR_NT_STORE bit mask of the stages (1 = stage 0, 2 = stage 1, 4 = stage 2)
