@@ -317,7 +317,7 @@ template <int Stage, int Din, int Dout, bool Recv>
 __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
                                                    uint32_t nchunks, uint32_t tstride,
                                                    uint32_t tile0, int W) {
-  static_assert(kThreads * kPerLane == kTileBlocks * 4, "a workgroup's chunks are one tile");
+  static_assert(kThreads * kPerLane == kTileBlocks * 4, "stage 0: a workgroup's chunks are one tile");
   constexpr int kS = Stage == 0 ? kStage0 : kStage2;
   // stage 0 (into the receive buffer, or planar) keeps one tile per
   // workgroup; stage 2 (planar) takes kS2PerLane chunks per lane
