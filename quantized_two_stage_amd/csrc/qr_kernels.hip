@@ -426,14 +426,15 @@ __device__ __forceinline__ void s1_reduce_store(const S1In<C, W>& in, uint8_t* r
   s1_store<C>(red, blk, g, w, p.s, p.z);
 }
 
-// one lane per block
+// one lane per block, s1_threads(W) lanes per workgroup
 template <int C, int D, int W, bool Recv>
 __global__ __launch_bounds__(kThreads) void k_stage1(InPtrs wires, uint8_t* red,
                                                      uint32_t blk_lo, uint32_t blk_hi,
                                                      Geo g) {
-  const uint32_t blk = blk_lo + blockIdx.x * kThreads + threadIdx.x;
+  constexpr uint32_t TB = s1_threads(W);
+  const uint32_t blk = blk_lo + blockIdx.x * TB + threadIdx.x;
   // uniform: every block of the workgroup is in range and holds 32 elements
-  const uint32_t wg_end = blk_lo + (blockIdx.x + 1) * kThreads;
+  const uint32_t wg_end = blk_lo + (blockIdx.x + 1) * TB;
   if (wg_end <= blk_hi && (uint64_t)wg_end * kBlock <= (uint64_t)g.n) {
     S1In<C, W> in;
     s1_load<C, W, Recv>(wires, blk, g, in);
@@ -756,8 +757,8 @@ void s1_launch(const InPtrs& wires, uint8_t* red, size_t blk_lo, size_t blk_hi,
                          dim3(groups(c_hi - c_lo, kThreads * kPerLane)), dim3(kThreads), 0, st,
                          w, out, c_lo, c_hi, g.tstride, g.tile0);
     } else {
-      hipLaunchKernelGGL((k_stage1<C, D, W, Recv>), dim3(groups(hi - lo, kThreads)),
-                         dim3(kThreads), 0, st, w, red, (uint32_t)lo, (uint32_t)hi, g);
+      hipLaunchKernelGGL((k_stage1<C, D, W, Recv>), dim3(groups(hi - lo, s1_threads(W))),
+                         dim3(s1_threads(W)), 0, st, w, red, (uint32_t)lo, (uint32_t)hi, g);
     }
   }
 }

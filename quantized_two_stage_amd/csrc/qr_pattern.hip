@@ -22,7 +22,7 @@ template <int C, int W>
 __global__ __launch_bounds__(kThreads) void k_stage1_pattern(InPtrs wires, uint8_t* red,
                                                              uint32_t nb, Geo g) {
   using T = CodecT<C>;
-  const uint32_t blk = blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t blk = blockIdx.x * s1_threads(W) + threadIdx.x;
   if (blk >= nb) return;
   S1In<C, W> in;
   s1_load<C, W, true>(wires, blk, g, in);
@@ -83,8 +83,9 @@ void launch(const InPtrs& in, uint8_t* red, size_t n, hipStream_t st) {
     const size_t off_z = a256(off_s + 2 * nb);
     const uint32_t tile = kTileBlocks * (T::block_bytes + 2 + (T::asym ? 2 : 0));
     const Geo g{(uint32_t)n, (uint32_t)nb, (uint32_t)off_s, (uint32_t)off_z, W * tile, 0u};
-    hipLaunchKernelGGL((k_stage1_pattern<C, W>), dim3((unsigned)((nb + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, st, in, red, (uint32_t)nb, g);
+    hipLaunchKernelGGL((k_stage1_pattern<C, W>),
+                       dim3((unsigned)((nb + s1_threads(W) - 1) / s1_threads(W))),
+                       dim3(s1_threads(W)), 0, st, in, red, (uint32_t)nb, g);
   }
 }
 

@@ -128,6 +128,11 @@ __device__ __forceinline__ uint32_t fp_chunk(uint32_t tstride, uint32_t tile0, u
   return c * 16u;
 }
 
+// Lanes per workgroup of stage 1 (one block per lane): 128 at W = 2, which
+// measured 3-5% faster than 256 for the 8-, 6- and 4-bit codecs there; 256
+// from W = 4 on, where 128 and 64 were no faster.
+constexpr int s1_threads(int W) { return W == 2 ? 128 : kThreads; }
+
 // the W code blocks and scales (and zeros) of one block index
 template <int C, int W>
 struct S1In {
