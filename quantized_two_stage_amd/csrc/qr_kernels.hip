@@ -19,19 +19,20 @@
 // Every kernel streams HBM; nothing is a contraction, so no MFMA and no LDS.
 //   - k_quantize and k_dequant work on quarter blocks (8 elements = 16
 //     contiguous bytes of 16-bit data, consecutive lanes on consecutive
-//     quarters).  k_quantize takes kS0PerLane quarters per lane, issued
-//     before any is used, so that a quad of lanes holds the quarters of that
-//     many blocks: it reduces each block's max/min with DPP quad permutes,
-//     lane j derives the scale of block j mod kS0PerLane, and 1/s reaches the
-//     other lanes by a DPP broadcast (a few instructions, instead of a round
-//     trip through LDS).  k_dequant takes kS2PerLane quarters per lane.
+//     quarters).  k_quantize takes U = 4 or 2 quarters per lane (by size,
+//     s0_quarters_per_lane), issued before any is used, so that a quad of
+//     lanes holds the quarters of U blocks: it reduces each block's max/min
+//     with DPP quad permutes, lane j derives the scale of block j mod U, and
+//     1/s reaches the other lanes by a DPP broadcast (a few instructions,
+//     instead of a round trip through LDS).  k_dequant takes 4 or 1 quarters
+//     per lane (s2_quarters_per_lane).
 //   - k_stage1 gives each lane a whole block: W code blocks of 16/24/32
 //     contiguous bytes and W scales in, one code block and scale out; the
 //     per-block work (max/min, two divisions, rounding of the scale) is done
 //     once, which matters because this kernel is the one closest to the
 //     VALU limit (W=2, 4-bit codes: 1.7 bytes of HBM per element).
-//   - the FP kernels give each lane 16-byte chunks, four per lane
-//     (kS2PerLane in stage 2).
+//   - the FP kernels give each lane 16-byte chunks, four per lane (stage
+//     2: as k_dequant).
 //   - k_fused gives each lane one quarter block of every rank (a workgroup
 //     holds 64 blocks) and quantizes four ranks at a time as the four slots
 //     of the quad quantizer.
@@ -79,7 +80,7 @@ struct QuarterIO {
 };
 
 // ---------------------------------------------------------------------------
-// stage 0: quarter blocks, U = kS0PerLane per lane.  For each u the four
+// stage 0: quarter blocks, U (4 or 2) per lane.  For each u the four
 // lanes of a quad hold the four quarters of one block, so a quad covers U
 // blocks.  Every lane reduces the max/min of all U blocks across the quad,
 // then lane j derives the scale (and zero) of block j mod U and hands 1/s,
@@ -287,9 +288,8 @@ __device__ __forceinline__ void s0_item(int W, uint32_t tile0, uint32_t& unit, i
   }
 }
 
-template <int C, int D, bool Recv>
+template <int C, int D, bool Recv, int U>
 __global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires, Geo g, int W) {
-  constexpr int U = kS0PerLane;
   static_assert(kThreads == kTileBlocks && 4 % U == 0, "4 / U workgroups per tile");
   uint32_t unit;
   int r;
@@ -313,15 +313,15 @@ __global__ __launch_bounds__(kThreads) void k_quantize(InPtrs xs, OutPtrs wires,
 // every element (the cast option: bfloat16 into a binary16 wire at stage 0,
 // binary16 back to bfloat16 at stage 2); Recv: the destination is a rank's
 // tiles of the receive buffer
-template <int Stage, int Din, int Dout, bool Recv>
+template <int Stage, int Din, int Dout, bool Recv, int K = kPerLane>
 __global__ __launch_bounds__(kThreads) void k_copy(InPtrs src, OutPtrs dst,
                                                    uint32_t nchunks, uint32_t tstride,
                                                    uint32_t tile0, int W) {
   static_assert(kThreads * kPerLane == kTileBlocks * 4, "stage 0: a workgroup's chunks are one tile");
   constexpr int kS = Stage == 0 ? kStage0 : kStage2;
   // stage 0 (into the receive buffer, or planar) keeps one tile per
-  // workgroup; stage 2 (planar) takes kS2PerLane chunks per lane
-  constexpr int K = Stage == 0 ? kPerLane : kS2PerLane;
+  // workgroup; stage 2 (planar) takes K chunks per lane
+  static_assert(Stage != 0 || K == kPerLane, "stage 0: one tile per workgroup");
   uint32_t unit;
   int r;
   s0_item<Recv, Stage == 0 ? kPerLane : 4>(W, tile0, unit, r);
@@ -426,12 +426,11 @@ __device__ __forceinline__ void s1_reduce_store(const S1In<C, W>& in, uint8_t* r
   s1_store<C>(red, blk, g, w, p.s, p.z);
 }
 
-// one lane per block, s1_threads(W) lanes per workgroup
-template <int C, int D, int W, bool Recv>
+// one lane per block, TB lanes per workgroup
+template <int C, int D, int W, bool Recv, int TB>
 __global__ __launch_bounds__(kThreads) void k_stage1(InPtrs wires, uint8_t* red,
                                                      uint32_t blk_lo, uint32_t blk_hi,
                                                      Geo g) {
-  constexpr uint32_t TB = s1_threads(W);
   const uint32_t blk = blk_lo + blockIdx.x * TB + threadIdx.x;
   // uniform: every block of the workgroup is in range and holds 32 elements
   const uint32_t wg_end = blk_lo + (blockIdx.x + 1) * TB;
@@ -488,10 +487,10 @@ __global__ __launch_bounds__(kThreads) void k_sum_fp(InPtrs xs, OutPtrs outs,
 }
 
 // ---------------------------------------------------------------------------
-// stage 2 / dequantize: quarter blocks, kS2PerLane per lane
+// stage 2 / dequantize: quarter blocks, U per lane
 
 // quarters q0 + 256u (u < U) of the wire -> y; Full: all hold 8 elements
-template <int C, int D, bool Full, int Stage = kStage2, int U = kS2PerLane>
+template <int C, int D, bool Full, int U, int Stage = kStage2>
 __device__ __forceinline__ void dequant_tile(const uint8_t* wire, uint8_t* y, uint32_t q0,
                                              uint32_t nq, const Geo& g) {
   using T = CodecT<C>;
@@ -522,16 +521,16 @@ __device__ __forceinline__ void dequant_tile(const uint8_t* wire, uint8_t* y, ui
   }
 }
 
-template <int C, int D>
+template <int C, int D, int U>
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* wire, OutPtrs ys,
                                                       Geo g) {
   const int r = blockIdx.y;
   const uint32_t nq = (g.n + 7) / 8;                // quarters that hold data
-  const uint32_t q0 = blockIdx.x * (kThreads * kS2PerLane) + threadIdx.x;
-  if (8ull * ((uint64_t)blockIdx.x + 1ull) * (kThreads * kS2PerLane) <= (uint64_t)g.n)
-    dequant_tile<C, D, true>(wire, ys.p[r], q0, nq, g);
+  const uint32_t q0 = blockIdx.x * (kThreads * U) + threadIdx.x;
+  if (8ull * ((uint64_t)blockIdx.x + 1ull) * (kThreads * U) <= (uint64_t)g.n)
+    dequant_tile<C, D, true, U>(wire, ys.p[r], q0, nq, g);
   else
-    dequant_tile<C, D, false>(wire, ys.p[r], q0, nq, g);
+    dequant_tile<C, D, false, U>(wire, ys.p[r], q0, nq, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -757,8 +756,17 @@ void s1_launch(const InPtrs& wires, uint8_t* red, size_t blk_lo, size_t blk_hi,
                          dim3(groups(c_hi - c_lo, kThreads * kPerLane)), dim3(kThreads), 0, st,
                          w, out, c_lo, c_hi, g.tstride, g.tile0);
     } else {
-      hipLaunchKernelGGL((k_stage1<C, D, W, Recv>), dim3(groups(hi - lo, s1_threads(W))),
-                         dim3(s1_threads(W)), 0, st, w, red, (uint32_t)lo, (uint32_t)hi, g);
+      bool launched = false;
+      if constexpr (W == 2) {
+        if (s1_lanes_per_workgroup(W, L.nb) == 128) {
+          hipLaunchKernelGGL((k_stage1<C, D, W, Recv, 128>), dim3(groups(hi - lo, 128)),
+                             dim3(128), 0, st, w, red, (uint32_t)lo, (uint32_t)hi, g);
+          launched = true;
+        }
+      }
+      if (!launched)
+        hipLaunchKernelGGL((k_stage1<C, D, W, Recv, kThreads>), dim3(groups(hi - lo, kThreads)),
+                           dim3(kThreads), 0, st, w, red, (uint32_t)lo, (uint32_t)hi, g);
     }
   }
 }
@@ -785,26 +793,28 @@ void s1_by_w(int W, const InPtrs& wires, bool recv, uint8_t* red, size_t lo, siz
 
 template <int C, int D, bool Recv>
 void q_launch(int W, const InPtrs& xs, const OutPtrs& wires, const Layout& L, hipStream_t st) {
-  // a workgroup quantizes one tile of one rank; into the receive buffer over
-  // tile ranges [t0, t1) as for stage 1
+  // a workgroup quantizes a tile (FP: copies it), or half a tile, of one
+  // rank; into the receive buffer over tile ranges [t0, t1) as for stage 1
   const size_t tiles = C == kFP ? groups(L.n / 8, kThreads * kPerLane)
                                 : groups(4 * L.nb, kThreads * kPerLane);
   const size_t per = Recv ? recv_tiles_per_launch(W, L) : tiles + 1;
+  const int U = C == kFP ? kPerLane : s0_quarters_per_lane(W, L.n);
+  const size_t wpt = 4 / U;                            // workgroups per tile
   for (size_t t0 = 0; t0 < tiles; t0 += per) {
     const size_t nt = tiles - t0 < per ? tiles - t0 : per;
     const OutPtrs w = Recv ? at_tile(wires, W, L, t0) : wires;
     const Geo g = geo(L, W, Recv, Recv ? t0 : 0);
-    // quantized: 4 / kS0PerLane workgroups per tile; FP: one
-    const size_t per = C == kFP ? 1 : 4 / kS0PerLane;
-    const dim3 grid = Recv ? dim3((unsigned)(nt * W * per)) : dim3((unsigned)(nt * per), W);
+    const dim3 grid = Recv ? dim3((unsigned)(nt * W * wpt)) : dim3((unsigned)(nt * wpt), W);
     if constexpr (C == kFP) {
       // the FP wire holds the buffer's raw elements (binary16 under the cast)
       constexpr int Dw = D == kBF16H ? kF16 : D;
       constexpr int Din = D == kBF16H ? kBF16 : D;
       hipLaunchKernelGGL((k_copy<0, Din, Dw, Recv>), grid, dim3(kThreads), 0, st, xs, w,
                          (uint32_t)(L.n / 8), g.tstride, g.tile0, W);
+    } else if (U == 2) {
+      hipLaunchKernelGGL((k_quantize<C, D, Recv, 2>), grid, dim3(kThreads), 0, st, xs, w, g, W);
     } else {
-      hipLaunchKernelGGL((k_quantize<C, D, Recv>), grid, dim3(kThreads), 0, st, xs, w, g, W);
+      hipLaunchKernelGGL((k_quantize<C, D, Recv, 4>), grid, dim3(kThreads), 0, st, xs, w, g, W);
     }
   }
 }
@@ -826,12 +836,19 @@ void dq_dispatch(int W, const uint8_t* wire, const OutPtrs& ys, const Layout& L,
     for (int r = 0; r < kMaxRanks; r++) src.p[r] = wire;
     constexpr int Dw = D == kBF16H ? kF16 : D;
     constexpr int Dout = D == kBF16H ? kBF16 : D;
-    hipLaunchKernelGGL((k_copy<2, Dw, Dout, false>),
-                       dim3(groups(L.n / 8, kThreads * kS2PerLane), W), dim3(kThreads), 0, st,
-                       src, ys, (uint32_t)(L.n / 8), 0u, 0u, W);
+    if (s2_quarters_per_lane(W, L.n) == 1)
+      hipLaunchKernelGGL((k_copy<2, Dw, Dout, false, 1>), dim3(groups(L.n / 8, kThreads), W),
+                         dim3(kThreads), 0, st, src, ys, (uint32_t)(L.n / 8), 0u, 0u, W);
+    else
+      hipLaunchKernelGGL((k_copy<2, Dw, Dout, false, 4>), dim3(groups(L.n / 8, kThreads * 4), W),
+                         dim3(kThreads), 0, st, src, ys, (uint32_t)(L.n / 8), 0u, 0u, W);
   } else {
-    hipLaunchKernelGGL((k_dequant<C, D>), dim3(groups(L.n / 8, kThreads * kS2PerLane), W),
-                       dim3(kThreads), 0, st, wire, ys, geo(L));
+    if (s2_quarters_per_lane(W, L.n) == 1)
+      hipLaunchKernelGGL((k_dequant<C, D, 1>), dim3(groups(L.n / 8, kThreads), W),
+                         dim3(kThreads), 0, st, wire, ys, geo(L));
+    else
+      hipLaunchKernelGGL((k_dequant<C, D, 4>), dim3(groups(L.n / 8, kThreads * 4), W),
+                         dim3(kThreads), 0, st, wire, ys, geo(L));
   }
 }
 

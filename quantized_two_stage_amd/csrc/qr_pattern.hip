@@ -18,11 +18,11 @@
 namespace qr {
 namespace {
 
-template <int C, int W>
+template <int C, int W, int TB>
 __global__ __launch_bounds__(kThreads) void k_stage1_pattern(InPtrs wires, uint8_t* red,
                                                              uint32_t nb, Geo g) {
   using T = CodecT<C>;
-  const uint32_t blk = blockIdx.x * s1_threads(W) + threadIdx.x;
+  const uint32_t blk = blockIdx.x * TB + threadIdx.x;
   if (blk >= nb) return;
   S1In<C, W> in;
   s1_load<C, W, true>(wires, blk, g, in);
@@ -83,9 +83,14 @@ void launch(const InPtrs& in, uint8_t* red, size_t n, hipStream_t st) {
     const size_t off_z = a256(off_s + 2 * nb);
     const uint32_t tile = kTileBlocks * (T::block_bytes + 2 + (T::asym ? 2 : 0));
     const Geo g{(uint32_t)n, (uint32_t)nb, (uint32_t)off_s, (uint32_t)off_z, W * tile, 0u};
-    hipLaunchKernelGGL((k_stage1_pattern<C, W>),
-                       dim3((unsigned)((nb + s1_threads(W) - 1) / s1_threads(W))),
-                       dim3(s1_threads(W)), 0, st, in, red, (uint32_t)nb, g);
+    // the workgroup size stage 1 takes for this size (s1_lanes_per_workgroup)
+    if (s1_lanes_per_workgroup(W, nb) == 128)
+      hipLaunchKernelGGL((k_stage1_pattern<C, W, 128>), dim3((unsigned)((nb + 127) / 128)),
+                         dim3(128), 0, st, in, red, (uint32_t)nb, g);
+    else
+      hipLaunchKernelGGL((k_stage1_pattern<C, W, kThreads>),
+                         dim3((unsigned)((nb + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
+                         in, red, (uint32_t)nb, g);
   }
 }
 

@@ -16,24 +16,26 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPerLane = 4;        // quarters / chunks per lane (k_quantize and
                                    // the FP kernels of stages 0 and 1)
-// Quarters (16-byte chunks of output) per lane of stage 2 (k_dequant and the
-// FP stage-2 copy).  One: four times the workgroups of the four-per-lane
-// form, which measured 2% faster over the W=8 64 MB allreduces (stage 2 is
-// the writes of W outputs; more, smaller workgroups keep more of them in
-// flight).
-#ifndef QR_S2_U
-#define QR_S2_U 1
-#endif
-constexpr int kS2PerLane = QR_S2_U;
-// Quarters per lane of k_quantize (1, 2 or 4; a quad of lanes holds one
-// block per quarter slot, and lane j derives slot j mod U's parameters).
-// Two: half a tile per workgroup, which measured 1% faster than four over the
-// W=8 64 MB allreduces and the same at W=2; with one, every lane of a quad
-// derives the same block's parameters, and stage 0 was 2-8% slower.
-#ifndef QR_S0_U
-#define QR_S0_U 2
-#endif
-constexpr int kS0PerLane = QR_S0_U;
+// Launch shapes chosen by size.  Finer work items (fewer quarters per lane,
+// smaller workgroups) measured faster on the largest grids and slower on
+// mid-size ones (8-32 MB per rank), where the coarser form's fewer
+// workgroups win; the thresholds sit between the measured points.
+//   stage 0: quarters per lane of k_quantize (the quad quantizer's slots):
+//            2 from W*n >= 2^28 elements (1% faster at W=8, 64 MB per rank),
+//            else 4 (2 was 3% slower at W*n = 2^26, the same at 2^27);
+//   stage 2: quarters per lane of k_dequant and the FP copy: 1 from
+//            W*n >= 2^26 (1-3% faster at W = 4 and 8), else 4;
+//   stage 1: lanes per workgroup, one block per lane: 128 at W = 2 from
+//            2^20 blocks per rank (3-5% faster at 64 MB per rank), else 256.
+inline int s0_quarters_per_lane(int W, size_t n) {
+  return (uint64_t)W * n >= (1ull << 28) ? 2 : 4;
+}
+inline int s2_quarters_per_lane(int W, size_t n) {
+  return (uint64_t)W * n >= (1ull << 26) ? 1 : 4;
+}
+inline int s1_lanes_per_workgroup(int W, size_t nb) {
+  return W == 2 && nb >= (1u << 20) ? 128 : kThreads;
+}
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X):
 // QR_NT_STORE bit mask of the stages (1 = stage 0, 2 = stage 1, 4 = stage 2)
@@ -127,11 +129,6 @@ __device__ __forceinline__ uint32_t fp_chunk(uint32_t tstride, uint32_t tile0, u
   if constexpr (Recv) return (c / kTC - tile0) * tstride + (c % kTC) * 16u;
   return c * 16u;
 }
-
-// Lanes per workgroup of stage 1 (one block per lane): 128 at W = 2, which
-// measured 3-5% faster than 256 for the 8-, 6- and 4-bit codecs there; 256
-// from W = 4 on, where 128 and 64 were no faster.
-constexpr int s1_threads(int W) { return W == 2 ? 128 : kThreads; }
 
 // the W code blocks and scales (and zeros) of one block index
 template <int C, int W>
