@@ -595,8 +595,22 @@ def min_sizes(sweep, margin=MIN_SIZE_MARGIN):
     return out, marginal
 
 
+def launch_floor(torch, stream, iters=100, repeats=3):
+    """the device time of one launch of a kernel that does nothing (torch's
+    spin kernel asked for zero cycles), timed as every sweep point is: the
+    floor under any one-launch call"""
+    meds = []
+    for _ in range(repeats):
+        for _ in range(3):
+            torch.cuda._sleep(0)
+        meds.append(float(np.median(time_each(lambda: torch.cuda._sleep(0), iters, stream))))
+    return {"us": float(np.median(meds)), "spread": float(max(meds) - min(meds))}
+
+
 def measure_extra(args, qr, I, torch, stream, log):
     extra = {}
+    log("bench: launch floor (an empty kernel, timed as the sweeps are)")
+    extra["launch_floor"] = launch_floor(torch, stream)
     for cid in (2, 4):
         c = I.CONFIGS[cid]
         log("bench: config %d (%s)" % (cid, c["desc"]))
