@@ -43,7 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "effective GB/s and μs per simulated allreduce, 4KB–64MB, W=2/4/8, per codec"
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "bench_w8_fp16_64MB_stage1_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_two_stage_amd", "csrc", f)
                   for f in ("qr_kernels.hip", "qr_device.h", "qr_stage_io.h")]
 STAGES = ("quantize", "stage1", "stage2")

@@ -42,9 +42,10 @@ def test_bench_prints_the_contract_line():
         abs(r["frac"] - min(r["per_codec_frac"].values())) < 1e-4
     assert set(r["per_codec_frac"]) == set(r["pattern_frac"]) == set(r["copy_frac"]) == \
         set(r["in_pipeline_frac"])
-    # traffic: the calibrated counters of profiles/traffic.json, reported only
+    # traffic: the calibrated stage-1 counters under profiles/, reported only
     # while the kernel sources are those the counters were taken on
-    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+    with open(os.path.join(ROOT, "profiles",
+                           "bench_w8_fp16_64MB_stage1_traffic.json")) as f:
         tj = json.load(f)
     codec = r["kernel"].split(",")[-2].strip()          # "<kernel> (...), <codec>, cold"
     if tj["source_sha"] == d["kernel_source_sha"]:
