@@ -114,6 +114,25 @@ def test_config5_full(qr, codec):
     _check_full(qr, 5, codec)
 
 
+# Sizes just past the workloads' own, with ragged tails, so that the launch
+# shapes the library picks for large grids (stage 0 with two quarters per lane
+# from W*n >= 2^28, stage 2 with one from W*n >= 2^26, stage 1 at W=2 with
+# 128-lane workgroups from 2^20 blocks) run their range-checked paths: at W=8
+# the last tile holds 6 blocks, the last of them 8 elements, so whole stage-0
+# and stage-2 workgroups lie past the end; at W=2 the last 128-lane stage-1
+# workgroup holds 3 blocks, the last of them 24 elements.
+RAGGED_N = {5: (1 << 25) + 32 * 5 + 8, 2: (1 << 25) + 32 * 130 + 24}
+
+
+RAGGED_CASES = [(5, O.FP), (5, O.FP8), (5, O.Q6A), (5, O.Q4A), (2, O.FP), (2, O.Q8), (2, O.Q4)]
+
+
+@pytest.mark.parametrize("cfg,codec", RAGGED_CASES,
+                         ids=["cfg%d-%s" % (c, I.CODEC_NAMES[k]) for c, k in RAGGED_CASES])
+def test_large_shapes_ragged(qr, cfg, codec):
+    _check_full(qr, cfg, codec, n=RAGGED_N[cfg])
+
+
 @pytest.mark.parametrize("codec", (O.Q4, O.FP8, O.FP))
 def test_max_size(qr, codec):
     """n = 2^30 elements (QR_MAX_BYTES = 2 GiB per rank), W = 2: the largest
