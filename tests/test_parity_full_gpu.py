@@ -121,16 +121,20 @@ def test_config5_full(qr, codec):
 # the last tile holds 6 blocks, the last of them 8 elements, so whole stage-0
 # and stage-2 workgroups lie past the end; at W=2 the last 128-lane stage-1
 # workgroup holds 3 blocks, the last of them 24 elements.
-RAGGED_N = {5: (1 << 25) + 32 * 5 + 8, 2: (1 << 25) + 32 * 130 + 24}
+# The bf16 workload's recipe (W=8) at the same size takes the large-grid stage
+# 0 from bfloat16 and through the cast option.
+RAGGED_N = {5: (1 << 25) + 32 * 5 + 8, 2: (1 << 25) + 32 * 130 + 24, 4: (1 << 25) + 32 * 5 + 8}
+CAST = O.BF16_VIA_FP16
+RAGGED_CASES = [(5, O.FP, None), (5, O.FP8, None), (5, O.Q6A, None), (5, O.Q4A, None),
+                (2, O.FP, None), (2, O.Q8, None), (2, O.Q4, None),
+                (4, O.Q6, None), (4, O.FP, None), (4, O.Q4A, CAST), (4, O.FP8, CAST)]
 
 
-RAGGED_CASES = [(5, O.FP), (5, O.FP8), (5, O.Q6A), (5, O.Q4A), (2, O.FP), (2, O.Q8), (2, O.Q4)]
-
-
-@pytest.mark.parametrize("cfg,codec", RAGGED_CASES,
-                         ids=["cfg%d-%s" % (c, I.CODEC_NAMES[k]) for c, k in RAGGED_CASES])
-def test_large_shapes_ragged(qr, cfg, codec):
-    _check_full(qr, cfg, codec, n=RAGGED_N[cfg])
+@pytest.mark.parametrize("cfg,codec,dtype", RAGGED_CASES,
+                         ids=["cfg%d-%s%s" % (c, I.CODEC_NAMES[k], "-cast" if d == CAST else "")
+                              for c, k, d in RAGGED_CASES])
+def test_large_shapes_ragged(qr, cfg, codec, dtype):
+    _check_full(qr, cfg, codec, n=RAGGED_N[cfg], dtype=dtype)
 
 
 @pytest.mark.parametrize("codec", (O.Q4, O.FP8, O.FP))
