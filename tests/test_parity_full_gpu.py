@@ -10,8 +10,9 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import (assert_bytes_equal, assert_recv_equal, assert_within_ulp, dev16, host16,
-                      hostu8, oracle_whole, plane_slices, recv_tile_bytes, sample_windows, say)
+from gpu_util import (assert_bytes_equal, assert_recv_equal, assert_within_ulp, block_ranges,
+                      dev16, host16, hostu8, oracle_whole, plane_slices, recv_tile_bytes,
+                      sample_windows, say)
 from quantized_two_stage_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -195,6 +196,47 @@ def test_max_size_w8(qr, codec):
             assert_within_ulp(host16(ys[r][e0:e1]), want, dtype,
                               "max W=8 rank %d y %d..%d" % (r, lo, hi))
     del xs, ys, ws
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("codec", (O.FP, O.Q8A), ids=("fp", "q8a"))
+def test_max_size_w8_owner(qr, codec):
+    """Stage 1 of one owner from the receive buffer at n = 2^30 elements per
+    rank, W = 8, for the owner whose chunk crosses the first launch split (a
+    launch spans (2^32 - 1) // (W * tile bytes) - 1 tiles): the reduced image
+    is cleared first, then the owner's blocks are compared with the oracle in
+    windows across the split and at the chunk's ends, and the blocks just
+    outside the chunk must still hold the clear pattern."""
+    n, W, dtype = 1 << 30, 8, O.FP16
+    nb = n // 32
+    split = ((2 ** 32 - 1) // (W * recv_tile_bytes(codec)) - 1) * 256
+    bpc = (nb + W - 1) // W
+    owner = split // bpc
+    c_lo, c_hi = owner * bpc, min(nb, (owner + 1) * bpc)
+    assert c_lo < split - 32 and split + 32 < c_hi
+    say("max size W=8 owner", owner, "codec", codec)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9696 + codec)
+    xs = [torch.randn(n, generator=g, device="cuda", dtype=torch.float32)
+          .to(torch.float16).view(torch.int16) for _ in range(W)]
+    recv = qr.alloc_recv(W, codec, n)
+    red = qr.alloc_wire(codec, n)
+    qr.qr_quantize_recv(codec, xs, recv, dtype=dtype)
+    red.fill_(0xA7)
+    qr.qr_reduce_recv(codec, W, recv, n, red, dtype, owner=owner)
+    torch.cuda.synchronize()
+    for (lo, hi) in [(split - 32, split + 32), (c_lo, c_lo + 64), (c_hi - 64, c_hi)]:
+        loc = [host16(x[32 * lo:32 * hi]) for x in xs]
+        _, want, _ = oracle_whole(codec, dtype, loc)
+        mine, theirs = block_ranges(codec, n, lo, hi), block_ranges(codec, 32 * (hi - lo), 0, hi - lo)
+        for name, (a, e) in mine.items():
+            a2, e2 = theirs[name]
+            assert_bytes_equal(hostu8(red[a:e]), want[a2:e2],
+                               "owner %d blocks %d..%d %s" % (owner, lo, hi, name))
+    for (lo, hi) in [(c_lo - 64, c_lo), (c_hi, c_hi + 64)]:
+        for name, (a, e) in block_ranges(codec, n, lo, hi).items():
+            assert bool(torch.all(red[a:e] == 0xA7)), ("written outside the chunk", name, lo, hi)
+    del xs, recv, red
     torch.cuda.empty_cache()
 
 
