@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "qr_device.h"
 #include "qr_internal.h"
 
@@ -35,6 +37,81 @@ inline int s2_quarters_per_lane(int W, size_t n) {
 }
 inline int s1_lanes_per_workgroup(int W, size_t nb) {
   return W == 2 && nb >= (1u << 20) ? 128 : kThreads;
+}
+
+// Full rounds.  A stage-1 grid gives each CU few workgroups (16 at W=8 and
+// 64 MB per rank), and when the kernel's occupancy does not divide that
+// number the last round runs nearly empty: 16 workgroups at 5 per CU run as
+// 5 + 5 + 5 + 1, the last with no other wave to hide its loads behind, where
+// 4 per CU run as four full rounds (Q4A 3.6% and Q6A 1.8% faster at W=8,
+// 64 MB per rank, whose registers allow 5; no change for the codecs whose
+// registers allow 3 or 4).  round_cap_lds<Kernel> gives the dynamic LDS,
+// which the kernels leave unused, that caps a launch of `groups` workgroups
+// at the fewest workgroups per CU that keep its number of rounds; 0 where
+// the kernel's own occupancy already does, where the cap would go below 3,
+// or where the occupancy calculator does not confirm that exact cap (LDS is
+// allocated in granules).  Host code; lookups are cached per device.
+constexpr int kRoundDevices = 64;
+constexpr int kRoundMaxCap = 32;
+
+inline int round_device() {
+  int d = -1;
+  return hipGetDevice(&d) == hipSuccess && d >= 0 && d < kRoundDevices ? d : -1;
+}
+
+// CUs and LDS bytes per CU of device dev (-1 where the runtime gives none)
+inline void round_resources(int dev, int& cus, int& lds) {
+  static std::atomic<int> c_cus[kRoundDevices], c_lds[kRoundDevices];   // 0: not looked up
+  cus = c_cus[dev].load(std::memory_order_acquire);
+  if (cus == 0) {
+    int a = -1, b = -1;
+    if (hipDeviceGetAttribute(&a, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) a = -1;
+    if (hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+        hipSuccess)
+      b = -1;
+    c_lds[dev].store(b > 0 ? b : -1, std::memory_order_relaxed);
+    c_cus[dev].store(a > 0 ? a : -1, std::memory_order_release);
+    cus = a > 0 ? a : -1;
+  }
+  lds = c_lds[dev].load(std::memory_order_relaxed);
+}
+
+template <auto Kernel>
+size_t round_cap_lds(int threads, size_t groups) {
+  const int dev = round_device();
+  if (dev < 0 || groups == 0) return 0;
+  int cus = 0, lds = 0;
+  round_resources(dev, cus, lds);
+  if (cus <= 0 || lds <= 0) return 0;
+  // workgroups per CU the kernel's own resources allow (threads is the same
+  // at every launch of one kernel)
+  static std::atomic<int> c_nat[kRoundDevices];                          // 0: not looked up
+  int nat = c_nat[dev].load(std::memory_order_relaxed);
+  if (nat == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nat, reinterpret_cast<const void*>(Kernel), threads, 0) != hipSuccess || nat <= 0)
+      nat = -1;
+    c_nat[dev].store(nat, std::memory_order_relaxed);
+  }
+  if (nat <= 1) return 0;
+  const size_t per_cu = (groups + cus - 1) / cus;
+  const size_t rounds = (per_cu + nat - 1) / nat;
+  const size_t cap = (per_cu + rounds - 1) / rounds;
+  if (cap >= (size_t)nat || cap < 3 || cap >= (size_t)kRoundMaxCap) return 0;
+  const size_t bytes = (size_t)lds / cap / 1024 * 1024;
+  // whether that many bytes give exactly `cap` workgroups per CU
+  static std::atomic<int> c_ok[kRoundDevices][kRoundMaxCap];             // 0: not checked
+  int ok = c_ok[dev][cap].load(std::memory_order_relaxed);
+  if (ok == 0) {
+    int got = 0;
+    ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+             &got, reinterpret_cast<const void*>(Kernel), threads, bytes) == hipSuccess &&
+                 got == (int)cap
+             ? 1
+             : -1;
+    c_ok[dev][cap].store(ok, std::memory_order_relaxed);
+  }
+  return ok > 0 ? bytes : 0;
 }
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X):
