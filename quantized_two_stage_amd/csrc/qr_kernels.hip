@@ -745,7 +745,7 @@ void s1_launch(const InPtrs& wires, uint8_t* red, size_t blk_lo, size_t blk_hi,
     if (hi <= lo) continue;                       // an owner's empty chunk: no launch
     const InPtrs w = Recv ? at_tile(wires, W, L, t0) : wires;
     const Geo g = geo(L, W, Recv, Recv ? t0 : 0);
-    // each launch in full rounds (round_cap_lds)
+    // at W=8, each launch in full rounds (round_cap_lds)
     if constexpr (C == kFP) {
       // block-granular range in 8-element chunks (a partial last block
       // holds fewer than 4 chunks)
@@ -755,24 +755,24 @@ void s1_launch(const InPtrs& wires, uint8_t* red, size_t blk_lo, size_t blk_hi,
       out.p[0] = red;
       constexpr auto K = k_sum_fp<D, W, kStage1, Recv>;
       const unsigned ng = groups(c_hi - c_lo, kThreads * kPerLane);
-      hipLaunchKernelGGL(K, dim3(ng), dim3(kThreads), round_cap_lds<K>(kThreads, ng), st, w,
-                         out, c_lo, c_hi, g.tstride, g.tile0);
+      hipLaunchKernelGGL(K, dim3(ng), dim3(kThreads), W == 8 ? round_cap_lds<K>(kThreads, ng) : 0,
+                         st, w, out, c_lo, c_hi, g.tstride, g.tile0);
     } else {
       bool launched = false;
       if constexpr (W == 2) {
         if (s1_lanes_per_workgroup(W, L.nb) == 128) {
           constexpr auto K = k_stage1<C, D, W, Recv, 128>;
           const unsigned ng = groups(hi - lo, 128);
-          hipLaunchKernelGGL(K, dim3(ng), dim3(128), round_cap_lds<K>(128, ng), st, w, red,
-                             (uint32_t)lo, (uint32_t)hi, g);
+          hipLaunchKernelGGL(K, dim3(ng), dim3(128), 0, st, w, red, (uint32_t)lo, (uint32_t)hi,
+                             g);
           launched = true;
         }
       }
       if (!launched) {
         constexpr auto K = k_stage1<C, D, W, Recv, kThreads>;
         const unsigned ng = groups(hi - lo, kThreads);
-        hipLaunchKernelGGL(K, dim3(ng), dim3(kThreads), round_cap_lds<K>(kThreads, ng), st, w,
-                           red, (uint32_t)lo, (uint32_t)hi, g);
+        hipLaunchKernelGGL(K, dim3(ng), dim3(kThreads), W == 8 ? round_cap_lds<K>(kThreads, ng) : 0,
+                           st, w, red, (uint32_t)lo, (uint32_t)hi, g);
       }
     }
   }

@@ -71,13 +71,13 @@ size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 template <int C, int W>
 void launch(const InPtrs& in, uint8_t* red, size_t n, hipStream_t st) {
   const size_t nb = (n + 31) / 32;
-  // in full rounds, as stage 1 launches (round_cap_lds)
+  // at W=8 in full rounds, as stage 1 launches (round_cap_lds)
   if constexpr (C == kFP) {
     const uint32_t nc = (uint32_t)(n / 8);
     constexpr auto K = k_sum_pattern<W>;
     const unsigned ng = (nc + kThreads * kPerLane - 1) / (kThreads * kPerLane);
-    hipLaunchKernelGGL(K, dim3(ng), dim3(kThreads), round_cap_lds<K>(kThreads, ng), st, in, red,
-                       nc, (uint32_t)(W * kTileBlocks * 64));
+    hipLaunchKernelGGL(K, dim3(ng), dim3(kThreads), W == 8 ? round_cap_lds<K>(kThreads, ng) : 0,
+                       st, in, red, nc, (uint32_t)(W * kTileBlocks * 64));
   } else {
     using T = CodecT<C>;
     const size_t off_s = a256(nb * T::block_bytes);
@@ -88,13 +88,12 @@ void launch(const InPtrs& in, uint8_t* red, size_t n, hipStream_t st) {
     if (s1_lanes_per_workgroup(W, nb) == 128) {
       constexpr auto K = k_stage1_pattern<C, W, 128>;
       const unsigned ng = (unsigned)((nb + 127) / 128);
-      hipLaunchKernelGGL(K, dim3(ng), dim3(128), round_cap_lds<K>(128, ng), st, in, red,
-                         (uint32_t)nb, g);
+      hipLaunchKernelGGL(K, dim3(ng), dim3(128), 0, st, in, red, (uint32_t)nb, g);
     } else {
       constexpr auto K = k_stage1_pattern<C, W, kThreads>;
       const unsigned ng = (unsigned)((nb + kThreads - 1) / kThreads);
-      hipLaunchKernelGGL(K, dim3(ng), dim3(kThreads), round_cap_lds<K>(kThreads, ng), st, in,
-                         red, (uint32_t)nb, g);
+      hipLaunchKernelGGL(K, dim3(ng), dim3(kThreads), W == 8 ? round_cap_lds<K>(kThreads, ng) : 0,
+                         st, in, red, (uint32_t)nb, g);
     }
   }
 }

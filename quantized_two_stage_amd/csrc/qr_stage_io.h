@@ -39,18 +39,20 @@ inline int s1_lanes_per_workgroup(int W, size_t nb) {
   return W == 2 && nb >= (1u << 20) ? 128 : kThreads;
 }
 
-// Full rounds.  A stage-1 grid gives each CU few workgroups (16 at W=8 and
-// 64 MB per rank), and when the kernel's occupancy does not divide that
-// number the last round runs nearly empty: 16 workgroups at 5 per CU run as
-// 5 + 5 + 5 + 1, the last with no other wave to hide its loads behind, where
-// 4 per CU run as four full rounds (Q4A 3.6% and Q6A 1.8% faster at W=8,
-// 64 MB per rank, whose registers allow 5; no change for the codecs whose
-// registers allow 3 or 4).  round_cap_lds<Kernel> gives the dynamic LDS,
-// which the kernels leave unused, that caps a launch of `groups` workgroups
-// at the fewest workgroups per CU that keep its number of rounds; 0 where
-// the kernel's own occupancy already does, where the cap would go below 3,
-// or where the occupancy calculator does not confirm that exact cap (LDS is
-// allocated in granules).  Host code; lookups are cached per device.
+// Full rounds.  A stage-1 grid gives each CU few workgroups (16 at 64 MB per
+// rank), and when the kernel's occupancy does not divide that number the
+// last round runs part-empty: 16 workgroups at 5 per CU run as 5 + 5 + 5 + 1.
+// round_cap_lds<Kernel> gives the dynamic LDS, which the kernels leave
+// unused, that caps a launch of `groups` workgroups at the fewest workgroups
+// per CU that keep its number of rounds (here 4 per CU: four full rounds);
+// 0 where the kernel's own occupancy already does, where the cap would go
+// below 3, or where the occupancy calculator does not confirm that exact cap
+// (LDS is allocated in granules).  Host code; lookups are cached per device.
+// Measured cold, alternating with uncapped launches: at W=8 and 64 MB per
+// rank Q4A 2.5-4.1% faster, Q6A between 0.4% slower and 1.8% faster (the
+// other codecs' registers allow 3 or 4 per CU: no cap); at W=4 the same caps
+// made Q4A and Q6A 0.5-1.7% slower at 16-64 MB per rank.  So stage 1 takes
+// it at W=8 only: the launch whose arithmetic is heaviest against its bytes.
 constexpr int kRoundDevices = 64;
 constexpr int kRoundMaxCap = 32;
 
