@@ -26,7 +26,9 @@ duration; `frac` is the lowest over the eight codecs, each codec's figure and
 its access-pattern ceiling beside it.  `cpu_baseline` times the CPU oracle on
 a bounded sample of the same workload.  The one JSON line on stdout carries
 the contract fields and compact per-codec figures; --extra PATH writes the
-other workloads, the size sweeps and the minimum-size table to a file.
+other workloads, the size sweeps and the minimum-size table to a file, and
+--stage1-scan PATH stage 1 at 8 to 256 MB per rank beside its access pattern
+and a copy of the same bytes.
 """
 import argparse
 import hashlib
@@ -64,6 +66,9 @@ def parse():
                    help="also measure the other workloads, the size sweeps and the "
                         "minimum-size table, written as JSON to PATH")
     p.add_argument("--sweep-repeats", type=int, default=3)
+    p.add_argument("--stage1-scan", metavar="PATH",
+                   help="also time stage 1 cold at 8-256 MB per rank (W=8) beside its "
+                        "access pattern and a copy of the same bytes, written as JSON to PATH")
     return p.parse_args()
 
 
@@ -607,6 +612,57 @@ def launch_floor(torch, stream, iters=100, repeats=3):
     return {"us": float(np.median(meds)), "spread": float(max(meds) - min(meds))}
 
 
+SCAN_SIZES = tuple(2 ** k for k in range(22, 28))        # elements: 8 .. 256 MB per rank
+
+
+def measure_stage1_scan(qr, I, torch, stream, log, sizes=SCAN_SIZES, reps=11):
+    """Stage 1 of the W=8 fp16 workload (same generator, a smaller size being
+    the leading part of the largest) at 8 to 256 MB per rank, cold, each
+    codec's launch in turn with its access pattern and a plain copy of the
+    same bytes: whether a larger launch streams faster than the 64 MB one.
+    Per codec and kernel: us and fraction of 8 TB/s at every size, and the
+    plateau, the median fraction over the sizes from 64 MB per rank up."""
+    cfg = I.CONFIGS[5]
+    W, dtype, nmax = cfg["W"], cfg["dtype"], max(sizes)
+    log("bench: stage-1 size scan, generating %d MB per rank" % (2 * nmax >> 20))
+    xs_all = [torch.from_numpy(x.view(np.int16)).to("cuda") for x in I.make(5, n=nmax)]
+    cl, pat = Cold(torch, stream, reps), Pattern()
+    out = {"workload": cfg["desc"], "W": W, "sizes_bytes_per_rank": [2 * n for n in sizes],
+           "reps": reps, "plateau_from_bytes_per_rank": 64 << 20, "per_codec": {}}
+    for c in cfg["codecs"]:
+        pts = {"stage1": [], "pattern": [], "copy": []}
+        abs_ = []
+        for n in sizes:
+            xs = [x[:n] for x in xs_all]
+            recv, red, red2 = qr.alloc_recv(W, c, n), qr.alloc_wire(c, n), qr.alloc_wire(c, n)
+            qr.qr_quantize_recv(c, xs, recv, dtype=dtype)
+            ab = algorithmic_bytes("stage1", W, n, qr.qr_wire_bytes(c, n))
+            copy, keep = cl.copy_fn(ab)
+            t = cl.us_interleaved({
+                "stage1": lambda: qr.qr_reduce_recv(c, W, recv, n, red, dtype),
+                "pattern": lambda: pat.stage1(c, W, recv, n, red2, stream),
+                "copy": copy})
+            for k in pts:
+                pts[k].append(t[k])
+            abs_.append(ab)
+            del recv, red, red2, keep, copy
+        r = {"bytes": abs_}
+        big = [i for i, n in enumerate(sizes) if 2 * n >= out["plateau_from_bytes_per_rank"]]
+        for k, ts in pts.items():
+            fr = [frac(x, y) for x, y in zip(abs_, ts)]
+            r[k] = {"us": [round(y, 2) for y in ts], "frac": [round(f, 4) for f in fr],
+                    "plateau_frac": round(float(np.median([fr[i] for i in big])), 4)}
+        r["stage1_vs_pattern"] = [round(p / s, 4) for p, s in zip(pts["pattern"], pts["stage1"])]
+        out["per_codec"][I.CODEC_NAMES[c]] = r
+        log("  %-4s plateau: stage 1 %.3f, pattern %.3f, copy %.3f" % (
+            I.CODEC_NAMES[c], r["stage1"]["plateau_frac"], r["pattern"]["plateau_frac"],
+            r["copy"]["plateau_frac"]))
+    cl.close()
+    del xs_all
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_extra(args, qr, I, torch, stream, log):
     extra = {}
     log("bench: launch floor (an empty kernel, timed as the sweeps are)")
@@ -705,6 +761,12 @@ def main():
         with open(args.extra, "w") as f:
             json.dump(extra, f, indent=1)
         log("bench: other workloads written to %s" % args.extra)
+
+    if args.stage1_scan:
+        scan = measure_stage1_scan(qr, I, torch, stream, log)
+        with open(args.stage1_scan, "w") as f:
+            json.dump(scan, f, indent=1)
+        log("bench: stage-1 size scan written to %s" % args.stage1_scan)
 
     for name, e in stages.items():
         log("  %-4s %8.1f us/allreduce  stage0 %.3f  stage1 %.3f (cold %s, pattern %s, "

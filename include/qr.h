@@ -127,10 +127,15 @@ size_t qr_wire_bytes(qr_codec codec, size_t n);
  * holds the 256 blocks' codes (256 * 32*b/8 bytes), then their binary16
  * scales (512 bytes), then (asymmetric codecs) their binary16 zeros (512
  * bytes), so T = 256 * (32*b/8 + 2 [+ 2]); FP: the 256 blocks' raw 16-bit
- * data, T = 16384.  Slots of blocks past the last one are padding, never
- * read or written.  The W tiles of one range of blocks are thus adjacent:
- * stage 1 reads them as one stream instead of W (on a real node the senders
- * would write their tiles into the owner's buffer at these offsets).
+ * data, T = 16384.  The codes are word-major: each block's 32*b/8 code
+ * bytes (the planar image's, in order) are cut into words of S bytes (S = 8
+ * for 6-bit codes, else 16), and the tile holds word 0 of its 256 blocks,
+ * then word 1 of them, and so on (4-bit blocks are one word).  Slots of
+ * blocks past the last one are padding, never read or written.  The W tiles
+ * of one range of blocks are thus adjacent: stage 1 reads them as one
+ * stream instead of W, and each of its load instructions reads one
+ * contiguous range (on a real node the senders would write their tiles into
+ * the owner's buffer at these offsets).
  * Bytes of the buffer: ceil(ceil(n/32)/256) * W * T (0 for an unknown codec
  * or W outside 1..8). */
 size_t qr_recv_bytes(int W, qr_codec codec, size_t n);

@@ -203,6 +203,7 @@ __device__ __forceinline__ uint32_t quad_perm_u(uint32_t v) {
 constexpr int kSwap1 = 0xb1;    // quad_perm [1,0,3,2]
 constexpr int kSwap2 = 0x4e;    // quad_perm [2,3,0,1]
 constexpr int kFromOdd = 0xf5;  // quad_perm [1,1,3,3]
+constexpr int kFromNext = 0xf9; // quad_perm [1,2,3,3]
 
 // ---------------------------------------------------------------------------
 // code packing: code i at bits [b*i, b*i+b) of a little-endian bitstring

@@ -77,6 +77,27 @@ struct QuarterIO {
       w[1] = c >> sh;
     }
   }
+  // the same quarter of block blk from a rank's tiles of the receive buffer
+  // (base: the rank's tile g.tile0; word-major codes)
+  __device__ static void load_recv(const uint8_t* base, const Geo& g, uint32_t blk, int j,
+                                   uint32_t (&w)[nw]) {
+    using A = At<C, true>;
+    if constexpr (b == 4) {
+      w[0] = *reinterpret_cast<const uint32_t*>(base + A::code_at(g, blk, 4 * j));
+    } else if constexpr (b == 8) {
+      const u32x2 q = *reinterpret_cast<const u32x2*>(base + A::code_at(g, blk, 8 * j));
+      w[0] = q.x;
+      w[1] = q.y;
+    } else {
+      const uint32_t i0 = (3 * j) >> 1;              // its first 32-bit word of the block
+      const uint32_t a = *reinterpret_cast<const uint32_t*>(base + A::code_at(g, blk, 4 * i0));
+      const uint32_t c =
+          *reinterpret_cast<const uint32_t*>(base + A::code_at(g, blk, 4 * i0 + 4));
+      const int sh = (j & 1) * 16;
+      w[0] = __builtin_amdgcn_alignbit(c, a, sh);
+      w[1] = c >> sh;
+    }
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -202,8 +223,21 @@ __device__ __forceinline__ void quantize_core(float (&v)[U][8], uint8_t* const (
     const bool keep = (Full || 8 * q[u] < g.n) && (!T::fp8 || (fl[u] & 2u) != 0u);
 #pragma unroll
     for (int k = 0; k < nw; k++) w[k] = keep ? w[k] : 0u;
-    uint8_t* cb = wire[u] + At<C, Recv>::code(g, q[u] >> 2);
-    if constexpr (T::bits == 6) {
+    const uint32_t blk = q[u] >> 2;
+    if constexpr (T::bits == 6 && Recv) {
+      // word-major 8-byte words: lanes 0, 1, 2 of the quad each write word j,
+      // bits [64j, 64j+64) of the block's bitstring: the top of their own 48
+      // bits (from bit 16j) and the bottom of the next lane's
+      const uint32_t n0 = quad_perm_u<kFromNext>(w[0]);
+      const uint32_t n1 = quad_perm_u<kFromNext>(w[1]);
+      const uint64_t a = ((uint64_t)(w[1] & 0xffffu) << 32) | w[0];
+      const uint64_t b = ((uint64_t)(n1 & 0xffffu) << 32) | n0;
+      const uint64_t word = (a >> (16 * j)) | (b << (48 - 16 * j));
+      if ((Full || q[u] < q_end) && j < 3)
+        st_out<Stage>(reinterpret_cast<u32x2*>(wire[u] + At<C, true>::code_at(g, blk, 8 * j)),
+                      u32x2{(uint32_t)word, (uint32_t)(word >> 32)});
+    } else if constexpr (T::bits == 6) {
+      uint8_t* cb = wire[u] + At<C, false>::code_at(g, blk, 0);
       // lanes 0 and 2 of the quad each write 96 bits (their own 48 and their
       // odd neighbour's 48)
       const uint32_t o0 = quad_perm_u<kFromOdd>(w[0]);
@@ -215,10 +249,12 @@ __device__ __forceinline__ void quantize_core(float (&v)[U][8], uint8_t* const (
         st_out<Stage>(d + 2, (o0 >> 16) | (o1 << 16));
       }
     } else if (Full || q[u] < q_end) {
+      // quarter j: bytes [4j, 4j+4) or [8j, 8j+8) of the block's codes
+      uint8_t* d = wire[u] + At<C, Recv>::code_at(g, blk, T::bits * j);
       if constexpr (T::bits == 4)
-        st_out<Stage>(reinterpret_cast<uint32_t*>(cb) + j, w[0]);
+        st_out<Stage>(reinterpret_cast<uint32_t*>(d), w[0]);
       else
-        st_out<Stage>(reinterpret_cast<u32x2*>(cb) + j, u32x2{w[0], w[1]});
+        st_out<Stage>(reinterpret_cast<u32x2*>(d), u32x2{w[0], w[1]});
     }
   }
 }
@@ -464,7 +500,8 @@ __global__ __launch_bounds__(kThreads) void k_sum_fp(InPtrs xs, OutPtrs outs,
     const uint32_t off = fp_chunk<Recv>(tstride, tile0, c < c_hi ? c : c_lo);
 #pragma unroll
     for (int r = 0; r < W; r++)
-      q[j][r] = ld_in<kStage1>(reinterpret_cast<const u32x4*>(xs.p[r] + off));
+      q[j][r] = ld_in<Stage == kStage1 ? kStage1 : kKeep>(
+          reinterpret_cast<const u32x4*>(xs.p[r] + off));
   }
   u32x4* out_p = reinterpret_cast<u32x4*>(outs.p[blockIdx.y]);
 #pragma unroll
@@ -599,11 +636,10 @@ __device__ __forceinline__ void fused_tile(const InPtrs& xs, const OutPtrs& wire
     const uint32_t blk = ql >> 2;
     uint32_t w[W][IO::nw];
     float sc[W], zc[W];
-    const uint32_t co = At<C, true>::code(g, blk);
     const uint32_t so = At<C, true>::scale(g, blk), zo = At<C, true>::zero(g, blk);
 #pragma unroll
     for (int r = 0; r < W; r++) {
-      IO::load(wires.p[r] + co, ql & 3, w[r]);
+      IO::load_recv(wires.p[r], g, blk, ql & 3, w[r]);
       sc[r] = h2f(ld_u16(wires.p[r] + so)) * T::unpack_scale;
       zc[r] = T::asym ? h2f(ld_u16(wires.p[r] + zo)) : 0.0f;
     }

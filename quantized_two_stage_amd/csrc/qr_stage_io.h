@@ -125,12 +125,23 @@ size_t round_cap_lds(int threads, size_t groups) {
 //             for their write-back; stage 1's reduced image is kept cached
 //             because stage 2 reads it W times.
 // QR_NT_LOAD  bit mask of the stages whose read-once inputs are loaded with
-//             non-temporal loads (default none: no gain measured).
+//             non-temporal loads.  Default 3: the inputs of stage 0 and the
+//             wire data of stage 1, wherever each load instruction of a wave
+//             reads one contiguous range (Stream below).  Cold at W=8, 64 MB
+//             per rank, against cached loads: stage 1 of Q4A 11% faster, Q4
+//             9%, FP 7%, and the whole step 3% faster from stage 0's.  Where
+//             two instructions read halves of the same lines (32-byte code
+//             blocks read as two 16-byte words per lane), non-temporal loads
+//             made stage 1 about 10% slower, so those stay cached: the
+//             receive buffer stores such codes word-major (WireAt) so that
+//             stage 1 can stream them, and the planar wire images keep cached
+//             loads for them.  Stage 2 and the one-stage allreduce re-read
+//             their inputs and always load through the caches.
 #ifndef QR_NT_STORE
 #define QR_NT_STORE 5
 #endif
 #ifndef QR_NT_LOAD
-#define QR_NT_LOAD 0
+#define QR_NT_LOAD 3
 #endif
 constexpr int kStage0 = 1, kStage1 = 2, kStage2 = 4;
 constexpr int kKeep = 0;           // store policy: always through the caches
@@ -142,9 +153,11 @@ __device__ __forceinline__ void st_out(V* p, V v) {
   else
     *p = v;
 }
-template <int Stage, typename V>
+// Stream: every load instruction of a wave at this site reads one contiguous
+// range, so no line is fetched by two instructions
+template <int Stage, bool Stream = true, typename V>
 __device__ __forceinline__ V ld_in(const V* p) {
-  if constexpr ((QR_NT_LOAD & Stage) != 0)
+  if constexpr ((QR_NT_LOAD & Stage) != 0 && Stream)
     return __builtin_nontemporal_load(p);
   else
     return *p;
@@ -167,17 +180,24 @@ struct Geo {
 // Recv == true: the rank's tiles in the receive buffer, the base being its
 // tile tile0; tile t = blk / kTileBlocks starts (t - tile0) * tstride further
 // and holds kTileBlocks blocks' codes, then their scales, then their zeros
-// (the host launches tile ranges whose offsets stay below 4 GiB).  FP (raw
-// data) uses code() alone, with CB = 64.
+// (the host launches tile ranges whose offsets stay below 4 GiB).  A tile's
+// codes are stored word-major: the blocks' code bytes are cut into words of
+// kWord bytes (16; 8 for 24-byte blocks) and word k of all kTileBlocks
+// blocks is contiguous, so that a wave whose lanes take consecutive blocks
+// reads one contiguous range with each load instruction (16-byte blocks are
+// one word: their layout is the planar one's).
 template <int CB, bool Recv>
 struct WireAt {
   static constexpr uint32_t kTB = kTileBlocks;
+  static constexpr uint32_t kWord = CB == 24 ? 8 : 16;
   __device__ static __forceinline__ uint32_t tile(const Geo& g, uint32_t blk) {
     return (blk / kTB - g.tile0) * g.tstride;
   }
-  __device__ static __forceinline__ uint32_t code(const Geo& g, uint32_t blk) {
-    if constexpr (Recv) return tile(g, blk) + (blk % kTB) * (uint32_t)CB;
-    return blk * (uint32_t)CB;
+  // byte o (< CB) of block blk's codes
+  __device__ static __forceinline__ uint32_t code_at(const Geo& g, uint32_t blk, uint32_t o) {
+    if constexpr (Recv)
+      return tile(g, blk) + (o / kWord) * (kTB * kWord) + (blk % kTB) * kWord + o % kWord;
+    return blk * (uint32_t)CB + o;
   }
   __device__ static __forceinline__ uint32_t scale(const Geo& g, uint32_t blk) {
     if constexpr (Recv) return tile(g, blk) + kTB * CB + (blk % kTB) * 2u;
@@ -223,22 +243,25 @@ template <int C, int W, bool Recv>
 __device__ __forceinline__ void s1_load(const InPtrs& wires, uint32_t blk, const Geo& g,
                                         S1In<C, W>& in) {
   using T = CodecT<C>;
-  const uint32_t co = At<C, Recv>::code(g, blk);
+  // word k of every lane's block: one contiguous range per wave in the
+  // receive buffer (word-major) and for 16-byte blocks (one word)
+  constexpr bool kStream = Recv || T::block_bytes == 16;
   const uint32_t so = At<C, Recv>::scale(g, blk), zo = At<C, Recv>::zero(g, blk);
 #pragma unroll
   for (int r = 0; r < W; r++) {
-    const uint8_t* cb = wires.p[r] + co;
     if constexpr (T::words == 6) {
 #pragma unroll
       for (int k = 0; k < 3; k++) {
-        const u32x2 q = ld_in<kStage1>(reinterpret_cast<const u32x2*>(cb) + k);
+        const u32x2 q = ld_in<kStage1, kStream>(
+            reinterpret_cast<const u32x2*>(wires.p[r] + At<C, Recv>::code_at(g, blk, 8 * k)));
         in.cw[r][2 * k] = q.x;
         in.cw[r][2 * k + 1] = q.y;
       }
     } else {
 #pragma unroll
       for (int k = 0; k < T::words / 4; k++) {
-        const u32x4 q = ld_in<kStage1>(reinterpret_cast<const u32x4*>(cb) + k);
+        const u32x4 q = ld_in<kStage1, kStream>(
+            reinterpret_cast<const u32x4*>(wires.p[r] + At<C, Recv>::code_at(g, blk, 16 * k)));
         in.cw[r][4 * k] = q.x; in.cw[r][4 * k + 1] = q.y;
         in.cw[r][4 * k + 2] = q.z; in.cw[r][4 * k + 3] = q.w;
       }
@@ -261,7 +284,7 @@ __device__ __forceinline__ void s1_store(uint8_t* red, uint32_t blk, const Geo& 
                                          const uint32_t (&w)[CodecT<C>::words], uint32_t s,
                                          uint32_t z) {
   using T = CodecT<C>;
-  uint8_t* cb = red + At<C, false>::code(g, blk);
+  uint8_t* cb = red + At<C, false>::code_at(g, blk, 0);
   const uint32_t so = At<C, false>::scale(g, blk), zo = At<C, false>::zero(g, blk);
   if constexpr (T::words == 6) {
 #pragma unroll

@@ -152,43 +152,64 @@ def recv_tile_bytes(codec):
     return 256 * (O.block_code_bytes(codec) + 2 + (2 if codec & 8 else 0))
 
 
-def recv_regions(codec, n, W):
-    """(offset in the receive buffer, rank, start, end in the rank's planar
-    wire image) of every defined byte range, from the layout's definition:
-    tile t of rank r starts at (t*W + r) * T and holds blocks [256t, 256t+256)
-    of that rank: their codes, then their scales, then their zeros"""
+def recv_word_bytes(codec):
+    """a tile's codes sit in the receive buffer word-major, in words of this
+    many bytes: word k of the tile's 256 blocks is contiguous"""
+    return 8 if O.block_code_bytes(codec) == 24 else 16
+
+
+def _rank_tiles(codec, n, wire):
+    """one rank's tiles of the receive buffer from its planar wire image, as
+    (tiles, defined) arrays of shape (tile count, tile bytes), from the
+    layout's definition: a tile holds blocks [256t, 256t+256): their codes,
+    word-major (word k, bytes [kS, kS+S) of each block's codes, of all 256
+    blocks one after the other, then word k+1), then their binary16 scales,
+    then their binary16 zeros; FP: the blocks' raw data.  Slots of blocks
+    past the last one are undefined."""
     nb = (n + 31) // 32
+    nt = (nb + 255) // 256
     T = recv_tile_bytes(codec)
-    out = []
-    for t in range((nb + 255) // 256):
-        b0, b1 = 256 * t, min(nb, 256 * t + 256)
-        for r in range(W):
-            base = (t * W + r) * T
-            if codec == O.FP:
-                out.append((base, r, 64 * b0, min(2 * n, 64 * b1)))
-                continue
-            cb = O.block_code_bytes(codec)
-            out.append((base, r, cb * b0, cb * b1))
-            so = O.scale_offset(codec, n)
-            out.append((base + 256 * cb, r, so + 2 * b0, so + 2 * b1))
-            if codec & 8:
-                zo = O.zero_offset(codec, n)
-                out.append((base + 256 * (cb + 2), r, zo + 2 * b0, zo + 2 * b1))
-    return out
+
+    def padded(src, size):
+        v, d = np.zeros(size, np.uint8), np.zeros(size, bool)
+        v[:src.size], d[:src.size] = src, True
+        return v, d
+
+    if codec == O.FP:
+        v, d = padded(np.asarray(wire[:2 * n]), nt * T)
+        return v.reshape(nt, T), d.reshape(nt, T)
+    cb, S = O.block_code_bytes(codec), recv_word_bytes(codec)
+    parts = []
+    v, d = padded(np.asarray(wire[:nb * cb]), nt * 256 * cb)
+    parts.append(tuple(x.reshape(nt, 256, cb // S, S).transpose(0, 2, 1, 3).reshape(nt, 256 * cb)
+                       for x in (v, d)))
+    planes = [O.scale_offset(codec, n)] + ([O.zero_offset(codec, n)] if codec & 8 else [])
+    for off in planes:
+        v, d = padded(np.asarray(wire[off:off + 2 * nb]), nt * 512)
+        parts.append((v.reshape(nt, 512), d.reshape(nt, 512)))
+    return (np.concatenate([p[0] for p in parts], axis=1),
+            np.concatenate([p[1] for p in parts], axis=1))
 
 
 def recv_from_wires(codec, n, wires, fill=0):
     """the receive buffer holding W planar wire images (numpy), with the
-    mask of its defined bytes; padding bytes hold `fill`"""
+    mask of its defined bytes; padding bytes hold `fill`.  Tile t of rank r
+    starts at byte (t*W + r) * T."""
     W = len(wires)
-    nb = (n + 31) // 32
-    size = ((nb + 255) // 256) * W * recv_tile_bytes(codec)
-    buf = np.full(size, fill, np.uint8)
-    mask = np.zeros(size, bool)
-    for dst, r, a, e in recv_regions(codec, n, W):
-        buf[dst:dst + e - a] = wires[r][a:e]
-        mask[dst:dst + e - a] = True
-    return buf, mask
+    tiles = [_rank_tiles(codec, n, w) for w in wires]
+    nt, T = tiles[0][0].shape
+    buf = np.full((nt, W, T), fill, np.uint8)
+    mask = np.zeros((nt, W, T), bool)
+    for r, (v, d) in enumerate(tiles):
+        buf[:, r] = np.where(d, v, np.uint8(fill))
+        mask[:, r] = d
+    return buf.ravel(), mask.ravel()
+
+
+def recv_mask(codec, n, W):
+    """the defined bytes of a receive buffer of W ranks"""
+    wb = O.wire_bytes(codec, n)
+    return recv_from_wires(codec, n, [np.zeros(wb, np.uint8)] * W)[1]
 
 
 def assert_recv_equal(got, wires, codec, n, what, fill=None):

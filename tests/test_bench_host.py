@@ -86,3 +86,4 @@ def test_stage2_hbm_bytes_read_the_reduced_image_once():
     n, wb = 1 << 25, 18874368
     assert bench.hbm_bytes_stage2(8, n, wb) == wb + 8 * 2 * n
     assert bench.hbm_bytes_stage2(8, n, wb) < bench.algorithmic_bytes("stage2", 8, n, wb)
+
