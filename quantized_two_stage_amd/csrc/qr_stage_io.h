@@ -119,11 +119,14 @@ size_t round_cap_lds(int threads, size_t groups) {
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X):
 // QR_NT_STORE bit mask of the stages (1 = stage 0, 2 = stage 1, 4 = stage 2)
 //             whose streamed outputs are written with non-temporal stores.
-//             Default 5: the wire images of stage 0 (read once, by another
-//             rank) and the outputs of stage 2 (the result).  Lines written
-//             through the caches stay dirty there and the next kernel pays
-//             for their write-back; stage 1's reduced image is kept cached
-//             because stage 2 reads it W times.
+//             Default 4: the outputs of stage 2 (the result; through the
+//             caches those lines stay dirty and the next kernel pays for
+//             their write-back: the W=8 step was 12-14% slower).  Stage 1's
+//             reduced image stays cached because stage 2 reads it W times,
+//             and so do stage 0's wire data, which stage 1 reads next (with
+//             stage 0's loads non-temporal, cached stores made the W=8 step
+//             1.5% faster: FP 5%, Q4 3%, the asymmetric 8- and 4-bit codes 1%
+//             slower).
 // QR_NT_LOAD  bit mask of the stages whose read-once inputs are loaded with
 //             non-temporal loads.  Default 3: the inputs of stage 0 and the
 //             wire data of stage 1, wherever each load instruction of a wave
@@ -138,7 +141,7 @@ size_t round_cap_lds(int threads, size_t groups) {
 //             loads for them.  Stage 2 and the one-stage allreduce re-read
 //             their inputs and always load through the caches.
 #ifndef QR_NT_STORE
-#define QR_NT_STORE 5
+#define QR_NT_STORE 4
 #endif
 #ifndef QR_NT_LOAD
 #define QR_NT_LOAD 3
