@@ -500,7 +500,7 @@ __global__ __launch_bounds__(kThreads) void k_sum_fp(InPtrs xs, OutPtrs outs,
     const uint32_t off = fp_chunk<Recv>(tstride, tile0, c < c_hi ? c : c_lo);
 #pragma unroll
     for (int r = 0; r < W; r++)
-      q[j][r] = ld_in<Stage == kStage1 ? kStage1 : kKeep>(
+      q[j][r] = ld_in<Stage == kStage1 ? kS1Load<W> : kKeep>(
           reinterpret_cast<const u32x4*>(xs.p[r] + off));
   }
   u32x4* out_p = reinterpret_cast<u32x4*>(outs.p[blockIdx.y]);

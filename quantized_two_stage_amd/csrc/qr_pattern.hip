@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void k_sum_pattern(InPtrs xs, uint8_t* re
     const uint32_t off = fp_chunk<true>(tstride, 0u, c < nchunks ? c : 0u);
 #pragma unroll
     for (int r = 0; r < W; r++)
-      q[j][r] = ld_in<kStage1>(reinterpret_cast<const u32x4*>(xs.p[r] + off));
+      q[j][r] = ld_in<kS1Load<W>>(reinterpret_cast<const u32x4*>(xs.p[r] + off));
   }
 #pragma unroll
   for (int j = 0; j < kPerLane; j++) {

@@ -129,13 +129,19 @@ size_t round_cap_lds(int threads, size_t groups) {
 //             slower).
 // QR_NT_LOAD  bit mask of the stages whose read-once inputs are loaded with
 //             non-temporal loads.  Default 3: the inputs of stage 0 and the
-//             wire data of stage 1, wherever each load instruction of a wave
-//             reads one contiguous range (Stream below).  Cold at W=8, 64 MB
-//             per rank, against cached loads: stage 1 of Q4A 11% faster, Q4
-//             9%, FP 7%, and the whole step 3% faster from stage 0's.  Where
-//             two instructions read halves of the same lines (32-byte code
-//             blocks read as two 16-byte words per lane), non-temporal loads
-//             made stage 1 about 10% slower, so those stay cached: the
+//             wire data of stage 1 from W = 4 up (kS1Stream), wherever each
+//             load instruction of a wave reads one contiguous range (Stream
+//             below).  Cold at W=8, 64 MB per rank, against cached loads:
+//             stage 1 of Q4A 11% faster, Q4 9%, FP 7%; the stage-1 reads then
+//             also leave the reduced image in the Infinity Cache for stage
+//             2's W reads (with cached stage-1 loads the W=8 FP allreduce took
+//             444 us instead of 395, the 8-bit codes 6-11% longer); and the
+//             whole step 3% faster from stage 0's.  At W = 4 stage 1 is 3-5%
+//             faster cold.  At W = 2 cached loads are better (cold stage 1
+//             3-6% faster, the allreduce 0.5%), so stage 1 keeps them there.
+//             Where two instructions read halves of the same lines (32-byte
+//             code blocks read as two 16-byte words per lane), non-temporal
+//             loads made stage 1 about 10% slower, so those stay cached: the
 //             receive buffer stores such codes word-major (WireAt) so that
 //             stage 1 can stream them, and the planar wire images keep cached
 //             loads for them.  Stage 2 and the one-stage allreduce re-read
@@ -148,6 +154,9 @@ size_t round_cap_lds(int threads, size_t groups) {
 #endif
 constexpr int kStage0 = 1, kStage1 = 2, kStage2 = 4;
 constexpr int kKeep = 0;           // store policy: always through the caches
+// stage 1's wire-data loads stream (non-temporal, QR_NT_LOAD) from W = 4 up
+template <int W>
+constexpr int kS1Load = W >= 4 ? kStage1 : kKeep;
 
 template <int Stage, typename V>
 __device__ __forceinline__ void st_out(V* p, V v) {
@@ -157,7 +166,7 @@ __device__ __forceinline__ void st_out(V* p, V v) {
     *p = v;
 }
 // Stream: every load instruction of a wave at this site reads one contiguous
-// range, so no line is fetched by two instructions
+// range, so no line is fetched by two instructions.  Stage kKeep: cached.
 template <int Stage, bool Stream = true, typename V>
 __device__ __forceinline__ V ld_in(const V* p) {
   if constexpr ((QR_NT_LOAD & Stage) != 0 && Stream)
@@ -255,7 +264,7 @@ __device__ __forceinline__ void s1_load(const InPtrs& wires, uint32_t blk, const
     if constexpr (T::words == 6) {
 #pragma unroll
       for (int k = 0; k < 3; k++) {
-        const u32x2 q = ld_in<kStage1, kStream>(
+        const u32x2 q = ld_in<kS1Load<W>, kStream>(
             reinterpret_cast<const u32x2*>(wires.p[r] + At<C, Recv>::code_at(g, blk, 8 * k)));
         in.cw[r][2 * k] = q.x;
         in.cw[r][2 * k + 1] = q.y;
@@ -263,7 +272,7 @@ __device__ __forceinline__ void s1_load(const InPtrs& wires, uint32_t blk, const
     } else {
 #pragma unroll
       for (int k = 0; k < T::words / 4; k++) {
-        const u32x4 q = ld_in<kStage1, kStream>(
+        const u32x4 q = ld_in<kS1Load<W>, kStream>(
             reinterpret_cast<const u32x4*>(wires.p[r] + At<C, Recv>::code_at(g, blk, 16 * k)));
         in.cw[r][4 * k] = q.x; in.cw[r][4 * k + 1] = q.y;
         in.cw[r][4 * k + 2] = q.z; in.cw[r][4 * k + 3] = q.w;
