@@ -28,7 +28,8 @@ a bounded sample of the same workload.  The one JSON line on stdout carries
 the contract fields and compact per-codec figures; --extra PATH writes the
 other workloads, the size sweeps and the minimum-size table to a file, and
 --stage1-scan PATH stage 1 at 8 to 256 MB per rank beside its access pattern
-and a copy of the same bytes.
+and a copy of the same bytes, and --stream-probes PATH plain reads, writes and
+copies of the memory system.
 """
 import argparse
 import hashlib
@@ -66,6 +67,10 @@ def parse():
                    help="also measure the other workloads, the size sweeps and the "
                         "minimum-size table, written as JSON to PATH")
     p.add_argument("--sweep-repeats", type=int, default=3)
+    p.add_argument("--stream-probes", metavar="PATH",
+                   help="also time plain reads, writes and copies (one or four 16-byte "
+                        "accesses per lane, cached or non-temporal) cold at 192 MiB-1.1 GiB, "
+                        "written as JSON to PATH")
     p.add_argument("--stage1-scan", metavar="PATH",
                    help="also time stage 1 cold at 8-256 MB per rank (W=8) beside its "
                         "access pattern and a copy of the same bytes, written as JSON to PATH")
@@ -160,6 +165,19 @@ class Pattern:
         self.L.qrp_stage1_pattern.argtypes = [i32, i32, P, sz, P, P]
         self.L.qrp_stage1_pattern.restype = i32
         self.ct = ctypes
+
+    def stream(self, kind, per_lane, nt, src, dst, nbytes, stream):
+        L = self.L
+        if not hasattr(L, "_stream_sig"):
+            P, i32, sz = self.ct.c_void_p, self.ct.c_int, self.ct.c_size_t
+            L.qrp_stream.argtypes = [i32, i32, i32, P, P, sz, P]
+            L.qrp_stream.restype = i32
+            L._stream_sig = True
+        rc = L.qrp_stream(kind, per_lane, nt, self.ct.c_void_p(src.data_ptr()),
+                          self.ct.c_void_p(dst.data_ptr()), nbytes,
+                          self.ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("qrp_stream failed (%d)" % rc)
 
     def stage1(self, codec, W, recv, n, red, stream):
         rc = self.L.qrp_stage1_pattern(codec, W, self.ct.c_void_p(recv.data_ptr()), n,
@@ -562,7 +580,7 @@ def measure_sweep(qr, I, torch, stream, repeats, Ws=(2, 4, 8), sizes=SWEEP_SIZES
     return res
 
 
-MIN_SIZE_MARGIN = 0.20
+MIN_SIZE_MARGIN = 0.30
 
 
 def min_sizes(sweep, margin=MIN_SIZE_MARGIN):
@@ -659,6 +677,37 @@ def measure_stage1_scan(qr, I, torch, stream, log, sizes=SCAN_SIZES, reps=11):
             r["copy"]["plateau_frac"]))
     cl.close()
     del xs_all
+    torch.cuda.empty_cache()
+    return out
+
+
+STREAM_PROBES = (("read", 0, 1, 0), ("read", 0, 4, 0), ("read, non-temporal", 0, 4, 1),
+                 ("write", 1, 1, 0), ("write", 1, 4, 0), ("write, non-temporal", 1, 1, 1),
+                 ("write, non-temporal", 1, 4, 1), ("copy", 2, 1, 0), ("copy", 2, 4, 0),
+                 ("copy, non-temporal loads", 2, 4, 1))
+
+
+def measure_streams(torch, stream, log, sizes_mib=(192, 576, 1152), reps=11):
+    """Plain reads, writes and copies of 16-byte accesses (libqr_pattern.so's
+    qrp_stream), cold, taken in turn launch by launch: the memory system's
+    own rates for one or four accesses per lane, through the caches or not.
+    A write's cold time ends with the launch, so the last lines it wrote may
+    still sit dirty in the Infinity Cache (up to 256 MB) and are not in it."""
+    pat, cl = Pattern(), Cold(torch, stream, reps)
+    out = {"reps": reps, "per_size": {}}
+    for mib in sizes_mib:
+        nbytes = mib << 20
+        a = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        b = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        fns = {"%s, %d per lane" % (name, k): (lambda kind=kind, k=k, nt=nt:
+                                               pat.stream(kind, k, nt, a, b, nbytes, stream))
+               for name, kind, k, nt in STREAM_PROBES}
+        t = cl.us_interleaved(fns)
+        out["per_size"]["%d MiB" % mib] = {k: {"us": round(v, 2), "frac": round(frac(nbytes, v), 4)}
+                                          for k, v in t.items()}
+        log("  %d MiB: " % mib + ", ".join("%s %.3f" % (k, frac(nbytes, v)) for k, v in t.items()))
+        del a, b
+    cl.close()
     torch.cuda.empty_cache()
     return out
 
@@ -767,6 +816,11 @@ def main():
         with open(args.stage1_scan, "w") as f:
             json.dump(scan, f, indent=1)
         log("bench: stage-1 size scan written to %s" % args.stage1_scan)
+
+    if args.stream_probes:
+        log("bench: plain streams, cold")
+        with open(args.stream_probes, "w") as f:
+            json.dump(measure_streams(torch, stream, log), f, indent=1)
 
     for name, e in stages.items():
         log("  %-4s %8.1f us/allreduce  stage0 %.3f  stage1 %.3f (cold %s, pattern %s, "

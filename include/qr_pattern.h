@@ -10,7 +10,7 @@
  * description item 2) replaced by an XOR of the W ranks' words.  Its time is
  * what the memory system needs for stage 1's bytes in stage 1's pattern:
  * the ceiling a benchmark sets beside the stage-1 kernel.  What it writes is
- * not a reduced image.
+ * not a reduced image.  qrp_stream times plain reads, writes and copies.
  */
 #ifndef QR_PATTERN_H
 #define QR_PATTERN_H
@@ -31,6 +31,20 @@ extern "C" {
  * not 16-byte aligned pointer, or such an n; -6 when the launch fails. */
 int qrp_stage1_pattern(int codec, int W, const void* recv, size_t n, void* reduced,
                        void* stream);
+
+/* Plain streams of 16-byte accesses, the memory system's own rates beside
+ * which the kernels' access choices were made.  kind: 0 reads `bytes` from
+ * src (one 4-byte word per workgroup may be written to dst, which must hold
+ * 4 bytes per workgroup: bytes / (4096 * per_lane) rounded up); 1 writes
+ * `bytes` to dst; 2 copies bytes / 2 from src to dst.  per_lane: 16-byte
+ * accesses per lane, 1 or 4 (a workgroup of 256 lanes covers 4096 * per_lane
+ * bytes, access k of lane l at chunk 256k + l of the workgroup's range);
+ * nontemporal: 0 through the caches, 1 non-temporal loads (kind 0, 2) or
+ * stores (kind 1).  bytes: a positive multiple of 32, at most 2^36.  src,
+ * dst: device memory, 16-byte aligned; stream as above.  Returns 0; -1
+ * (nothing launched) for other arguments; -6 when the launch fails. */
+int qrp_stream(int kind, int per_lane, int nontemporal, const void* src, void* dst,
+               size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

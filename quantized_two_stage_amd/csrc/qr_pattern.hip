@@ -66,6 +66,66 @@ __global__ __launch_bounds__(kThreads) void k_sum_pattern(InPtrs xs, uint8_t* re
   }
 }
 
+// plain streams: kind 0 read, 1 write, 2 copy; K 16-byte accesses per lane,
+// access k of lane l at chunk 256k + l of the workgroup's 256K chunks
+template <int Kind, int K, bool NT>
+__global__ __launch_bounds__(kThreads) void k_stream(const u32x4* src, u32x4* dst,
+                                                     uint64_t nchunks, uint32_t* out) {
+  const uint64_t base = (uint64_t)blockIdx.x * (kThreads * K) + threadIdx.x;
+  if constexpr (Kind == 0) {
+    u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+      const uint64_t c = base + (uint64_t)k * kThreads;
+      if (c < nchunks) acc ^= NT ? __builtin_nontemporal_load(src + c) : src[c];
+    }
+    // never true for the benchmark's data, but the loads cannot be dropped
+    if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) out[blockIdx.x] = acc.x;
+  } else if constexpr (Kind == 1) {
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+      const uint64_t c = base + (uint64_t)k * kThreads;
+      const u32x4 v = {(uint32_t)c, 1u, 2u, 3u};
+      if (c < nchunks) {
+        if constexpr (NT)
+          __builtin_nontemporal_store(v, dst + c);
+        else
+          dst[c] = v;
+      }
+    }
+  } else {
+    u32x4 v[K];
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+      const uint64_t c = base + (uint64_t)k * kThreads;
+      if (c < nchunks) v[k] = NT ? __builtin_nontemporal_load(src + c) : src[c];
+    }
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+      const uint64_t c = base + (uint64_t)k * kThreads;
+      if (c < nchunks) dst[c] = v[k];
+    }
+  }
+}
+
+template <int Kind, int K, bool NT>
+void stream_launch(const void* src, void* dst, uint64_t nchunks, hipStream_t st) {
+  const unsigned ng = (unsigned)((nchunks + kThreads * K - 1) / (kThreads * K));
+  hipLaunchKernelGGL((k_stream<Kind, K, NT>), dim3(ng), dim3(kThreads), 0, st,
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), nchunks,
+                     static_cast<uint32_t*>(dst));
+}
+
+template <int Kind>
+void stream_by(int K, bool nt, const void* src, void* dst, uint64_t nchunks, hipStream_t st) {
+  if (K == 1)
+    nt ? stream_launch<Kind, 1, true>(src, dst, nchunks, st)
+       : stream_launch<Kind, 1, false>(src, dst, nchunks, st);
+  else
+    nt ? stream_launch<Kind, 4, true>(src, dst, nchunks, st)
+       : stream_launch<Kind, 4, false>(src, dst, nchunks, st);
+}
+
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 template <int C, int W>
@@ -144,6 +204,28 @@ int qrp_stage1_pattern(int codec, int W, const void* recv, size_t n, void* reduc
     case QR_Q4_ASYM: by_w<kQ4A>(W, in, red, n, st); break;
     default: return -1;
   }
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// declared, with its arguments, in qr_pattern.h
+int qrp_stream(int kind, int per_lane, int nontemporal, const void* src, void* dst,
+               size_t bytes, void* stream) {
+  using namespace qr;
+  if (kind < 0 || kind > 2 || (per_lane != 1 && per_lane != 4) ||
+      (nontemporal != 0 && nontemporal != 1) || bytes == 0 || bytes % 32 != 0 ||
+      bytes > ((size_t)1 << 36) || dst == nullptr || ((uintptr_t)dst & 15u) != 0 ||
+      (kind != 1 && (src == nullptr || ((uintptr_t)src & 15u) != 0)))
+    return -1;
+  // a copy moves bytes / 2 each way
+  const uint64_t nchunks = (kind == 2 ? bytes / 2 : bytes) / 16;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (kind == 0)
+    stream_by<0>(per_lane, nontemporal != 0, src, dst, nchunks, st);
+  else if (kind == 1)
+    stream_by<1>(per_lane, nontemporal != 0, src, dst, nchunks, st);
+  else
+    stream_by<2>(per_lane, nontemporal != 0, src, dst, nchunks, st);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

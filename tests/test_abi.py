@@ -254,7 +254,7 @@ def test_pattern_library_exports_its_header_and_rejects():
     src = open(os.path.join(ROOT, "include", "qr_pattern.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = sorted(set(re.findall(r"\b(qrp_[a-z0-9_]+)\s*\(", src)))
-    assert names == ["qrp_stage1_pattern"]
+    assert names == ["qrp_stage1_pattern", "qrp_stream"]
     L = ctypes.CDLL(qbuild.PATTERN_LIB)
     for name in names:
         assert hasattr(L, name), name
@@ -269,3 +269,14 @@ def test_pattern_library_exports_its_header_and_rejects():
     for b in bad:
         a = dict(good, **b)
         assert f(a["codec"], a["W"], a["recv"], a["n"], a["red"], None) == -1, b
+    g = L.qrp_stream
+    g.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    g.restype = ctypes.c_int
+    good = dict(kind=2, k=4, nt=1, src=1 << 20, dst=1 << 24, nbytes=1 << 20)
+    bad = [dict(kind=3), dict(kind=-1), dict(k=2), dict(k=0), dict(nt=2), dict(nbytes=0),
+           dict(nbytes=48), dict(nbytes=(1 << 36) + 32), dict(dst=0), dict(dst=(1 << 24) + 8),
+           dict(src=0), dict(src=(1 << 20) + 4), dict(kind=0, src=0)]
+    for b in bad:
+        a = dict(good, **b)
+        assert g(a["kind"], a["k"], a["nt"], a["src"], a["dst"], a["nbytes"], None) == -1, b

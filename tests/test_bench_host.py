@@ -77,9 +77,11 @@ def test_min_sizes_needs_the_margin_and_reports_points_near_it():
     tab, marginal = bench.min_sizes(sweep, margin=0.2)
     assert tab["W4"]["q4"] == 16777216
     assert [m["bytes"] for m in marginal] == [8388608]
-    # the default margin is the one the benchmark reports
-    assert bench.min_sizes(sweep)[0] == tab
     assert bench.min_sizes(sweep, margin=0.1)[0]["W4"]["q4"] == 4194304
+    # the benchmark's own margin, 30 %: only the 25 % lead at 16 MB falls short
+    assert bench.MIN_SIZE_MARGIN == 0.30
+    assert bench.min_sizes(sweep)[0]["W4"]["q4"] is None
+    assert bench.min_sizes(sweep, margin=0.3) == bench.min_sizes(sweep)
 
 
 def test_stage2_hbm_bytes_read_the_reduced_image_once():
