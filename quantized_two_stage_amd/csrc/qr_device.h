@@ -3,8 +3,9 @@
 //
 // Two work decompositions are used (see qr_kernels.hip):
 //   - one lane per 32-element block (stage 1): the block's codes are 16, 24
-//     or 32 contiguous bytes, its statistics and scale are computed once, in
-//     registers, with no cross-lane traffic;
+//     or 32 bytes (one, three or two words in the receive buffer's word-major
+//     tiles), its statistics and scale are computed once, in registers, with
+//     no cross-lane traffic;
 //   - four lanes per block, 8 elements each (stage 0 and stage 2): every lane
 //     reads or writes 16 contiguous bytes of 16-bit data, so those planes
 //     stream at full coalescing; stage 0 combines the block's max/min across

@@ -27,10 +27,13 @@
 //     instead of a round trip through LDS).  k_dequant takes 4 or 1 quarters
 //     per lane (s2_quarters_per_lane).
 //   - k_stage1 gives each lane a whole block: W code blocks of 16/24/32
-//     contiguous bytes and W scales in, one code block and scale out; the
-//     per-block work (max/min, two divisions, rounding of the scale) is done
-//     once, which matters because this kernel is the one closest to the
-//     VALU limit (W=2, 4-bit codes: 1.7 bytes of HBM per element).
+//     bytes and W scales in, one code block and scale out; the per-block
+//     work (max/min, two divisions, rounding of the scale) is done once,
+//     which matters because this kernel is the one closest to the VALU limit
+//     (W=2, 4-bit codes: 1.7 bytes of HBM per element).  From the receive
+//     buffer, whose tiles hold the codes word-major, each load instruction of
+//     a wave reads one contiguous range, so from W = 4 up the wire data
+//     stream in with non-temporal loads (QR_NT_LOAD).
 //   - the FP kernels give each lane 16-byte chunks, four per lane (stage
 //     2: as k_dequant).
 //   - k_fused gives each lane one quarter block of every rank (a workgroup
