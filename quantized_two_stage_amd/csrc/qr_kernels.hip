@@ -844,7 +844,7 @@ void q_launch(int W, const InPtrs& xs, const OutPtrs& wires, const Layout& L, hi
   const size_t tiles = C == kFP ? groups(L.n / 8, kThreads * kPerLane)
                                 : groups(4 * L.nb, kThreads * kPerLane);
   const size_t per = Recv ? recv_tiles_per_launch(W, L) : tiles + 1;
-  const int U = C == kFP ? kPerLane : s0_quarters_per_lane(W, L.n);
+  const int U = C == kFP ? kPerLane : s0_quarters_per_lane(W, L.n, CodecT<C>::bits);
   const size_t wpt = 4 / U;                            // workgroups per tile
   for (size_t t0 = 0; t0 < tiles; t0 += per) {
     const size_t nt = tiles - t0 < per ? tiles - t0 : per;

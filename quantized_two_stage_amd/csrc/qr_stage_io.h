@@ -25,12 +25,17 @@ constexpr int kPerLane = 4;        // quarters / chunks per lane (k_quantize and
 //   stage 0: quarters per lane of k_quantize (the quad quantizer's slots):
 //            2 from W*n >= 2^28 elements (1% faster at W=8, 64 MB per rank),
 //            else 4 (2 was 3% slower at W*n = 2^26, the same at 2^27);
+//            8-bit codes keep 4 at every size: with the inputs streamed in,
+//            their quantizer is VALU-heavy, and 4 slots spread each lane's
+//            share of the block parameters over 32 elements instead of 16
+//            (W=8, 64 MB per rank: FP8, Q8 and Q8A 1.5-2% faster per
+//            allreduce; the 6- and 4-bit codes equal or up to 2% slower);
 //   stage 2: quarters per lane of k_dequant and the FP copy: 1 from
 //            W*n >= 2^26 (1-3% faster at W = 4 and 8), else 4;
 //   stage 1: lanes per workgroup, one block per lane: 128 at W = 2 from
 //            2^20 blocks per rank (3-5% faster at 64 MB per rank), else 256.
-inline int s0_quarters_per_lane(int W, size_t n) {
-  return (uint64_t)W * n >= (1ull << 28) ? 2 : 4;
+inline int s0_quarters_per_lane(int W, size_t n, int bits) {
+  return (uint64_t)W * n >= (1ull << 28) && bits != 8 ? 2 : 4;
 }
 inline int s2_quarters_per_lane(int W, size_t n) {
   return (uint64_t)W * n >= (1ull << 26) ? 1 : 4;
