@@ -19,8 +19,8 @@
 // Every kernel streams HBM; nothing is a contraction, so no MFMA and no LDS.
 //   - k_quantize and k_dequant work on quarter blocks (8 elements = 16
 //     contiguous bytes of 16-bit data, consecutive lanes on consecutive
-//     quarters).  k_quantize takes U = 4 or 2 quarters per lane (by size,
-//     s0_quarters_per_lane), issued before any is used, so that a quad of
+//     quarters).  k_quantize takes U = 4 or 2 quarters per lane (by size and
+//     code width, s0_quarters_per_lane), issued before any is used, so that a quad of
 //     lanes holds the quarters of U blocks: it reduces each block's max/min
 //     with DPP quad permutes, lane j derives the scale of block j mod U, and
 //     1/s reaches the other lanes by a DPP broadcast (a few instructions,
