@@ -55,3 +55,33 @@ def test_bench_prints_the_contract_line():
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1
     assert isinstance(c["unit"], str) and isinstance(c["sample"], str)
+
+
+def test_stage1_scan_and_stream_probes_run():
+    """bench.py's stage-1 size scan and plain-stream legs, at small sizes:
+    every kernel timed at every size, fractions of 8 TB/s in a plausible
+    range, and the plateau taken over the sizes from 64 MB per rank up"""
+    import torch
+
+    import bench
+    from quantized_two_stage_amd import inputs as I
+    from quantized_two_stage_amd import qr
+
+    torch.cuda.set_device(0)
+    st = torch.cuda.current_stream()
+    sizes = (1 << 20, 1 << 25)                      # 2 MB and 64 MB per rank
+    print("stage-1 scan at", sizes, flush=True)
+    sc = bench.measure_stage1_scan(qr, I, torch, st, lambda m: None, sizes=sizes, reps=2)
+    assert sc["sizes_bytes_per_rank"] == [2 * n for n in sizes]
+    assert set(sc["per_codec"]) == {I.CODEC_NAMES[c] for c in I.CONFIGS[5]["codecs"]}
+    for c, r in sc["per_codec"].items():
+        assert len(r["bytes"]) == len(sizes)
+        for k in ("stage1", "pattern", "copy"):
+            assert len(r[k]["us"]) == len(sizes) and all(u > 0 for u in r[k]["us"]), (c, k)
+            assert all(0.0 < f < 1.2 for f in r[k]["frac"]), (c, k, r[k]["frac"])
+            assert r[k]["plateau_frac"] == r[k]["frac"][-1], (c, k)     # only 64 MB counts
+    print("plain streams", flush=True)
+    ps = bench.measure_streams(torch, st, lambda m: None, sizes_mib=(256,), reps=2)
+    row = ps["per_size"]["256 MiB"]
+    assert len(row) == len(bench.STREAM_PROBES)
+    assert all(v["us"] > 0 and 0.0 < v["frac"] < 1.5 for v in row.values()), row
