@@ -164,18 +164,16 @@ class Pattern:
         P, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         self.L.qrp_stage1_pattern.argtypes = [i32, i32, P, sz, P, P]
         self.L.qrp_stage1_pattern.restype = i32
+        self.L.qrp_stream.argtypes = [i32, i32, i32, P, P, sz, P]
+        self.L.qrp_stream.restype = i32
         self.ct = ctypes
 
     def stream(self, kind, per_lane, nt, src, dst, nbytes, stream):
-        L = self.L
-        if not hasattr(L, "_stream_sig"):
-            P, i32, sz = self.ct.c_void_p, self.ct.c_int, self.ct.c_size_t
-            L.qrp_stream.argtypes = [i32, i32, i32, P, P, sz, P]
-            L.qrp_stream.restype = i32
-            L._stream_sig = True
-        rc = L.qrp_stream(kind, per_lane, nt, self.ct.c_void_p(src.data_ptr()),
-                          self.ct.c_void_p(dst.data_ptr()), nbytes,
-                          self.ct.c_void_p(stream.cuda_stream))
+        """qrp_stream: kind 0 read, 1 write, 2 copy of nbytes (src, dst: device
+        tensors of at least nbytes)"""
+        rc = self.L.qrp_stream(kind, per_lane, nt, self.ct.c_void_p(src.data_ptr()),
+                               self.ct.c_void_p(dst.data_ptr()), nbytes,
+                               self.ct.c_void_p(stream.cuda_stream))
         if rc != 0:
             raise RuntimeError("qrp_stream failed (%d)" % rc)
 
