@@ -27,14 +27,14 @@ def qr():
     return q
 
 
-def _data(cfg, n=None):
-    key = (cfg, n)
+def _data(cfg, n=None, W=None):
+    key = (cfg, n, W)
     if key not in _cache:
         _cache.clear()
         c = I.CONFIGS[cfg]
         n_ = n or c["n"]
         xs_np = []
-        for r in range(c["W"]):
+        for r in range(W or c["W"]):
             say("generating config", cfg, "n", n_, "rank", r)
             xs_np.append(I.to_bits(I.draw(cfg, r, n_), c["dtype"]))
         _cache[key] = (xs_np, [dev16(x) for x in xs_np])
@@ -46,12 +46,13 @@ def _planes_equal(got, want, codec, n, what):
         assert_bytes_equal(got[a:e], want[a:e], "%s %s" % (what, name))
 
 
-def _check_full(qr, cfg, codec, n=None, staged=True, dtype=None):
-    """one qr_allreduce_sim call against the oracle over the whole buffers"""
+def _check_full(qr, cfg, codec, n=None, staged=True, dtype=None, W=None):
+    """one qr_allreduce_sim call against the oracle over the whole buffers
+    (W: the workload's recipe for another number of ranks)"""
     c = I.CONFIGS[cfg]
-    W = c["W"]
+    W = W or c["W"]
     dtype = c["dtype"] if dtype is None else dtype
-    xs_np, xs = _data(cfg, n)
+    xs_np, xs = _data(cfg, n, W)
     n = xs_np[0].size
     label = "cfg%d %s W%d n%d dtype%d" % (cfg, I.CODEC_NAMES[codec], W, n, dtype)
     say("full", label)
@@ -107,6 +108,14 @@ def test_config3_sweep(qr, n):
 
 def test_config4_full(qr):
     _check_full(qr, 4, O.Q6)
+
+
+# W=4 at 64 MB per rank in fp16, every codec (the W=2 64 MB workload's recipe
+# for four ranks): the stage-1 kernels that stream their wire data
+# non-temporally from W=4 up, at the size the W=2 and W=8 workloads run
+@pytest.mark.parametrize("codec", I.ALL_CODECS, ids=[I.CODEC_NAMES[c] for c in I.ALL_CODECS])
+def test_w4_64MB_full(qr, codec):
+    _check_full(qr, 2, codec, W=4, staged=codec in (O.Q8, O.Q6A))
 
 
 @pytest.mark.parametrize("codec", I.CONFIGS[5]["codecs"],
